@@ -1,0 +1,173 @@
+"""CPU oracle for the w8a16 block-scaled FP8 projection (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The GPU library does
+not import it and shares no code with it.
+
+The arithmetic lives in ``w8a16_oracle.c`` (plain C, fp64, closed-form E4M3
+decode); this module compiles it with gcc and marshals numpy arrays into it.
+The operation is the one the Qwen3SsmLayer docs give for the w8a16 GEMV
+(``set_fp8_decode_weights``), with the block-scale index of the
+NemotronMamba2Layer docs (``set_fp8_weights``):
+
+    out[m, n] = sum_k A[m, k] * E4M3(W[n, k]) * S[n // 128, k // 128]
+
+Arrays are raw bit patterns: A and S are ``uint16`` BF16 bits, W is ``uint8``
+E4M3 codes. Results are fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "w8a16_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_w8a16.so")
+BLOCK = 128
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (OpenMP over independent output elements)."""
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_bf16_value.restype = ctypes.c_double
+    lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
+    for name in ("oracle_e4m3_values", "oracle_bf16_values", "oracle_bf16_rne_array"):
+        getattr(lib, name).restype = None
+        getattr(lib, name).argtypes = [P, I64, P]
+    lib.oracle_dequant.restype = None
+    lib.oracle_dequant.argtypes = [P, P, I64, I64, P]
+    lib.oracle_w8a16.restype = None
+    lib.oracle_w8a16.argtypes = [P, P, P, I64, I64, I64, P, P]
+    lib.oracle_w8a16_points.restype = None
+    lib.oracle_w8a16_points.argtypes = [P, P, P, I64, I64, I64, P, P, I64, P, P]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def scale_grid(N: int, K: int) -> tuple[int, int]:
+    """Shape of the block-scale grid: [ceil(N/128), ceil(K/128)]."""
+    return ((N + BLOCK - 1) // BLOCK, (K + BLOCK - 1) // BLOCK)
+
+
+def _check_operands(A, W, S):
+    A = _c(A, np.uint16)
+    W = _c(W, np.uint8)
+    S = _c(S, np.uint16)
+    if A.ndim != 2 or W.ndim != 2 or S.ndim != 2:
+        raise ValueError("A, W and S must be 2-D")
+    M, K = A.shape
+    N, K2 = W.shape
+    if K2 != K:
+        raise ValueError(f"A is [{M},{K}] but W is [{N},{K2}]")
+    if S.shape != scale_grid(N, K):
+        raise ValueError(f"S must be {scale_grid(N, K)}, got {S.shape}")
+    return A, W, S, M, N, K
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """Closed-form E4M3 decode of each byte (NaN for 0x7F / 0xFF)."""
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e4m3_values(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def bf16_value(bits) -> np.ndarray:
+    """Exact value of each BF16 bit pattern."""
+    b = _c(bits, np.uint16)
+    out = np.empty(b.shape, np.float64)
+    _load().oracle_bf16_values(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def bf16_rne(x) -> np.ndarray:
+    """BF16 bit pattern nearest each fp64 value (ties to even)."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(a.shape, np.uint16)
+    _load().oracle_bf16_rne_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def dequant(W, S) -> np.ndarray:
+    """Wdeq[n, k] = E4M3(W[n, k]) * S[n//128, k//128] in fp64 (exact)."""
+    W = _c(W, np.uint8)
+    S = _c(S, np.uint16)
+    N, K = W.shape
+    if S.shape != scale_grid(N, K):
+        raise ValueError(f"S must be {scale_grid(N, K)}, got {S.shape}")
+    out = np.empty((N, K), np.float64)
+    _load().oracle_dequant(_ptr(W), _ptr(S), N, K, _ptr(out))
+    return out
+
+
+def w8a16(A, W, S) -> tuple[np.ndarray, np.ndarray]:
+    """Whole result: (ref, den), each [M, N] fp64.
+
+    ref[m, n] = sum_k A[m,k] * Wdeq[n,k] (k ascending, fp64);
+    den[m, n] = sum_k |A[m,k] * Wdeq[n,k]|.
+    """
+    A, W, S, M, N, K = _check_operands(A, W, S)
+    ref = np.empty((M, N), np.float64)
+    den = np.empty((M, N), np.float64)
+    _load().oracle_w8a16(_ptr(A), _ptr(W), _ptr(S), M, N, K, _ptr(ref), _ptr(den))
+    return ref, den
+
+
+def w8a16_points(A, W, S, mi, ni) -> tuple[np.ndarray, np.ndarray]:
+    """(ref, den) at the listed output coordinates (mi[p], ni[p])."""
+    A, W, S, M, N, K = _check_operands(A, W, S)
+    mi = np.ascontiguousarray(np.asarray(mi, dtype=np.int64))
+    ni = np.ascontiguousarray(np.asarray(ni, dtype=np.int64))
+    if mi.shape != ni.shape or mi.ndim != 1:
+        raise ValueError("mi and ni must be 1-D and of equal length")
+    if mi.size and (mi.min() < 0 or mi.max() >= M or ni.min() < 0 or ni.max() >= N):
+        raise IndexError("output coordinate out of range")
+    ref = np.empty(mi.size, np.float64)
+    den = np.empty(mi.size, np.float64)
+    _load().oracle_w8a16_points(_ptr(A), _ptr(W), _ptr(S), M, N, K,
+                                _ptr(mi), _ptr(ni), mi.size, _ptr(ref), _ptr(den))
+    return ref, den
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())

@@ -1,0 +1,191 @@
+/*
+ * CPU oracle for the w8a16 block-scaled FP8 projection.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is a plain, slow, fp64 statement of what
+ * the projection computes. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load it. The GPU library shares no code,
+ * header, table or helper with it, and nothing here calls the GPU.
+ *
+ * The operation (Qwen3SsmLayer docs, `set_fp8_decode_weights`: the w8a16 GEMV
+ * formula; NemotronMamba2Layer docs, `set_fp8_weights`: the block-scale index):
+ *
+ *     out[m][n] = sum over k of  A[m][k] * E4M3(W[n][k]) * S[n / 128][k / 128]
+ *
+ *   A  : BF16 bit patterns, [M][K] row-major.
+ *   W  : E4M3 bytes, [N][K] row-major (K contiguous).
+ *   S  : BF16 bit patterns, [ceil(N/128)][ceil(K/128)] row-major, so the scale
+ *        of element (n, k) sits at index (n / 128) * ceil(K/128) + (k / 128).
+ *
+ * Every product here is exact in fp64: a BF16 value has 8 significant bits,
+ * an E4M3 value 4 and a BF16 scale 8, so A * E4M3 * S has at most 20. The sum
+ * runs over k in ascending order in fp64. `den` is the same sum of absolute
+ * values; it scales the parity tolerance.
+ *
+ * Parity pins (the tests that tie this file to something other than itself):
+ * E4M3 decode against the OCP 8-bit floating-point specification's special
+ * values and against torch's float8_e4m3fn; BF16 decode against torch's
+ * bfloat16 on all 65536 patterns; BF16 rounding against exact rational
+ * rounding; the contraction against exact rational (fractions.Fraction) sums
+ * on tiny shapes, against a library fp64 matmul, and against the invariants
+ * of a bilinear block-scaled product (one-hot rows, zero weights, scale
+ * doubling, sign and power-of-two scaling, row permutation).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#define ORACLE_BLOCK 128
+
+/*
+ * E4M3 (OCP "OFP8" E4M3, the FN variant: bias 7, no infinities, NaN only at
+ * S.1111.111). The pages call the weights E4M3 with a 448 maximum; this is
+ * the closed form of that encoding, with no lookup table:
+ *   exponent field 0  : (-1)^s * m * 2^-9            (subnormals, and +-0)
+ *   exponent 15, m = 7: NaN
+ *   otherwise         : (-1)^s * (1 + m/8) * 2^(E - 7)
+ */
+double oracle_e4m3_value(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* BF16 is the upper half of an IEEE binary32; widening it is exact. */
+double oracle_bf16_value(uint16_t bits)
+{
+    union { uint32_t u; float f; } v;
+    v.u = (uint32_t)bits << 16;
+    return (double)v.f;
+}
+
+/*
+ * Round a real (given exactly as a double) to BF16, round-to-nearest with
+ * ties to even, directly from the double (no intermediate float, so there is
+ * no double rounding). BF16: 8 significant bits, exponent range of binary32,
+ * subnormal quantum 2^-133. Overflow past the largest finite value rounds to
+ * infinity as in IEEE 754.
+ */
+uint16_t oracle_bf16_rne(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    double a = fabs(x);
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7FC0u);
+    if (isinf(x))
+        return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);               /* a = f * 2^e, f in [0.5, 1) -> unbiased exponent e-1 */
+    int ue = e - 1;
+    if (ue < -126)
+        ue = -126;              /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, ue - 7);
+    double q = nearbyint(a / quantum); /* exact division by a power of two; ties-to-even */
+    double r = q * quantum;
+    /* r has at most 9 significant bits only when q == 256 (carry), which is
+     * still exactly representable in BF16 as the next binade's 1.0. */
+    if (r >= ldexp(1.0, 128))
+        return (uint16_t)(sign | 0x7F80u);
+    union { uint32_t u; float f; } v;
+    v.f = (float)r;             /* exact: r is representable in binary32 */
+    return (uint16_t)(sign | ((v.u >> 16) & 0x7FFFu));
+}
+
+static int64_t ceil_blocks(int64_t n) { return (n + ORACLE_BLOCK - 1) / ORACLE_BLOCK; }
+
+/* Dequantized weight as a real: E4M3(W[n][k]) * S[n/128][k/128]. */
+static double wdeq(const uint8_t* W, const uint16_t* S, int64_t K, int64_t n, int64_t k)
+{
+    int64_t kb = ceil_blocks(K);
+    double e = oracle_e4m3_value(W[n * K + k]);
+    double s = oracle_bf16_value(S[(n / ORACLE_BLOCK) * kb + (k / ORACLE_BLOCK)]);
+    return e * s;
+}
+
+/* out[n*K + k] = E4M3(W[n][k]) * S[n/128][k/128], exact, [N][K] fp64. */
+void oracle_dequant(const uint8_t* W, const uint16_t* S, int64_t N, int64_t K, double* out)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = wdeq(W, S, K, n, k);
+}
+
+/* One output element: ref = sum_k A[m][k]*Wdeq[n][k] (k ascending), den = sum |.|. */
+static void dot_one(const uint16_t* A, const uint8_t* W, const uint16_t* S,
+                    int64_t K, int64_t m, int64_t n, double* ref, double* den)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double t = oracle_bf16_value(A[m * K + k]) * wdeq(W, S, K, n, k);
+        acc += t;
+        mag += fabs(t);
+    }
+    *ref = acc;
+    *den = mag;
+}
+
+/* Every element of the [M][N] result. Elements are independent; the threads
+ * split the (m, n) pairs and never reorder a sum. */
+void oracle_w8a16(const uint16_t* A, const uint8_t* W, const uint16_t* S,
+                  int64_t M, int64_t N, int64_t K, double* ref, double* den)
+{
+    int64_t total = M * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t m = i / N, n = i % N;
+        dot_one(A, W, S, K, m, n, &ref[i], &den[i]);
+    }
+}
+
+/* Selected elements (mi[p], ni[p]) of the result, for shapes too large to
+ * compute whole. */
+void oracle_w8a16_points(const uint16_t* A, const uint8_t* W, const uint16_t* S,
+                         int64_t M, int64_t N, int64_t K,
+                         const int64_t* mi, const int64_t* ni, int64_t npts,
+                         double* ref, double* den)
+{
+    (void)M; (void)N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npts; ++p)
+        dot_one(A, W, S, K, mi[p], ni[p], &ref[p], &den[p]);
+}
+
+/* Element-wise array forms of the scalar conversions above. */
+void oracle_e4m3_values(const uint8_t* codes, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3_value(codes[i]);
+}
+
+void oracle_bf16_values(const uint16_t* bits, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_value(bits[i]);
+}
+
+void oracle_bf16_rne_array(const double* x, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_rne(x[i]);
+}
+
+/* Threads the parallel loops above would use (for reporting). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
