@@ -1,0 +1,176 @@
+"""Python binding of libw8a16.so: argument marshalling only.
+
+Every function here checks torch tensors (dtype, shape, contiguity, device),
+then calls the C ABI declared in ``include/w8a16.h`` on the current torch HIP
+stream. All arithmetic runs in the HIP kernels; there is no fallback path, and
+a missing library raises.
+
+The scale layout check mirrors the NemotronMamba2Layer docs
+(``set_fp8_weights``): block-scaled weights must carry the
+[ceil(N/128), ceil(K/128)] BF16 grid, since a per-row [N] or scalar scale
+would be read past its end inside the kernel. The Qwen3SsmLayer docs
+(``set_fp8_rowwise_prefill_weights``) make the same point the other way: a
+layout mix-up between formats is only caught by an explicit check.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw8a16.so")
+BLOCK = 128
+
+EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_dequant", "w8a16_strerror")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ALIAS, ERR_ARG = 0, -1, -2, -3, -4, -5, -6
+GEMV_MAX_M = 16
+GEMV_MAX_K_SMALL_M = 16384   # M <= 4
+GEMV_MAX_K = 8192            # M >= 5
+
+_lib = None
+
+
+class W8A16Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {strerror(status)}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libw8a16.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m gemm_mamba_ssm_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    for name in ("w8a16_gemv", "w8a16_gemm"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P, P, P, P, I64, I64, I64, P]
+    lib.w8a16_dequant.restype = ctypes.c_int
+    lib.w8a16_dequant.argtypes = [P, P, P, I64, I64, ctypes.c_int, P]
+    lib.w8a16_strerror.restype = ctypes.c_char_p
+    lib.w8a16_strerror.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load().w8a16_strerror(int(status)).decode()
+
+
+# --- raw pointer calls (integers in, status out) ------------------------------
+
+def gemv_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    return load().w8a16_gemv(A, Wq, scale, out, M, N, K, stream)
+
+
+def gemm_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    return load().w8a16_gemm(A, Wq, scale, out, M, N, K, stream)
+
+
+def dequant_raw(Wq: int, scale: int, out: int, N: int, K: int, mode: int, stream: int = 0) -> int:
+    return load().w8a16_dequant(Wq, scale, out, N, K, mode, stream)
+
+
+# --- torch tensors ------------------------------------------------------------
+
+def scale_grid(N: int, K: int) -> tuple[int, int]:
+    return ((N + BLOCK - 1) // BLOCK, (K + BLOCK - 1) // BLOCK)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_weights(Wq: torch.Tensor, scale: torch.Tensor) -> tuple[int, int]:
+    _need(Wq.dtype in (torch.uint8, torch.float8_e4m3fn),
+          f"Wq must hold E4M3 bytes (torch.uint8 or torch.float8_e4m3fn), got {Wq.dtype}")
+    _need(Wq.dim() == 2, f"Wq must be [N, K], got shape {tuple(Wq.shape)}")
+    N, K = Wq.shape
+    _need(K >= 16 and K % 16 == 0, f"K must be a multiple of 16 and >= 16, got {K}")
+    _need(Wq.is_contiguous(), "Wq must be contiguous (row-major [N, K])")
+    _need(scale.dtype == torch.bfloat16,
+          f"scale must be the BF16 block-scale grid, got dtype {scale.dtype}")
+    _need(tuple(scale.shape) == scale_grid(N, K),
+          f"scale must be the [ceil(N/128), ceil(K/128)] = {list(scale_grid(N, K))} block grid, "
+          f"got shape {list(scale.shape)} (per-row or scalar scales are a different format)")
+    _need(scale.is_contiguous(), "scale must be contiguous (row-major by n-block)")
+    return N, K
+
+
+def _check_device(*tensors: torch.Tensor):
+    dev = tensors[0].device
+    _need(dev.type == "cuda", f"tensors must be on a HIP device, got {dev}")
+    for t in tensors[1:]:
+        _need(t.device == dev, f"all tensors must be on {dev}, got {t.device}")
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+
+
+def _product(fn_name: str, A, Wq, scale, out, stream, max_m=None):
+    _need(A.dtype == torch.bfloat16, f"A must be bfloat16, got {A.dtype}")
+    _need(A.dim() == 2, f"A must be [M, K], got shape {tuple(A.shape)}")
+    N, K = _check_weights(Wq, scale)
+    M = A.shape[0]
+    _need(A.shape[1] == K, f"A is {list(A.shape)} but Wq is {list(Wq.shape)}")
+    _need(A.is_contiguous(), "A must be contiguous (row-major [M, K])")
+    if max_m is not None:
+        _need(M <= max_m, f"{fn_name} takes at most {max_m} rows, got M={M} (use w8a16_gemm)")
+    if out is None:
+        _check_device(A, Wq, scale)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    else:
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (M, N) and out.is_contiguous(),
+              f"out must be a contiguous bfloat16 [{M}, {N}] tensor")
+        _check_device(A, Wq, scale, out)
+    with torch.cuda.device(A.device):
+        st = getattr(load(), fn_name)(A.data_ptr(), Wq.data_ptr(), scale.data_ptr(), out.data_ptr(),
+                                      M, N, K, _stream_handle(A.device, stream))
+    if st != OK:
+        raise W8A16Error(fn_name, st)
+    return out
+
+
+def w8a16_gemv(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode GEMV, M = 1..16: out[M, N] = A[M, K] x dequant(Wq[N, K], scale)^T (BF16)."""
+    return _product("w8a16_gemv", A, Wq, scale, out, stream, max_m=GEMV_MAX_M)
+
+
+def w8a16_gemm(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Prefill GEMM, any M: out[M, N] = A[M, K] x dequant(Wq[N, K], scale)^T (BF16)."""
+    return _product("w8a16_gemm", A, Wq, scale, out, stream)
+
+
+def w8a16_dequant(Wq: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None,
+                  mode: int = 0, stream=None) -> torch.Tensor:
+    """Dequantize only (test path): FP32 [N, K]; mode 0 = E4M3*s, mode 1 = bf16(E4M3*s)."""
+    N, K = _check_weights(Wq, scale)
+    _need(mode in (0, 1), f"mode must be 0 or 1, got {mode}")
+    if out is None:
+        _check_device(Wq, scale)
+        out = torch.empty((N, K), dtype=torch.float32, device=Wq.device)
+    else:
+        _need(out.dtype == torch.float32 and tuple(out.shape) == (N, K) and out.is_contiguous(),
+              f"out must be a contiguous float32 [{N}, {K}] tensor")
+        _check_device(Wq, scale, out)
+    with torch.cuda.device(Wq.device):
+        st = load().w8a16_dequant(Wq.data_ptr(), scale.data_ptr(), out.data_ptr(), N, K, mode,
+                                  _stream_handle(Wq.device, stream))
+    if st != OK:
+        raise W8A16Error("w8a16_dequant", st)
+    return out

@@ -1,0 +1,35 @@
+// Status strings and the per-device compute-unit count used to size grids.
+#include <hip/hip_runtime.h>
+
+#include "w8a16_host.h"
+
+namespace w8a16 {
+
+int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static int cached[kMaxDevices] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+}  // namespace w8a16
+
+extern "C" const char* w8a16_strerror(int status) {
+    switch (status) {
+        case W8A16_OK: return "ok";
+        case W8A16_ERR_NULL: return "a required pointer is NULL";
+        case W8A16_ERR_SHAPE: return "M, N or K out of range (K must be >= 16 and a multiple of 16)";
+        case W8A16_ERR_ALIGN: return "A, Wq (and dequant out) must be 16-byte aligned; scale and out 2-byte aligned";
+        case W8A16_ERR_LAUNCH: return "HIP kernel launch failed";
+        case W8A16_ERR_ALIAS: return "out overlaps an input buffer";
+        case W8A16_ERR_ARG: return "invalid argument";
+        default: return "unknown w8a16 status";
+    }
+}

@@ -1,0 +1,109 @@
+// Device-side building blocks shared by the GEMV, GEMM and dequant kernels:
+// E4M3 -> BF16 decode with the gfx950 packed converts, the block-scale index,
+// BF16 <-> FP32 and the wavefront reduction. gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a16 {
+
+// Scale blocks are 128 x 128 (NemotronMamba2Layer docs, `set_fp8_weights`).
+constexpr int kScaleBlock = 128;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Index of the scale of weight element (n, k) in the row-major
+// [ceil(N/128)][ceil(K/128)] grid: (n / 128) * ceil(K/128) + k / 128.
+__device__ __forceinline__ int64_t scale_index(int64_t n, int64_t k, int64_t k_blocks) {
+    return (n / kScaleBlock) * k_blocks + k / kScaleBlock;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) {
+    return __uint_as_float(bits << 16);
+}
+
+// fp32 -> BF16 bits, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Two E4M3 codes (bytes 0-1 of `w` if !hi, bytes 2-3 if hi) -> two BF16.
+// Every finite E4M3 value (3 mantissa bits, exponents 2^-9 .. 2^8) is exactly
+// representable in BF16, and a scale of 1.0 leaves it unchanged: exact.
+__device__ __forceinline__ bf16x2_t e4m3x2_to_bf16(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+
+// 16 E4M3 codes (one 16-byte load) -> 16 BF16, as 8 packed pairs in order.
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4_t w, bf16x2_t (&out)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = e4m3x2_to_bf16(w[i], false);
+        out[2 * i + 1] = e4m3x2_to_bf16(w[i], true);
+    }
+}
+
+// Two E4M3 codes times a block scale, rounded once to BF16:
+// bf16_rne(E4M3 * s). The E4M3 -> fp32 convert is exact, so is the fp32
+// product (4 + 8 significant bits), and v_cvt_pk_bf16_f32 rounds it once.
+__device__ __forceinline__ uint32_t e4m3x2_scaled_to_bf16(uint32_t w, bool hi, float s) {
+    f32x2_t f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true)
+                   : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    f.x *= s;
+    f.y *= s;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// 16 E4M3 codes scaled by s -> 16 BF16 (bf16_rne(e * s)), as 8 packed pairs.
+__device__ __forceinline__ void e4m3x16_scaled_to_bf16(u32x4_t w, float s, uint32_t (&out)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = e4m3x2_scaled_to_bf16(w[i], false, s);
+        out[2 * i + 1] = e4m3x2_scaled_to_bf16(w[i], true, s);
+    }
+}
+
+// DPP lane moves (within rows of 16 lanes). Controls from the GCN/CDNA DPP encoding.
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;   // row_ror:4
+constexpr int kDppRowRor8 = 0x128;   // row_ror:8
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront, in a fixed order (deterministic).
+// Within each row of 16 lanes: quad sums, then pairs of quads, then the
+// row; across the four rows: read each row's sum and add (r0+r1)+(r2+r3).
+// The result is uniform (the same in every lane).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_move<kDppQuadXor1>(v);
+    v += dpp_move<kDppQuadXor2>(v);
+    v += dpp_move<kDppRowRor4>(v);
+    v += dpp_move<kDppRowRor8>(v);
+    float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// 16-byte global load that bypasses cache retention (weights are streamed once).
+__device__ __forceinline__ u32x4_t load_stream16(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+}  // namespace w8a16

@@ -1,0 +1,60 @@
+// Host-side argument checks and kernel launch shared by the entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w8a16.h"
+
+namespace w8a16 {
+
+constexpr int64_t kScaleBlockHost = 128;   // 128 x 128 scale blocks
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [lo, lo + bytes) and [lo2, lo2 + bytes2) intersect?
+inline bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return abytes > 0 && bbytes > 0 && a0 < b0 + static_cast<uintptr_t>(bbytes) &&
+           b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+// Checks shared by w8a16_gemv and w8a16_gemm. Returns W8A16_OK or an error;
+// *noop is set when there is nothing to compute (M == 0 or N == 0).
+inline int check_product_args(const void* A, const void* Wq, const void* scale, const void* out,
+                              int64_t M, int64_t N, int64_t K, bool* noop) {
+    *noop = false;
+    if (M < 0 || N < 0 || K < 16 || (K % 16) != 0 || M > INT32_MAX || N > INT32_MAX ||
+        K > INT32_MAX)
+        return W8A16_ERR_SHAPE;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return W8A16_OK;
+    }
+    if (!A || !Wq || !scale || !out) return W8A16_ERR_NULL;
+    if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, 2) || !aligned(out, 2))
+        return W8A16_ERR_ALIGN;
+    const int64_t out_bytes = M * N * 2;
+    const int64_t scale_bytes = ceil_div(N, kScaleBlockHost) * ceil_div(K, kScaleBlockHost) * 2;
+    if (overlaps(out, out_bytes, A, M * K * 2) || overlaps(out, out_bytes, Wq, N * K) ||
+        overlaps(out, out_bytes, scale, scale_bytes))
+        return W8A16_ERR_ALIAS;
+    return W8A16_OK;
+}
+
+// Launch `kernel` with exactly the argument types of its signature; the HIP
+// launch status becomes W8A16_OK / W8A16_ERR_LAUNCH.
+template <typename... KArgs>
+inline int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                  KArgs... args) {
+    void* argv[] = {static_cast<void*>(&args)...};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
+    return e == hipSuccess ? W8A16_OK : W8A16_ERR_LAUNCH;
+}
+
+}  // namespace w8a16

@@ -1,0 +1,101 @@
+/*
+ * w8a16.h - C ABI of the MI355X (gfx950) w8a16 block-scaled FP8 projection.
+ *
+ * The operation (Qwen3SsmLayer docs, `set_fp8_decode_weights`, which gives the
+ * w8a16 GEMV formula and the BF16 [N/BS, K/BS] scale buffer; NemotronMamba2Layer
+ * docs, `set_fp8_weights`, which gives the 128-wide block index and the
+ * [ceil(N/128), ceil(K/128)] grid):
+ *
+ *     out[m][n] = sum_k A[m][k] * E4M3(Wq[n][k]) * scale[n/128][k/128]
+ *
+ * Operands (all DEVICE pointers, row-major, no padding between rows):
+ *   A      BF16  [M][K]                          activations (row stride K)
+ *   Wq     E4M3  [N][K]  (one byte per value)    weights, K contiguous
+ *   scale  BF16  [ceil(N/128)][ceil(K/128)]      block scales; element (n, k)
+ *                                                uses scale[(n/128)*ceil(K/128) + k/128]
+ *   out    BF16  [M][N]                          result (row stride N)
+ * E4M3 is the OCP FP8 E4M3 ("FN") encoding: bias 7, largest finite 448, NaN
+ * at 0x7F/0xFF (a NaN code propagates to the outputs it touches). Partial
+ * edge blocks (N or K not multiples of 128) use their block's scale.
+ * Accumulation is fp32; each output is rounded once to BF16 (nearest, ties
+ * to even). The scale must be exactly the [ceil(N/128)][ceil(K/128)] BF16 grid:
+ * the library cannot see allocation sizes, so a per-row [N] or scalar scale
+ * buffer reads past its end (a device fault, not wrong numbers) - callers
+ * must check the layout before calling, as the Python binding does.
+ *
+ * Ownership: the caller owns every buffer; the library allocates nothing and
+ * keeps no pointer after a call returns.
+ * Streams: `stream` is a hipStream_t (NULL = the legacy default stream). Every
+ * call only enqueues work on it and returns without synchronizing; the result
+ * is ready once the stream reaches that point.
+ * Errors: every argument is checked on the host BEFORE anything is enqueued;
+ * a failed check returns a negative W8A16_ERR_* code and launches nothing.
+ * W8A16_ERR_LAUNCH reports a HIP launch failure. The result is deterministic:
+ * the same inputs give the same bits on every call.
+ */
+#ifndef W8A16_H
+#define W8A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum w8a16_status {
+    W8A16_OK = 0,
+    W8A16_ERR_NULL = -1,   /* a required pointer is NULL                        */
+    W8A16_ERR_SHAPE = -2,  /* M, N or K out of range, or K not a multiple of 16 */
+    W8A16_ERR_ALIGN = -3,  /* A or Wq not 16-byte aligned; scale/out not 2-byte */
+    W8A16_ERR_LAUNCH = -4, /* the HIP launch failed                             */
+    W8A16_ERR_ALIAS = -5,  /* out overlaps an input                             */
+    W8A16_ERR_ARG = -6     /* another argument is invalid (e.g. dequant mode)   */
+};
+
+/* Largest M the GEMV entry point accepts, and its largest K: 16384 when
+ * M <= 4, 8192 otherwise (w8a16_gemm takes any M and K). */
+#define W8A16_GEMV_MAX_M 16
+#define W8A16_GEMV_MAX_K_SMALL_M 16384
+#define W8A16_GEMV_MAX_K 8192
+
+/*
+ * Decode GEMV: one or a few tokens (TransformerLayer docs, `decode`: a
+ * [1, hidden] BF16 row per token; `decode_multi_seq`: N sequences with the
+ * weights read once for all of them). 1 <= M <= 16, N >= 0, K % 16 == 0,
+ * 16 <= K <= 16384 for M <= 4 and 16 <= K <= 8192 for M >= 5.
+ * M == 0 or N == 0 is a no-op returning W8A16_OK.
+ * Each weight byte is read from HBM once per call for all M rows.
+ */
+int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
+               int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Prefill GEMM: M prompt tokens at once (TransformerLayer docs, `prefill`:
+ * the weights are read once for all N tokens as one GEMM with M = N).
+ * M >= 0 (any), N >= 0, K >= 16, K % 16 == 0; M == 0 or N == 0 is a no-op.
+ * Each weight tile is converted to BF16 once per staged tile and shared by
+ * all rows of the output tile.
+ */
+int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
+               int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Dequantize only (a test path that exposes the device E4M3 decode and the
+ * scale indexing the two entry points above use). out is FP32 [N][K]:
+ *   mode 0: out[n][k] = float(E4M3(Wq[n][k])) * scale[n/128][k/128]
+ *           (exact; the GEMV's decode, which applies the scale in fp32)
+ *   mode 1: out[n][k] = float(bf16_rne(E4M3(Wq[n][k]) * scale[n/128][k/128]))
+ *           (the GEMM's staged BF16 weight tile, with the scale folded in)
+ * Same shape, alignment (Wq 16 B, out 16 B) and error rules as above.
+ */
+int w8a16_dequant(const void* Wq, const void* scale, float* out,
+                  int64_t N, int64_t K, int mode, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* w8a16_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A16_H */

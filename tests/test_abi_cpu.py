@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/w8a16.h declares, and rejects bad arguments on the host before any
+HIP call. Also the binding's refusals of wrong dtypes and scale layouts."""
+import os
+import re
+
+import pytest
+import torch
+
+from gemm_mamba_ssm_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a16.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a16_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_every_status():
+    for st in (binding.OK, binding.ERR_NULL, binding.ERR_SHAPE, binding.ERR_ALIGN,
+               binding.ERR_LAUNCH, binding.ERR_ALIAS, binding.ERR_ARG):
+        s = binding.strerror(st)
+        assert s and "unknown" not in s
+    assert "unknown" in binding.strerror(12345)
+
+
+FAKE = 1 << 40          # an aligned address that is never dereferenced (checks fail first)
+
+
+@pytest.mark.parametrize("fn", [binding.gemv_raw, binding.gemm_raw])
+def test_rejections_before_any_hip_call(fn):
+    ok = dict(A=FAKE, Wq=FAKE + (1 << 30), scale=FAKE + (2 << 30), out=FAKE + (3 << 30))
+
+    def call(M=4, N=256, K=256, **over):
+        a = dict(ok, **over)
+        return fn(a["A"], a["Wq"], a["scale"], a["out"], M, N, K, 0)
+
+    assert call(K=0) == binding.ERR_SHAPE
+    assert call(K=8) == binding.ERR_SHAPE
+    assert call(K=264 - 1) == binding.ERR_SHAPE
+    assert call(K=136) == binding.ERR_SHAPE            # not a multiple of 16
+    assert call(M=-1) == binding.ERR_SHAPE
+    assert call(N=-5) == binding.ERR_SHAPE
+    assert call(M=1 << 31) == binding.ERR_SHAPE
+    assert call(M=0) == binding.OK                      # no-op
+    assert call(N=0) == binding.OK
+    assert call(M=0, A=0, out=0) == binding.OK         # no-op needs no buffers
+    assert call(A=0) == binding.ERR_NULL
+    assert call(Wq=0) == binding.ERR_NULL
+    assert call(scale=0) == binding.ERR_NULL
+    assert call(out=0) == binding.ERR_NULL
+    assert call(A=FAKE + 8) == binding.ERR_ALIGN
+    assert call(Wq=FAKE + (1 << 30) + 4) == binding.ERR_ALIGN
+    assert call(scale=FAKE + (2 << 30) + 1) == binding.ERR_ALIGN
+    assert call(out=FAKE + (3 << 30) + 1) == binding.ERR_ALIGN
+    assert call(out=FAKE) == binding.ERR_ALIAS           # out on top of A
+    assert call(out=FAKE + (1 << 30) + 1024) == binding.ERR_ALIAS   # inside Wq
+    # out's last 16 bytes reach into the scale grid
+    assert call(out=FAKE + (2 << 30) - 2 * 4 * 256 + 16) == binding.ERR_ALIAS
+
+
+def test_gemv_limits():
+    F = FAKE
+    args = (F, F + (1 << 30), F + (2 << 30), F + (3 << 30))
+    assert binding.gemv_raw(*args, 17, 256, 256, 0) == binding.ERR_SHAPE
+    assert binding.gemv_raw(*args, 4, 256, binding.GEMV_MAX_K_SMALL_M + 16, 0) == binding.ERR_SHAPE
+    assert binding.gemv_raw(*args, 5, 256, binding.GEMV_MAX_K + 16, 0) == binding.ERR_SHAPE
+
+
+def test_dequant_rejections():
+    F = FAKE
+    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30), 256, 256, 2, 0) == binding.ERR_ARG
+    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30), 256, 100, 0, 0) == binding.ERR_SHAPE
+    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30), 0, 256, 0, 0) == binding.OK
+    assert binding.dequant_raw(0, F + (1 << 30), F + (2 << 30), 256, 256, 0, 0) == binding.ERR_NULL
+    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30) + 4, 256, 256, 0, 0) == binding.ERR_ALIGN
+    assert binding.dequant_raw(F, F + (1 << 30), F, 256, 256, 0, 0) == binding.ERR_ALIAS
+
+
+def _cpu_operands(M=2, N=300, K=256):
+    A = torch.zeros((M, K), dtype=torch.bfloat16)
+    W = torch.zeros((N, K), dtype=torch.uint8)
+    S = torch.zeros(binding.scale_grid(N, K), dtype=torch.bfloat16)
+    return A, W, S
+
+
+def test_binding_refuses_wrong_layouts():
+    A, W, S = _cpu_operands()
+    N, K = W.shape
+    bad_scales = [
+        torch.zeros((N,), dtype=torch.bfloat16),                       # per-row [N]
+        torch.zeros((), dtype=torch.bfloat16),                         # scalar
+        torch.zeros((1,), dtype=torch.float32),                        # raw 4-byte scalar
+        torch.zeros(binding.scale_grid(N, K), dtype=torch.float32),    # fp32 grid
+        torch.zeros(binding.scale_grid(N, K)[::-1], dtype=torch.bfloat16),   # transposed shape
+        torch.zeros((3, 4), dtype=torch.bfloat16)[:, :2],              # right shape, not contiguous
+    ]
+    for s in bad_scales:
+        for fn in (binding.w8a16_gemv, binding.w8a16_gemm):
+            with pytest.raises(ValueError):
+                fn(A, W, s)
+    with pytest.raises(ValueError):
+        binding.w8a16_gemm(A.float(), W, S)                            # A not bf16
+    with pytest.raises(ValueError):
+        binding.w8a16_gemm(A, W.to(torch.int8), S)                     # not E4M3 bytes
+    with pytest.raises(ValueError):
+        binding.w8a16_gemm(A[:, :128], W, S)                           # K mismatch
+    with pytest.raises(ValueError):
+        binding.w8a16_gemv(torch.zeros((17, K), dtype=torch.bfloat16), W, S)
+    with pytest.raises(ValueError):
+        binding.w8a16_gemm(A, W, S)                                    # CPU tensors
+    with pytest.raises(ValueError):
+        binding.w8a16_dequant(W, S, mode=3)

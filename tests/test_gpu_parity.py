@@ -1,0 +1,293 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: bit-exact for the dequant-only path (E4M3 decode and scale indexing);
+for the products every checked element satisfies
+    |gpu - ref| <= 4e-3 * sum_k |A[m,k] * Wdeq[n,k]| + 1e-6
+(one BF16 output ulp plus fp32 reordering), with ref and the sum from the
+fp64 oracle on the same seeded inputs. Shapes the oracle finishes in seconds
+are checked on every element; the full prefill sizes on whole sampled rows,
+whole sampled columns and random points. Invariants with a unique answer
+(one-hot rows, zero weights, sign and power-of-two scaling, row permutation,
+run-to-run determinism) are checked bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_mamba_ssm_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+RTOL, ATOL = 4e-3, 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray, dtype, device):
+    raw = np.ascontiguousarray(a)
+    view = raw.view(np.int16) if raw.dtype == np.uint16 else raw
+    return torch.from_numpy(view.copy()).view(dtype).to(device)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def upload(A, W, S, device):
+    return (to_dev(A, torch.bfloat16, device), to_dev(W, torch.uint8, device),
+            to_dev(S, torch.bfloat16, device))
+
+
+def assert_within_tol(got_bits, ref, den, what):
+    g = oracle.bf16_value(got_bits)
+    tol = RTOL * den + ATOL
+    err = np.abs(g - ref)
+    bad = ~(err <= tol)
+    ratio = float(np.max(err / tol)) if err.size else 0.0
+    say(f"  {what}: {err.size} elements, max err/tol {ratio:.4f}")
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} elements outside tolerance; first {np.argwhere(bad)[:5].tolist()}"
+    return ratio
+
+
+def run(fn, A, W, S, device):
+    dA, dW, dS = upload(A, W, S, device)
+    out = fn(dA, dW, dS)
+    torch.cuda.synchronize()
+    return bf16_bits(out)
+
+
+# --- dequant-only path: bit-exact ---------------------------------------------
+
+def _all_codes_weights(N, K, seed):
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    W = finite[rng.integers(0, finite.size, (N, K))]
+    W.flat[:finite.size] = finite                          # every finite code at least once
+    return W
+
+
+def _distinct_scales(N, K, seed):
+    nb, kb = inputs.scale_grid(N, K)
+    rng = np.random.default_rng(seed)
+    vals = np.exp2(rng.integers(-20, 21, (nb, kb))) * (1 + rng.integers(0, 128, (nb, kb)) / 128)
+    S = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return S
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("N,K", [(300, 1040), (128, 128), (1, 16), (257, 4096)])
+def test_dequant_bit_exact(dev, mode, N, K):
+    say(f"dequant mode={mode} N={N} K={K}")
+    W = _all_codes_weights(N, K, N + K) if N * K >= 254 else np.full((N, K), 0xB9, np.uint8)
+    S = _distinct_scales(N, K, 7 * N + K)
+    dW, dS = to_dev(W, torch.uint8, dev), to_dev(S, torch.bfloat16, dev)
+    got = binding.w8a16_dequant(dW, dS, mode=mode)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    exact = oracle.dequant(W, S)
+    if mode == 0:
+        want = exact.astype(np.float32)                    # exact: e*s fits fp32
+        assert np.array_equal(want.astype(np.float64), exact)
+    else:
+        want = oracle.bf16_value(oracle.bf16_rne(exact)).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), \
+        f"{int((got.view(np.uint32) != want.view(np.uint32)).sum())} mismatching elements"
+
+
+# --- GEMV ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("workload", ["tiny_gemv", "decode_m1", "decode_m1_large"]
+                         + [f"multiseq_m{m}" for m in inputs.MULTISEQ_M])
+def test_gemv_workloads_every_element(dev, workload):
+    for p in inputs.WORKLOADS[workload]:
+        say(f"gemv {workload} {p.name} M={p.M} N={p.N} K={p.K}")
+        A, W, S = inputs.make(p)
+        got = run(binding.w8a16_gemv, A, W, S, dev)
+        ref, den = oracle.w8a16(A, W, S)
+        assert_within_tol(got, ref, den, f"{workload}/{p.name}")
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_gemv_every_m_ragged(dev, M):
+    N, K = 1000, 1040                       # ragged against 128-blocks, row groups and 1024-wide slices
+    say(f"gemv ragged M={M} N={N} K={K}")
+    A = inputs.activations(M, K, 500 + M)
+    W, S = inputs.weights(N, K, 0.02, 600 + M)
+    got = run(binding.w8a16_gemv, A, W, S, dev)
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(got, ref, den, f"gemv M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 300, 16384), (5, 300, 8192), (16, 129, 8192), (1, 7, 16),
+                                   (3, 1, 48), (1, 130, 3072), (2, 259, 12288)])
+def test_gemv_k_edges(dev, M, N, K):
+    say(f"gemv edge M={M} N={N} K={K}")
+    A = inputs.activations(M, K, 700 + K)
+    W, S = inputs.weights(N, K, 0.02, 800 + N)
+    got = run(binding.w8a16_gemv, A, W, S, dev)
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(got, ref, den, f"gemv M={M} N={N} K={K}")
+
+
+# --- GEMM ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 384, 256), (17, 130, 144), (127, 300, 272), (129, 1000, 1040),
+                                   (300, 257, 4096), (256, 256, 128), (1, 1, 16), (64, 4096, 512),
+                                   (513, 640, 1024), (130, 18560, 128)])
+def test_gemm_every_element(dev, M, N, K):
+    say(f"gemm M={M} N={N} K={K}")
+    A = inputs.activations(M, K, 900 + M)
+    W, S = inputs.weights(N, K, 0.02, 1000 + N + K)
+    got = run(binding.w8a16_gemm, A, W, S, dev)
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(got, ref, den, f"gemm M={M} N={N} K={K}")
+
+
+def _sample(M, N, seed, rows=4, cols=4, points=20000):
+    rng = np.random.default_rng(seed)
+    rs = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, rows - 2)]))
+    cs = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, cols - 2)]))
+    mi = [np.repeat(rs, N), np.repeat(np.arange(M), cs.size), rng.integers(0, M, points)]
+    ni = [np.tile(np.arange(N), rs.size), np.tile(cs, M), rng.integers(0, N, points)]
+    return np.concatenate(mi), np.concatenate(ni)
+
+
+@pytest.mark.parametrize("workload", ["prefill_1k", "prefill_8k_large"])
+def test_gemm_full_size_sampled(dev, workload):
+    for p in inputs.WORKLOADS[workload]:
+        say(f"gemm {workload} {p.name} M={p.M} N={p.N} K={p.K} (sampled)")
+        A, W, S = inputs.make(p)
+        got = run(binding.w8a16_gemm, A, W, S, dev)
+        mi, ni = _sample(p.M, p.N, p.seed_a)
+        ref, den = oracle.w8a16_points(A, W, S, mi, ni)
+        assert_within_tol(got[mi, ni], ref, den, f"{workload}/{p.name}")
+
+
+def test_gemv_matches_gemm_on_decode_shapes(dev):
+    for p in inputs.WORKLOADS["multiseq_m8"]:
+        A, W, S = inputs.make(p)
+        gv = run(binding.w8a16_gemv, A, W, S, dev)
+        gm = run(binding.w8a16_gemm, A, W, S, dev)
+        ref, den = oracle.w8a16(A, W, S)
+        assert_within_tol(gv, ref, den, "gemv")
+        assert_within_tol(gm, ref, den, "gemm")
+
+
+# --- invariants with a unique answer ------------------------------------------------
+
+ENTRY = {"gemv": binding.w8a16_gemv, "gemm": binding.w8a16_gemm}
+
+
+@pytest.mark.parametrize("entry,M", [("gemv", 4), ("gemv", 16), ("gemm", 130)])
+def test_one_hot_rows_return_rounded_dequantized_columns(dev, entry, M):
+    N, K = 300, 1040
+    W, S = inputs.weights(N, K, 0.02, 31)
+    A = np.zeros((M, K), np.uint16)
+    cols = (np.arange(M) * 97 + 5) % K
+    A[np.arange(M), cols] = 0x3F80
+    got = run(ENTRY[entry], A, W, S, dev)
+    want = oracle.bf16_rne(oracle.dequant(W, S)[:, cols].T)
+    # unique up to the sign of zero (a -0 weight times +1 may sum to +0)
+    assert np.array_equal(oracle.bf16_value(got), oracle.bf16_value(want))
+
+
+@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+def test_zero_weights_give_exact_zero(dev, entry):
+    A = inputs.activations(8, 1040, 41)
+    W, S = inputs.weights(300, 1040, 0.02, 42)
+    got = run(ENTRY[entry], A, np.zeros_like(W), S, dev)
+    assert np.all((got & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("entry,M", [("gemv", 6), ("gemm", 200)])
+def test_sign_scaling_permutation_and_determinism(dev, entry, M):
+    N, K = 520, 2048
+    A = inputs.activations(M, K, 51)
+    W, S = inputs.weights(N, K, 0.02, 52)
+    fn = ENTRY[entry]
+    base = run(fn, A, W, S, dev)
+    again = run(fn, A, W, S, dev)
+    assert np.array_equal(base, again), "not deterministic"
+    neg = run(fn, A ^ np.uint16(0x8000), W, S, dev)
+    assert np.array_equal(neg, base ^ np.uint16(0x8000)) or np.array_equal(
+        oracle.bf16_value(neg), -oracle.bf16_value(base))
+    A2 = np.where((A & 0x7FFF) == 0, A, A + np.uint16(0x80))   # A * 2 exactly
+    dbl = run(fn, A2, W, S, dev)
+    assert np.array_equal(oracle.bf16_value(dbl), 2 * oracle.bf16_value(base))
+    perm = np.random.default_rng(3).permutation(M)
+    got = run(fn, A[perm], W, S, dev)
+    assert np.array_equal(got, base[perm])
+
+
+@pytest.mark.parametrize("entry,M", [("gemv", 3), ("gemm", 150)])
+def test_scale_doubling_touches_only_its_block(dev, entry, M):
+    N, K = 300, 1040
+    A = inputs.activations(M, K, 61)
+    W, S = inputs.weights(N, K, 0.02, 62)
+    fn = ENTRY[entry]
+    base = run(fn, A, W, S, dev)
+    S2 = S.copy()
+    S2[1, 3] += 0x80                                  # x2 exactly
+    got = run(fn, A, W, S2, dev)
+    cols = np.zeros(N, bool)
+    cols[128:256] = True
+    assert np.array_equal(got[:, ~cols], base[:, ~cols])
+    ref, den = oracle.w8a16(A, W, S2)
+    assert_within_tol(got, ref, den, "scale x2")
+
+
+@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+def test_output_guard_band_untouched(dev, entry):
+    M, N, K = 5, 333, 1040
+    A = inputs.activations(M, K, 71)
+    W, S = inputs.weights(N, K, 0.02, 72)
+    dA, dW, dS = upload(A, W, S, dev)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), -7.0, dtype=torch.bfloat16, device=dev)
+    out = buf[pad:pad + M * N].view(M, N)
+    ENTRY[entry](dA, dW, dS, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == -7.0) and torch.all(buf[pad + M * N:] == -7.0)
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(bf16_bits(out), ref, den, f"{entry} into a view")
+
+
+@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+def test_empty_and_rejected_calls(dev, entry):
+    W, S = inputs.weights(256, 256, 0.02, 81)
+    dW, dS = to_dev(W, torch.uint8, dev), to_dev(S, torch.bfloat16, dev)
+    out = ENTRY[entry](torch.empty((0, 256), dtype=torch.bfloat16, device=dev), dW, dS)
+    assert tuple(out.shape) == (0, 256)
+    dA = torch.ones((2, 256), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        ENTRY[entry](dA, dW, dS.reshape(-1))           # wrong scale layout refused before launch
+    st = (binding.gemv_raw if entry == "gemv" else binding.gemm_raw)(
+        dA.data_ptr(), dW.data_ptr(), dS.data_ptr(), dA.data_ptr(), 2, 256, 256, 0)
+    assert st == binding.ERR_ALIAS
+    torch.cuda.synchronize()
+
+
+def test_stream_ordering(dev):
+    """The call is enqueued on the caller's stream and ordered with other work on it."""
+    p = inputs.WORKLOADS["tiny_gemv"][0]
+    A, W, S = inputs.make(p)
+    dA, dW, dS = upload(A, W, S, dev)
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        out = torch.full((1, p.N), 3.0, dtype=torch.bfloat16, device=dev)
+        binding.w8a16_gemv(dA, dW, dS, out=out)
+        res = out.clone()
+    s.synchronize()
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(bf16_bits(res), ref, den, "stream")
