@@ -1,0 +1,268 @@
+"""Benchmark of the w8a16 block-scaled FP8 projections on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+  * decode: one token through LAYERS layers of the Mamba-2 projections, i.e.
+    LAYERS in_proj GEMVs (M=1, K=4096, N=18560) and LAYERS out_proj GEMVs
+    (M=1, K=8192, N=4096), each layer with its own weight copy, and
+  * prefill: one 1024-token prompt through in_proj and out_proj with the
+    prefill GEMM (M=1024),
+on seeded random inputs (A ~ N(0,1) BF16; weights N(0, 0.02) quantized per
+128x128 block to E4M3 with BF16 scales). Inputs are resident in HBM before
+timing starts. The weight copies (layers) rotate over more than 1 GB, so
+every GEMV reads its weights from HBM rather than from the 256 MB Infinity
+Cache, as decode over a real layer stack does.
+
+The JSON line reports the decode GEMV's HBM bandwidth as `value` (GB/s over
+both projections: algorithmic bytes / kernel time) and the prefill GEMM's
+TFLOP/s under `prefill`, each with a roofline object for its larger
+(in_proj) kernel. Kernel times come from HIP events on the launch stream:
+the GEMVs of one projection run back to back between two events (so the
+average launch duration is not inflated by per-event overhead), the GEMMs
+each between their own two events. `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workloads.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from gemm_mamba_ssm_amd import binding, inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+ROTATE_BYTES = 1.2e9            # weight copies per projection span at least this much
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "gemv": ["gemm_mamba_ssm_amd/csrc/w8a16_gemv.hip", "gemm_mamba_ssm_amd/csrc/w8a16_device.h"],
+    "gemm": ["gemm_mamba_ssm_amd/csrc/w8a16_gemm.hip", "gemm_mamba_ssm_amd/csrc/w8a16_device.h"],
+}
+METRIC = "M=1 GEMV HBM GB/s (%peak) + 1k-token prefill GEMM TFLOP/s (%MFMA peak)"
+
+
+def source_digest(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str, launch: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when missing or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("kernels", {}).get(launch)
+    if not entry or entry.get("source_digest") != source_digest(kind):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def to_dev(a: np.ndarray, dtype, device):
+    raw = np.ascontiguousarray(a)
+    view = raw.view(np.int16) if raw.dtype == np.uint16 else raw
+    return torch.from_numpy(view.copy()).view(dtype).to(device)
+
+
+class Projection:
+    """Device buffers of one projection: rotating weight copies, decode and prefill operands."""
+
+    def __init__(self, p_dec, p_pre, device):
+        assert (p_dec.N, p_dec.K, p_dec.seed_w) == (p_pre.N, p_pre.K, p_pre.seed_w)
+        self.p_dec, self.p_pre = p_dec, p_pre
+        A1, W, S = inputs.make(p_dec)
+        Ap, _, _ = inputs.make(p_pre)
+        wq = to_dev(W, torch.uint8, device)
+        sc = to_dev(S, torch.bfloat16, device)
+        self.copies = max(2, math.ceil(ROTATE_BYTES / W.nbytes))   # distinct layers' weights
+        self.W = [wq] + [wq.clone() for _ in range(self.copies - 1)]
+        self.S = [sc] + [sc.clone() for _ in range(self.copies - 1)]
+        self.A1 = to_dev(A1, torch.bfloat16, device)
+        self.Ap = to_dev(Ap, torch.bfloat16, device)
+        self.out1 = torch.empty((p_dec.M, p_dec.N), dtype=torch.bfloat16, device=device)
+        self.outp = torch.empty((p_pre.M, p_pre.N), dtype=torch.bfloat16, device=device)
+
+    def gemv(self, i, stream):
+        return binding.gemv_raw(self.A1.data_ptr(), self.W[i % self.copies].data_ptr(),
+                                self.S[i % self.copies].data_ptr(), self.out1.data_ptr(),
+                                self.p_dec.M, self.p_dec.N, self.p_dec.K, stream)
+
+    def gemm(self, i, stream):
+        return binding.gemm_raw(self.Ap.data_ptr(), self.W[i % self.copies].data_ptr(),
+                                self.S[i % self.copies].data_ptr(), self.outp.data_ptr(),
+                                self.p_pre.M, self.p_pre.N, self.p_pre.K, stream)
+
+
+def cpu_baseline(budget_s: float):
+    """Time the CPU oracle on a bounded sample of the same two workloads."""
+    import oracle
+
+    cores = oracle.num_threads()
+    dec = inputs.WORKLOADS["decode_m1"]
+    pre = inputs.WORKLOADS["prefill_1k"]
+    # decode: whole M=1 in_proj + out_proj products, repeated within half the budget
+    ops = [(inputs.make(p), p) for p in dec]
+    t0 = time.perf_counter()
+    reps, nbytes = 0, 0
+    while True:
+        for (A, W, S), p in ops:
+            oracle.w8a16(A, W, S)
+            nbytes += p.bytes_moved()
+        reps += 1
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    t_dec = time.perf_counter() - t0
+    # prefill: whole output rows of the M=1024 in_proj (each row = N*K MACs)
+    (A, W, S), p = inputs.make(pre[0]), pre[0]
+    t0 = time.perf_counter()
+    rows, flops = 0, 0
+    while time.perf_counter() - t0 < budget_s / 2 and rows < p.M:
+        take = min(8, p.M - rows)
+        mi = np.repeat(np.arange(rows, rows + take), p.N)
+        ni = np.tile(np.arange(p.N), take)
+        oracle.w8a16_points(A, W, S, mi, ni)
+        rows += take
+        flops += 2 * take * p.N * p.K
+    t_pre = time.perf_counter() - t0
+    return {
+        "value": round(nbytes / t_dec / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": f"{reps} whole M=1 decode passes (in_proj + out_proj) in {t_dec:.1f} s",
+        "prefill": {"value": round(flops / t_pre / 1e12, 5), "unit": "TFLOP/s",
+                    "sample": f"{rows} whole output rows of the M=1024 in_proj in {t_pre:.1f} s"},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    ap.add_argument("--layers", type=int, default=8, help="decode layers (weight copies) per step")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with a plain device copy of 256 MiB (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (HIP device)", file=sys.stderr)
+        sys.exit(2)
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    binding.load()
+
+    dec, pre = inputs.WORKLOADS["decode_m1"], inputs.WORKLOADS["prefill_1k"]
+    projs = [Projection(dec[i], pre[i], device) for i in range(2)]
+    stream = torch.cuda.current_stream(device)
+    sh = stream.cuda_stream
+    torch.cuda.synchronize()
+
+    L = args.layers
+
+    def check(st, kind):
+        if st != binding.OK:
+            raise binding.W8A16Error(f"w8a16_{kind}", st)
+
+    def step(i, ev=None):
+        # ev: 5 events -> [decode in_proj x L][decode out_proj x L][prefill in][prefill out]
+        mark = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        mark(0)
+        for l in range(L):
+            check(projs[0].gemv(i * L + l, sh), "gemv")
+        mark(1)
+        for l in range(L):
+            check(projs[1].gemv(i * L + l, sh), "gemv")
+        mark(2)
+        check(projs[0].gemm(i, sh), "gemm")
+        mark(3)
+        check(projs[1].gemm(i, sh), "gemm")
+        mark(4)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=device)   # 256 MiB read, 256 MiB written
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+
+    dur = np.array([[ev[j].elapsed_time(ev[j + 1]) * 1e-3 for j in range(4)] for ev in events])
+    dur[:, :2] /= L                                  # per GEMV launch
+    mean = dur.mean(axis=0)                          # seconds per launch: gemv in, gemv out, gemm in, gemm out
+    b_in, b_out = projs[0].p_dec.bytes_moved(), projs[1].p_dec.bytes_moved()
+    f_in, f_out = projs[0].p_pre.flops(), projs[1].p_pre.flops()
+    gemv_gbs = (b_in + b_out) / (mean[0] + mean[1]) / 1e9
+    gemm_tfs = (f_in + f_out) / (mean[2] + mean[3]) / 1e12
+
+    def roof(bound, achieved, peak, unit, traffic):
+        return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gemv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x e4m3 -> fp32 accumulate -> bf16",
+        "data": "synthetic (seeded N(0,1) activations; N(0,0.02) weights quantized per 128x128 block to E4M3 + BF16 scales)",
+        "config": {
+            "workload": "decode_m1 + prefill_1k: Mamba-2 (hidden 4096) in_proj K=4096 N=18560 and "
+                        "out_proj K=8192 N=4096; decode GEMV M=1, prefill GEMM M=1024",
+            "decode_layers_per_step": L,
+            "weight_copies_rotated": [p.copies for p in projs],
+            "timing": "HIP events on the launch stream; GEMVs timed over L back-to-back launches",
+        },
+        "frac_of_hbm_peak": round(gemv_gbs / HBM_PEAK_GBS, 4),
+        "kernel_us": {"gemv_in_proj": round(mean[0] * 1e6, 3), "gemv_out_proj": round(mean[1] * 1e6, 3),
+                      "gemm_in_proj": round(mean[2] * 1e6, 3), "gemm_out_proj": round(mean[3] * 1e6, 3)},
+        "roofline": roof("hbm", b_in / mean[0] / 1e9, HBM_PEAK_GBS, "GB/s",
+                         measured_traffic("gemv", "gemv_in_proj")),
+        "prefill": {
+            "value": round(gemm_tfs, 2), "unit": "TFLOP/s",
+            "frac_of_mfma_peak": round(gemm_tfs / BF16_PEAK_TFLOPS, 4),
+            "roofline": roof("mfma", f_in / mean[2] / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s",
+                             measured_traffic("gemm", "gemm_in_proj")),
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,8 +27,8 @@ EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_dequant", "w8a16_strerror")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ALIAS, ERR_ARG = 0, -1, -2, -3, -4, -5, -6
 GEMV_MAX_M = 16
-GEMV_MAX_K_SMALL_M = 16384   # M <= 4
-GEMV_MAX_K = 8192            # M >= 5
+GEMV_MAX_K_SMALL_M = 16384   # M <= 8
+GEMV_MAX_K = 8192            # M >= 9
 
 _lib = None
 
@@ -55,7 +55,7 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
         fn.argtypes = [P, P, P, P, I64, I64, I64, P]
     lib.w8a16_dequant.restype = ctypes.c_int
-    lib.w8a16_dequant.argtypes = [P, P, P, I64, I64, ctypes.c_int, P]
+    lib.w8a16_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.w8a16_strerror.restype = ctypes.c_char_p
     lib.w8a16_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -76,8 +76,8 @@ def gemm_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: int, stre
     return load().w8a16_gemm(A, Wq, scale, out, M, N, K, stream)
 
 
-def dequant_raw(Wq: int, scale: int, out: int, N: int, K: int, mode: int, stream: int = 0) -> int:
-    return load().w8a16_dequant(Wq, scale, out, N, K, mode, stream)
+def dequant_raw(Wq: int, scale: int, out: int, N: int, K: int, stream: int = 0) -> int:
+    return load().w8a16_dequant(Wq, scale, out, N, K, stream)
 
 
 # --- torch tensors ------------------------------------------------------------
@@ -157,10 +157,9 @@ def w8a16_gemm(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
 
 
 def w8a16_dequant(Wq: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None,
-                  mode: int = 0, stream=None) -> torch.Tensor:
-    """Dequantize only (test path): FP32 [N, K]; mode 0 = E4M3*s, mode 1 = bf16(E4M3*s)."""
+                  stream=None) -> torch.Tensor:
+    """Dequantize only (test path): FP32 [N, K] = E4M3(Wq) * block scale, exact."""
     N, K = _check_weights(Wq, scale)
-    _need(mode in (0, 1), f"mode must be 0 or 1, got {mode}")
     if out is None:
         _check_device(Wq, scale)
         out = torch.empty((N, K), dtype=torch.float32, device=Wq.device)
@@ -169,7 +168,7 @@ def w8a16_dequant(Wq: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | Non
               f"out must be a contiguous float32 [{N}, {K}] tensor")
         _check_device(Wq, scale, out)
     with torch.cuda.device(Wq.device):
-        st = load().w8a16_dequant(Wq.data_ptr(), scale.data_ptr(), out.data_ptr(), N, K, mode,
+        st = load().w8a16_dequant(Wq.data_ptr(), scale.data_ptr(), out.data_ptr(), N, K,
                                   _stream_handle(Wq.device, stream))
     if st != OK:
         raise W8A16Error("w8a16_dequant", st)

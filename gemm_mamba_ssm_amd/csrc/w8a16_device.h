@@ -50,26 +50,6 @@ __device__ __forceinline__ void e4m3x16_to_bf16(u32x4_t w, bf16x2_t (&out)[8]) {
     }
 }
 
-// Two E4M3 codes times a block scale, rounded once to BF16:
-// bf16_rne(E4M3 * s). The E4M3 -> fp32 convert is exact, so is the fp32
-// product (4 + 8 significant bits), and v_cvt_pk_bf16_f32 rounds it once.
-__device__ __forceinline__ uint32_t e4m3x2_scaled_to_bf16(uint32_t w, bool hi, float s) {
-    f32x2_t f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true)
-                   : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    f.x *= s;
-    f.y *= s;
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-// 16 E4M3 codes scaled by s -> 16 BF16 (bf16_rne(e * s)), as 8 packed pairs.
-__device__ __forceinline__ void e4m3x16_scaled_to_bf16(u32x4_t w, float s, uint32_t (&out)[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        out[2 * i] = e4m3x2_scaled_to_bf16(w[i], false, s);
-        out[2 * i + 1] = e4m3x2_scaled_to_bf16(w[i], true, s);
-    }
-}
-
 // DPP lane moves (within rows of 16 lanes). Controls from the GCN/CDNA DPP encoding.
 constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]

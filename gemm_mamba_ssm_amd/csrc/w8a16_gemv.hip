@@ -7,21 +7,25 @@
 // multi-sequence decode applies one weight pass to all rows
 // (TransformerLayer docs, `decode_multi_seq`).
 //
-// The GEMV is HBM-bound: each weight byte is read exactly once per call. The
-// layout that follows from that on CDNA4:
-//  * A workgroup holds `nwaves` wavefronts; wave w owns the K-slice
-//    [w*1024*J, (w+1)*1024*J). Lane l of that wave owns the 16-value chunks
-//    k = slice + j*1024 + 16*l (j < J), so one wave-wide 16-byte load covers
-//    1 KB of a weight row, fully coalesced.
-//  * The lane's activations for its chunks (MR rows x J chunks x 16 BF16)
-//    stay in registers for the whole kernel; the weight rows stream past.
+// The GEMV is HBM-bound: each weight byte is read exactly once per call, so
+// the design is about keeping enough 16-byte loads in flight on every CU:
+//  * K is split across the `kw` waves of a workgroup: wave w owns
+//    k in [w*1024*J, (w+1)*1024*J), and lane l of it the 16-value chunks
+//    k = w*1024*J + j*1024 + 16*l (j < J). One wave-wide load covers 1 KB of a
+//    weight row, fully coalesced. The lane's activations for its chunks
+//    (MR x J x 16 BF16) stay in registers for the whole kernel.
+//  * Each workgroup streams a contiguous range of row groups (RB rows each);
+//    the loads of the next group are issued before the current one is
+//    reduced (two register buffers), and the grid is sized so every CU holds
+//    several workgroups.
 //  * Each 16-byte weight chunk is decoded once (8 packed E4M3->BF16
 //    converts, exact) and used for all MR rows with v_dot2_f32_bf16. A chunk
 //    lies inside one 128-wide scale block, so its 16-term partial sum is
 //    multiplied by that block's scale in fp32 (exact dequantization).
-//  * Partial sums are reduced across the 64 lanes with DPP row operations and
-//    across the waves of the workgroup through LDS, always in the same order,
-//    so results are deterministic. No atomics.
+//  * The RB*MR partial sums of a lane are reduced across the wave with a
+//    butterfly that halves the value count at every step (so the cost per
+//    output shrinks as RB*MR grows), then across the kw waves through LDS.
+//    The order of every sum is fixed: results are deterministic. No atomics.
 #include "w8a16_device.h"
 #include "w8a16_host.h"
 
@@ -30,31 +34,150 @@ namespace {
 
 constexpr int kChunk = 16;             // K values (bytes of W) per lane per load
 constexpr int kWaveK = 64 * kChunk;    // K values covered by one wave-wide load
-constexpr int kMaxWaves = 8;      // 512 threads: up to 256 VGPRs per lane
+constexpr int kMaxWaves = 8;           // 512 threads: up to 256 VGPRs per lane
+constexpr int kWavesPerCu = 8;         // resident waves per CU the grid aims for
+
+constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
+constexpr int log2i(int v) { return v <= 1 ? 0 : 1 + log2i(v / 2); }
+
+// Butterfly reduction of COUNT values per lane over the 64 lanes. At each
+// distance D the lanes with bit D set keep the upper half of the values and
+// the others the lower half; each adds its partner's copy of the half it
+// keeps. Once one value is left the remaining distances add plainly. Lane l
+// ends with the wave-wide sum of value index l >> (6 - log2(P)).
+template <int P, int COUNT, int D>
+__device__ __forceinline__ void butterfly(float (&v)[P], int lane) {
+    if constexpr (D >= 1) {
+        if constexpr (COUNT > 1) {
+            const bool upper = (lane & D) != 0;
+#pragma unroll
+            for (int i = 0; i < COUNT / 2; ++i) {
+                const float keep = upper ? v[i + COUNT / 2] : v[i];
+                const float send = upper ? v[i] : v[i + COUNT / 2];
+                v[i] = keep + __shfl_xor(send, D);
+            }
+            butterfly<P, COUNT / 2, D / 2>(v, lane);
+        } else {
+            v[0] += __shfl_xor(v[0], D);
+            butterfly<P, 1, D / 2>(v, lane);
+        }
+    }
+}
+
+template <int MR, int J, int RB>
+struct Gemv {
+    static constexpr int V = RB * MR;          // partial sums per lane per group
+    static constexpr int P = pow2_ceil(V);     // padded to a power of two for the butterfly
+    static_assert(P <= 64, "at most one output per lane");
+    static_assert(kScaleBlock % RB == 0, "a row group must stay inside one scale block");
+    static constexpr int kLaneShift = 6 - log2i(P);   // lane l holds value l >> kLaneShift
+
+    struct Regs {
+        u32x4_t w[RB][J];
+        float s[J];
+    };
+
+    __device__ static __forceinline__ void load(Regs& r, const uint8_t* __restrict__ W,
+                                                const uint16_t* __restrict__ S, int g, int N, int K,
+                                                int k_blocks, const int (&kch)[J], const bool (&kvalid)[J]) {
+        const int n0 = g * RB;
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                if (n0 + i < N && kvalid[j])
+                    r.w[i][j] = load_stream16(W + static_cast<int64_t>(n0 + i) * K + kch[j]);
+                else
+                    r.w[i][j] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+        // All RB rows sit in scale row-block n0/128.
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            r.s[j] = kvalid[j] ? bf16_bits_to_f32(S[scale_index(n0, kch[j], k_blocks)]) : 0.0f;
+    }
+
+    __device__ static __forceinline__ void process(const Regs& r, const uint32_t (&a)[MR][J][8],
+                                                   float (*red)[kMaxWaves][V], int parity,
+                                                   uint16_t* __restrict__ out, int g, int N,
+                                                   int lane, int wave, int nwaves) {
+        float v[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) v[i] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                bf16x2_t wv[8];
+                e4m3x16_to_bf16(r.w[i][j], wv);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    float p = 0.0f;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        p = __builtin_amdgcn_fdot2_f32_bf16(
+                            wv[t], __builtin_bit_cast(bf16x2_t, a[m][j][t]), p, false);
+                    v[i * MR + m] = fmaf(p, r.s[j], v[i * MR + m]);
+                }
+            }
+        butterfly<P, P, 32>(v, lane);
+
+        const int idx = lane >> kLaneShift;                       // value this lane now holds
+        const bool holder = (lane & ((1 << kLaneShift) - 1)) == 0 && idx < V;
+        const int n0 = g * RB;
+        if (nwaves == 1) {
+            if (holder) {
+                const int i = idx / MR, m = idx % MR;
+                if (n0 + i < N) out[static_cast<int64_t>(m) * N + n0 + i] = f32_to_bf16_bits(v[0]);
+            }
+        } else {
+            if (holder) red[parity][wave][idx] = v[0];
+            __syncthreads();
+            if (wave == 0 && lane < V) {
+                float tot = 0.0f;
+                for (int w = 0; w < nwaves; ++w) tot += red[parity][w][lane];
+                const int i = lane / MR, m = lane % MR;
+                if (n0 + i < N) out[static_cast<int64_t>(m) * N + n0 + i] = f32_to_bf16_bits(tot);
+            }
+            // The next group writes red[parity ^ 1]; red[parity] is written
+            // again only after the next barrier, which wave 0 reaches after
+            // it has read red[parity].
+        }
+    }
+};
 
 template <int MR, int J, int RB>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             const uint16_t* __restrict__ S, uint16_t* __restrict__ out,
             int N, int K, int groups_per_block) {
-    static_assert(kScaleBlock % RB == 0, "a row group must stay inside one scale block");
-    static_assert(RB * MR <= 64, "one output per lane after the reduction");
-    __shared__ float red[2][kMaxWaves][RB * MR];
+    using G = Gemv<MR, J, RB>;
+    __shared__ float red[2][kMaxWaves][G::V];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
     const int k_blocks = (K + kScaleBlock - 1) / kScaleBlock;
-    const int k_wave = wave * (kWaveK * J);
+
+    const int groups = (N + RB - 1) / RB;
+    const int g_begin = blockIdx.x * groups_per_block;
+    const int g_end = min(groups, g_begin + groups_per_block);
+    if (g_begin >= g_end) return;                              // uniform over the workgroup
+
+    int kch[J];
+    bool kvalid[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        kch[j] = wave * (kWaveK * J) + j * kWaveK + lane * kChunk;
+        kvalid[j] = kch[j] < K;
+    }
+
+    typename G::Regs ra, rb;
+    G::load(ra, W, S, g_begin, N, K, k_blocks, kch, kvalid);
 
     // Activations of this lane's chunks, as packed BF16 pairs (k, k+1).
     uint32_t a[MR][J][8];
-    bool kvalid[J];
-    int kch[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        kch[j] = k_wave + j * kWaveK + lane * kChunk;
-        kvalid[j] = kch[j] < K;
+    for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
@@ -69,138 +192,75 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
                 a[m][j][4 + t] = hi[t];
             }
         }
-    }
 
-    const int groups = (N + RB - 1) / RB;
-    const int g_begin = blockIdx.x * groups_per_block;
-    const int g_end = min(groups, g_begin + groups_per_block);
     int parity = 0;
-    for (int g = g_begin; g < g_end; ++g, parity ^= 1) {
-        const int n0 = g * RB;
-
-        u32x4_t w[RB][J];
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                if (n0 + r < N && kvalid[j])
-                    w[r][j] = load_stream16(W + static_cast<int64_t>(n0 + r) * K + kch[j]);
-                else
-                    w[r][j] = u32x4_t{0u, 0u, 0u, 0u};
-            }
-        // All RB rows sit in scale row-block n0/128 (RB divides 128).
-        float s[J];
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-            s[j] = kvalid[j] ? bf16_bits_to_f32(S[scale_index(n0, kch[j], k_blocks)]) : 0.0f;
-
-        float acc[RB][MR];
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int m = 0; m < MR; ++m) acc[r][m] = 0.0f;
-
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                bf16x2_t wv[8];
-                e4m3x16_to_bf16(w[r][j], wv);
-#pragma unroll
-                for (int m = 0; m < MR; ++m) {
-                    float p = 0.0f;
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        p = __builtin_amdgcn_fdot2_f32_bf16(
-                            wv[t], __builtin_bit_cast(bf16x2_t, a[m][j][t]), p, false);
-                    acc[r][m] = fmaf(p, s[j], acc[r][m]);
-                }
-            }
-
-        // Lane t ends up holding output t = r*MR + m of this group.
-        float mine = 0.0f;
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                const float v = wave_sum(acc[r][m]);
-                if (lane == r * MR + m) mine = v;
-            }
-
-        if (nwaves == 1) {
-            if (lane < RB * MR) {
-                const int r = lane / MR, m = lane % MR;
-                if (n0 + r < N)
-                    out[static_cast<int64_t>(m) * N + n0 + r] = f32_to_bf16_bits(mine);
-            }
-        } else {
-            if (lane < RB * MR) red[parity][wave][lane] = mine;
-            __syncthreads();
-            if (wave == 0 && lane < RB * MR) {
-                float tot = 0.0f;
-                for (int v = 0; v < nwaves; ++v) tot += red[parity][v][lane];
-                const int r = lane / MR, m = lane % MR;
-                if (n0 + r < N)
-                    out[static_cast<int64_t>(m) * N + n0 + r] = f32_to_bf16_bits(tot);
-            }
-            // The next group writes red[parity ^ 1]; red[parity] is rewritten
-            // only after the next barrier, which wave 0 reaches after reading it.
-        }
+    for (int g = g_begin; g < g_end; g += 2) {
+        if (g + 1 < g_end) G::load(rb, W, S, g + 1, N, K, k_blocks, kch, kvalid);
+        G::process(ra, a, red, parity, out, g, N, lane, wave, nwaves);
+        parity ^= 1;
+        if (g + 1 >= g_end) break;
+        if (g + 2 < g_end) G::load(ra, W, S, g + 2, N, K, k_blocks, kch, kvalid);
+        G::process(rb, a, red, parity, out, g + 1, N, lane, wave, nwaves);
+        parity ^= 1;
     }
 }
 
 typedef void (*gemv_fn)(const uint16_t*, const uint8_t*, const uint16_t*, uint16_t*, int, int, int);
 
-// Largest chunk count per lane that keeps MR*J*8 activation registers <= 64.
-constexpr int max_chunks(int mr) { return mr == 1 ? 8 : mr == 2 ? 4 : mr <= 4 ? 2 : 1; }
+// Chunks per lane: 1 while K <= 8192 (8 waves of 1024), 2 up to 16384 (M <= 8).
+constexpr int max_chunks(int mr) { return mr <= 8 ? 2 : 1; }
 
-// W rows per iteration: about 16 loads in flight per lane, at most 64 partial
-// sums (32 when MR > 8, where the activations already take 72-128 registers).
-constexpr int rows_per_iter(int mr, int j) {
+// Rows per group: up to 16 loads per lane per buffer, at most 64 partial sums
+// per lane, and a power of two (so a group never straddles a scale block).
+constexpr int rows_per_group(int mr, int j) {
     int rb = 16 / j;
-    rb = rb < 2 ? 2 : (rb > 8 ? 8 : rb);
-    while (rb * mr > (mr > 8 ? 32 : 64)) rb /= 2;
+    while (rb * mr > 64 && rb > 1) rb /= 2;
+    if (mr * j * 8 >= 64 && rb * j > 8) rb = 8 / j;   // big activation footprint: 8 loads per buffer
     return rb;
 }
 
 template <int MR, int J>
 gemv_fn pick_j() {
-    return &gemv_kernel<MR, J, rows_per_iter(MR, J)>;
+    return &gemv_kernel<MR, J, rows_per_group(MR, J)>;
 }
 
 template <int MR>
 gemv_fn pick(int j) {
-    if constexpr (max_chunks(MR) >= 8)
-        if (j == 8) return pick_j<MR, 8>();
-    if constexpr (max_chunks(MR) >= 4)
-        if (j == 4) return pick_j<MR, 4>();
     if constexpr (max_chunks(MR) >= 2)
         if (j == 2) return pick_j<MR, 2>();
     return pick_j<MR, 1>();
 }
 
-gemv_fn select_kernel(int mr, int j) {
-    switch (mr) {
-        case 1: return pick<1>(j);
-        case 2: return pick<2>(j);
-        case 3: return pick<3>(j);
-        case 4: return pick<4>(j);
-        case 5: return pick<5>(j);
-        case 6: return pick<6>(j);
-        case 7: return pick<7>(j);
-        case 8: return pick<8>(j);
-        case 9: return pick<9>(j);
-        case 10: return pick<10>(j);
-        case 11: return pick<11>(j);
-        case 12: return pick<12>(j);
-        case 13: return pick<13>(j);
-        case 14: return pick<14>(j);
-        case 15: return pick<15>(j);
-        default: return pick<16>(j);
-    }
+struct Choice {
+    gemv_fn fn;
+    int rows_per_group;
+};
+
+template <int MR>
+Choice choose(int j) {
+    return {pick<MR>(j), j == 2 ? rows_per_group(MR, 2) : rows_per_group(MR, 1)};
 }
 
-int rows_per_iter_rt(int mr, int j) { return rows_per_iter(mr, j); }
+Choice select_kernel(int mr, int j) {
+    switch (mr) {
+        case 1: return choose<1>(j);
+        case 2: return choose<2>(j);
+        case 3: return choose<3>(j);
+        case 4: return choose<4>(j);
+        case 5: return choose<5>(j);
+        case 6: return choose<6>(j);
+        case 7: return choose<7>(j);
+        case 8: return choose<8>(j);
+        case 9: return choose<9>(j);
+        case 10: return choose<10>(j);
+        case 11: return choose<11>(j);
+        case 12: return choose<12>(j);
+        case 13: return choose<13>(j);
+        case 14: return choose<14>(j);
+        case 15: return choose<15>(j);
+        default: return choose<16>(j);
+    }
+}
 
 }  // namespace
 }  // namespace w8a16
@@ -211,23 +271,22 @@ extern "C" int w8a16_gemv(const void* A, const void* Wq, const void* scale, void
     bool noop = false;
     int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
     if (st != W8A16_OK || noop) return st;
-    if (M > W8A16_GEMV_MAX_M || K > (M <= 4 ? W8A16_GEMV_MAX_K_SMALL_M : W8A16_GEMV_MAX_K))
+    if (M > W8A16_GEMV_MAX_M || K > (M <= 8 ? W8A16_GEMV_MAX_K_SMALL_M : W8A16_GEMV_MAX_K))
         return W8A16_ERR_SHAPE;
 
     const int mr = static_cast<int>(M);
-    const int jneed = static_cast<int>(ceil_div(K, kWaveK));
-    int j = 1;
-    while (j < jneed && j < max_chunks(mr)) j *= 2;
+    const int j = K > static_cast<int64_t>(kWaveK) * kMaxWaves ? 2 : 1;
     const int nwaves = static_cast<int>(ceil_div(K, static_cast<int64_t>(kWaveK) * j));
-    if (nwaves > kMaxWaves) return W8A16_ERR_SHAPE;
-    const int rb = rows_per_iter_rt(mr, j);
+    if (nwaves > kMaxWaves || j > max_chunks(mr)) return W8A16_ERR_SHAPE;
+    const Choice c = select_kernel(mr, j);
 
-    const int64_t groups = ceil_div(N, rb);
-    const int64_t target_blocks = static_cast<int64_t>(device_cu_count()) * 32 / nwaves;
-    const int64_t per_block = ceil_div(groups, target_blocks < 1 ? 1 : target_blocks);
+    const int64_t groups = ceil_div(N, c.rows_per_group);
+    const int64_t resident = static_cast<int64_t>(device_cu_count()) *
+                             (kWavesPerCu / nwaves > 0 ? kWavesPerCu / nwaves : 1);
+    const int64_t per_block = ceil_div(groups, resident);
     const int64_t blocks = ceil_div(groups, per_block);
 
-    return launch(select_kernel(mr, j), dim3(static_cast<unsigned>(blocks)), dim3(64 * nwaves),
+    return launch(c.fn, dim3(static_cast<unsigned>(blocks)), dim3(64 * nwaves),
                   static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(A),
                   static_cast<const uint8_t*>(Wq), static_cast<const uint16_t*>(scale),
                   static_cast<uint16_t*>(out), static_cast<int>(N), static_cast<int>(K),

@@ -49,11 +49,11 @@ enum w8a16_status {
     W8A16_ERR_ALIGN = -3,  /* A or Wq not 16-byte aligned; scale/out not 2-byte */
     W8A16_ERR_LAUNCH = -4, /* the HIP launch failed                             */
     W8A16_ERR_ALIAS = -5,  /* out overlaps an input                             */
-    W8A16_ERR_ARG = -6     /* another argument is invalid (e.g. dequant mode)   */
+    W8A16_ERR_ARG = -6     /* another argument is invalid                       */
 };
 
 /* Largest M the GEMV entry point accepts, and its largest K: 16384 when
- * M <= 4, 8192 otherwise (w8a16_gemm takes any M and K). */
+ * M <= 8, 8192 otherwise (w8a16_gemm takes any M and K). */
 #define W8A16_GEMV_MAX_M 16
 #define W8A16_GEMV_MAX_K_SMALL_M 16384
 #define W8A16_GEMV_MAX_K 8192
@@ -62,7 +62,7 @@ enum w8a16_status {
  * Decode GEMV: one or a few tokens (TransformerLayer docs, `decode`: a
  * [1, hidden] BF16 row per token; `decode_multi_seq`: N sequences with the
  * weights read once for all of them). 1 <= M <= 16, N >= 0, K % 16 == 0,
- * 16 <= K <= 16384 for M <= 4 and 16 <= K <= 8192 for M >= 5.
+ * 16 <= K <= 16384 for M <= 8 and 16 <= K <= 8192 for M >= 9.
  * M == 0 or N == 0 is a no-op returning W8A16_OK.
  * Each weight byte is read from HBM once per call for all M rows.
  */
@@ -72,24 +72,23 @@ int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
 /*
  * Prefill GEMM: M prompt tokens at once (TransformerLayer docs, `prefill`:
  * the weights are read once for all N tokens as one GEMM with M = N).
- * M >= 0 (any), N >= 0, K >= 16, K % 16 == 0; M == 0 or N == 0 is a no-op.
- * Each weight tile is converted to BF16 once per staged tile and shared by
- * all rows of the output tile.
+ * M >= 0 (any), N >= 0, 16 <= K < 2^23, K % 16 == 0; M == 0 or N == 0 is a
+ * no-op. The E4M3 weight bytes of a tile are staged once per workgroup and
+ * decoded in registers; the block scale is applied in fp32 per 128-wide
+ * k-block, as in the GEMV.
  */
 int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
                int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Dequantize only (a test path that exposes the device E4M3 decode and the
- * scale indexing the two entry points above use). out is FP32 [N][K]:
- *   mode 0: out[n][k] = float(E4M3(Wq[n][k])) * scale[n/128][k/128]
- *           (exact; the GEMV's decode, which applies the scale in fp32)
- *   mode 1: out[n][k] = float(bf16_rne(E4M3(Wq[n][k]) * scale[n/128][k/128]))
- *           (the GEMM's staged BF16 weight tile, with the scale folded in)
- * Same shape, alignment (Wq 16 B, out 16 B) and error rules as above.
+ * block-scale indexing the two entry points above use). out is FP32 [N][K]:
+ *   out[n][k] = float(E4M3(Wq[n][k])) * scale[n/128][k/128]
+ * which is exact (a 4-bit by 8-bit significand product). Same shape rules
+ * as above; Wq and out must be 16-byte aligned, scale 2-byte aligned.
  */
 int w8a16_dequant(const void* Wq, const void* scale, float* out,
-                  int64_t N, int64_t K, int mode, void* stream);
+                  int64_t N, int64_t K, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* w8a16_strerror(int status);

@@ -76,18 +76,17 @@ def test_gemv_limits():
     F = FAKE
     args = (F, F + (1 << 30), F + (2 << 30), F + (3 << 30))
     assert binding.gemv_raw(*args, 17, 256, 256, 0) == binding.ERR_SHAPE
-    assert binding.gemv_raw(*args, 4, 256, binding.GEMV_MAX_K_SMALL_M + 16, 0) == binding.ERR_SHAPE
-    assert binding.gemv_raw(*args, 5, 256, binding.GEMV_MAX_K + 16, 0) == binding.ERR_SHAPE
+    assert binding.gemv_raw(*args, 8, 256, binding.GEMV_MAX_K_SMALL_M + 16, 0) == binding.ERR_SHAPE
+    assert binding.gemv_raw(*args, 9, 256, binding.GEMV_MAX_K + 16, 0) == binding.ERR_SHAPE
 
 
 def test_dequant_rejections():
     F = FAKE
-    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30), 256, 256, 2, 0) == binding.ERR_ARG
-    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30), 256, 100, 0, 0) == binding.ERR_SHAPE
-    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30), 0, 256, 0, 0) == binding.OK
-    assert binding.dequant_raw(0, F + (1 << 30), F + (2 << 30), 256, 256, 0, 0) == binding.ERR_NULL
-    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30) + 4, 256, 256, 0, 0) == binding.ERR_ALIGN
-    assert binding.dequant_raw(F, F + (1 << 30), F, 256, 256, 0, 0) == binding.ERR_ALIAS
+    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30), 256, 100, 0) == binding.ERR_SHAPE
+    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30), 0, 256, 0) == binding.OK
+    assert binding.dequant_raw(0, F + (1 << 30), F + (2 << 30), 256, 256, 0) == binding.ERR_NULL
+    assert binding.dequant_raw(F, F + (1 << 30), F + (2 << 30) + 4, 256, 256, 0) == binding.ERR_ALIGN
+    assert binding.dequant_raw(F, F + (1 << 30), F, 256, 256, 0) == binding.ERR_ALIAS
 
 
 def _cpu_operands(M=2, N=300, K=256):
@@ -123,4 +122,4 @@ def test_binding_refuses_wrong_layouts():
     with pytest.raises(ValueError):
         binding.w8a16_gemm(A, W, S)                                    # CPU tensors
     with pytest.raises(ValueError):
-        binding.w8a16_dequant(W, S, mode=3)
+        binding.w8a16_dequant(W, S[:, :1])
