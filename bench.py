@@ -22,6 +22,11 @@ each between their own two events. `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workloads.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Profile helpers (read rocprofv3 CSV output; no GPU needed):
+    python bench.py --summarize-trace <dir>/<name>_kernel_trace.csv
+    python bench.py --summarize-counters <fetch counter_collection.csv> <write counter_collection.csv>
+The second writes profiles/hbm_traffic.json, which `roofline.traffic` reads.
 """
 from __future__ import annotations
 
@@ -50,6 +55,16 @@ KERNEL_SOURCES = {
     "gemm": ["gemm_mamba_ssm_amd/csrc/w8a16_gemm.hip", "gemm_mamba_ssm_amd/csrc/w8a16_device.h"],
 }
 METRIC = "M=1 GEMV HBM GB/s (%peak) + 1k-token prefill GEMM TFLOP/s (%MFMA peak)"
+CALIBRATION_BYTES = 256 << 20   # the plain copy run with --copy-calibration reads and writes this much
+
+# Launches of the timed step, told apart in profiler output by kernel name and
+# grid size (threads): (label, kernel-name fragment, grid threads).
+LAUNCHES = [
+    ("gemv_in_proj", "gemv_kernel", None),
+    ("gemv_out_proj", "gemv_kernel", None),
+    ("gemm_in_proj", "gemm_kernel", None),
+    ("gemm_out_proj", "gemm_kernel", None),
+]
 
 
 def source_digest(kind: str) -> str:
@@ -72,6 +87,89 @@ def measured_traffic(kind: str, launch: str):
     if not entry or entry.get("source_digest") != source_digest(kind):
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def _launch_grids():
+    """Grid size (threads) of each timed launch, from the host-side launch rules."""
+    cus = 256
+    dec, pre = inputs.WORKLOADS["decode_m1"], inputs.WORKLOADS["prefill_1k"]
+
+    def gemv_grid(p):
+        nwaves = -(-p.K // 1024) if p.K <= 8192 else -(-p.K // 2048)
+        rb = 16 if p.K <= 8192 else 8
+        groups = -(-p.N // rb)
+        resident = cus * max(1, 8 // nwaves)
+        per = -(-groups // resident)
+        return -(-groups // per) * 64 * nwaves
+
+    def gemm_grid(p):
+        return (-(-p.M // 128)) * (-(-p.N // 128)) * 256
+
+    return {"gemv_in_proj": gemv_grid(dec[0]), "gemv_out_proj": gemv_grid(dec[1]),
+            "gemm_in_proj": gemm_grid(pre[0]), "gemm_out_proj": gemm_grid(pre[1])}
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(path):
+    """Average duration per (kernel, grid) from a rocprofv3 kernel_trace.csv."""
+    grids = _launch_grids()
+    by = {}
+    for r in _read_csv(path):
+        name = r["Kernel_Name"]
+        grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1)
+        by.setdefault((name, grid), []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("| launch | kernel | grid (threads) | dispatches | mean us | min us | max us |")
+    print("|---|---|---|---|---|---|---|")
+    for (name, grid), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        label = next((lab for lab, frag, _ in LAUNCHES if frag in name and grids[lab] == grid), "")
+        short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        print(f"| {label} | {short} | {grid} | {len(d)} | {np.mean(d) / 1e3:.2f} | "
+              f"{np.min(d) / 1e3:.2f} | {np.max(d) / 1e3:.2f} |")
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for a plain copy of known size."""
+    grids = _launch_grids()
+
+    def per_launch(path, counter):
+        vals, calib = {}, []
+        for r in _read_csv(path):
+            if r["Counter_Name"] != counter:
+                continue
+            name, grid, v = r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])
+            if "neg" in name and grid >= CALIBRATION_BYTES // 4 // 8:
+                calib.append(v)
+            for lab, frag, _ in LAUNCHES:
+                if frag in name and grids[lab] == grid:
+                    vals.setdefault(lab, []).append(v)
+        if not calib:
+            raise SystemExit(f"no calibration copy found in {path}")
+        factor = (CALIBRATION_BYTES / 1024) / float(np.median(calib))
+        return {k: float(np.median(v)) for k, v in vals.items()}, factor
+
+    fetch, f_fac = per_launch(fetch_csv, "FETCH_SIZE")
+    write, w_fac = per_launch(write_csv, "WRITE_SIZE")
+    rec = {"source": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, of "
+                     "`python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration`",
+           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4), "kernels": {}}
+    for lab in fetch:
+        kind = lab.split("_")[0]
+        kib_f, kib_w = fetch[lab], write.get(lab, 0.0)
+        rec["kernels"][lab] = {
+            "fetch_kib": kib_f, "write_kib": kib_w,
+            "hbm_bytes_per_launch": int(round((kib_f * f_fac + kib_w * w_fac) * 1024)),
+            "source_digest": source_digest(kind)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec, indent=1, sort_keys=True))
 
 
 def to_dev(a: np.ndarray, dtype, device):
@@ -158,7 +256,15 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="decode layers (weight copies) per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a plain device copy of 256 MiB (for HBM counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
@@ -210,7 +316,7 @@ def main():
     wall = time.perf_counter() - t0
 
     if args.copy_calibration:
-        src = torch.empty(64 << 20, dtype=torch.float32, device=device)   # 256 MiB read, 256 MiB written
+        src = torch.empty(CALIBRATION_BYTES // 4, dtype=torch.float32, device=device)   # read once, written once
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.neg(src, out=dst)
