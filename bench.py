@@ -58,13 +58,42 @@ METRIC = "M=1 GEMV HBM GB/s (%peak) + 1k-token prefill GEMM TFLOP/s (%MFMA peak)
 CALIBRATION_BYTES = 256 << 20   # the plain copy run with --copy-calibration reads and writes this much
 
 # Launches of the timed step, told apart in profiler output by kernel name and
-# grid size (threads): (label, kernel-name fragment, grid threads).
+# dispatch order: every step issues LAYERS in_proj GEMVs, LAYERS out_proj GEMVs,
+# then the in_proj GEMM and the out_proj GEMM, and nothing else in the process
+# launches these kernels. (label, kernel-name fragment)
 LAUNCHES = [
-    ("gemv_in_proj", "gemv_kernel", None),
-    ("gemv_out_proj", "gemv_kernel", None),
-    ("gemm_in_proj", "gemm_kernel", None),
-    ("gemm_out_proj", "gemm_kernel", None),
+    ("gemv_in_proj", "gemv_kernel"),
+    ("gemv_out_proj", "gemv_kernel"),
+    ("gemm_in_proj", "gemm_kernel"),
+    ("gemm_out_proj", "gemm_kernel"),
 ]
+DEFAULT_LAYERS = 8
+
+
+def label_dispatches(rows, layers=DEFAULT_LAYERS):
+    """Label each rocprofv3 CSV row (one per dispatch, or per dispatch and
+    counter) with its launch, from the dispatch order; None for other kernels."""
+    order = sorted({int(r["Dispatch_Id"]) for r in rows})
+    seen = {"gemv_kernel": {}, "gemm_kernel": {}}
+    labels_by_id = {}
+    names = {int(r["Dispatch_Id"]): r["Kernel_Name"] for r in rows}
+    prev_gemm = None
+    for d in order:
+        name = names[d]
+        if "combine_kernel" in name:            # the split-tile combine after a GEMM
+            labels_by_id[d] = f"{prev_gemm}_combine" if prev_gemm else None
+            continue
+        frag = next((f for f in seen if f in name), None)
+        if frag is None:
+            labels_by_id[d] = None
+            continue
+        i = len(seen[frag])
+        seen[frag][d] = i
+        if frag == "gemv_kernel":
+            labels_by_id[d] = "gemv_in_proj" if (i // layers) % 2 == 0 else "gemv_out_proj"
+        else:
+            labels_by_id[d] = prev_gemm = "gemm_in_proj" if i % 2 == 0 else "gemm_out_proj"
+    return [labels_by_id[int(r["Dispatch_Id"])] for r in rows]
 
 
 def source_digest(kind: str) -> str:
@@ -89,65 +118,41 @@ def measured_traffic(kind: str, launch: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def _launch_grids():
-    """Grid size (threads) of each timed launch, from the host-side launch rules."""
-    cus = 256
-    dec, pre = inputs.WORKLOADS["decode_m1"], inputs.WORKLOADS["prefill_1k"]
-
-    def gemv_grid(p):
-        nwaves = -(-p.K // 1024) if p.K <= 8192 else -(-p.K // 2048)
-        rb = 16 if p.K <= 8192 else 8
-        groups = -(-p.N // rb)
-        resident = cus * max(1, 8 // nwaves)
-        per = -(-groups // resident)
-        return -(-groups // per) * 64 * nwaves
-
-    def gemm_grid(p):
-        return (-(-p.M // 128)) * (-(-p.N // 128)) * 256
-
-    return {"gemv_in_proj": gemv_grid(dec[0]), "gemv_out_proj": gemv_grid(dec[1]),
-            "gemm_in_proj": gemm_grid(pre[0]), "gemm_out_proj": gemm_grid(pre[1])}
-
-
 def _read_csv(path):
     import csv
     with open(path) as f:
         return list(csv.DictReader(f))
 
 
-def summarize_trace(path):
-    """Average duration per (kernel, grid) from a rocprofv3 kernel_trace.csv."""
-    grids = _launch_grids()
+def summarize_trace(path, layers=DEFAULT_LAYERS):
+    """Average duration per launch (and per other kernel) from a rocprofv3 kernel_trace.csv."""
+    rows = _read_csv(path)
     by = {}
-    for r in _read_csv(path):
+    for r, lab in zip(rows, label_dispatches(rows, layers)):
         name = r["Kernel_Name"]
         grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1)
-        by.setdefault((name, grid), []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        by.setdefault((lab or "", name, grid), []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     print("| launch | kernel | grid (threads) | dispatches | mean us | min us | max us |")
     print("|---|---|---|---|---|---|---|")
-    for (name, grid), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        label = next((lab for lab, frag, _ in LAUNCHES if frag in name and grids[lab] == grid), "")
+    for (lab, name, grid), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-        print(f"| {label} | {short} | {grid} | {len(d)} | {np.mean(d) / 1e3:.2f} | "
+        print(f"| {lab} | {short} | {grid} | {len(d)} | {np.mean(d) / 1e3:.2f} | "
               f"{np.min(d) / 1e3:.2f} | {np.max(d) / 1e3:.2f} |")
 
 
-def summarize_counters(fetch_csv, write_csv):
+def summarize_counters(fetch_csv, write_csv, layers=DEFAULT_LAYERS):
     """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
     scaled by what the same counter reads for a plain copy of known size."""
-    grids = _launch_grids()
 
     def per_launch(path, counter):
         vals, calib = {}, []
-        for r in _read_csv(path):
-            if r["Counter_Name"] != counter:
-                continue
+        rows = [r for r in _read_csv(path) if r["Counter_Name"] == counter]
+        for r, lab in zip(rows, label_dispatches(rows, layers)):
             name, grid, v = r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])
             if "neg" in name and grid >= CALIBRATION_BYTES // 4 // 8:
                 calib.append(v)
-            for lab, frag, _ in LAUNCHES:
-                if frag in name and grids[lab] == grid:
-                    vals.setdefault(lab, []).append(v)
+            if lab is not None:
+                vals.setdefault(lab, []).append(v)
         if not calib:
             raise SystemExit(f"no calibration copy found in {path}")
         factor = (CALIBRATION_BYTES / 1024) / float(np.median(calib))
@@ -253,17 +258,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
-    ap.add_argument("--layers", type=int, default=8, help="decode layers (weight copies) per step")
+    ap.add_argument("--layers", type=int, default=DEFAULT_LAYERS, help="decode layers (weight copies) per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a plain device copy of 256 MiB (for HBM counter calibration)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.layers)
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, layers=args.layers)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path; "

@@ -25,7 +25,7 @@ BLOCK = 128
 
 EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_dequant", "w8a16_strerror")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ALIAS, ERR_ARG = 0, -1, -2, -3, -4, -5, -6
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ALIAS, ERR_ARG, ERR_MEMORY = 0, -1, -2, -3, -4, -5, -6, -7
 GEMV_MAX_M = 16
 GEMV_MAX_K_SMALL_M = 16384   # M <= 8
 GEMV_MAX_K = 8192            # M >= 9

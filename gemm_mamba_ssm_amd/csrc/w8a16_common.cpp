@@ -30,6 +30,7 @@ extern "C" const char* w8a16_strerror(int status) {
         case W8A16_ERR_LAUNCH: return "HIP kernel launch failed";
         case W8A16_ERR_ALIAS: return "out overlaps an input buffer";
         case W8A16_ERR_ARG: return "invalid argument";
+        case W8A16_ERR_MEMORY: return "could not allocate the GEMM workspace";
         default: return "unknown w8a16 status";
     }
 }

@@ -32,7 +32,28 @@
 //  * the block scale is applied exactly, in fp32: the MFMAs of one 128-wide
 //    k-block accumulate into `blk`, which is then added to the result as
 //    acc += scale * blk (TN = 128 keeps a wave's columns in one scale row).
+//
+// Schedule (persistent grid of G = 2 workgroups per CU): the 128 x 128 output
+// tiles rarely come in a multiple of G (the 1024-token in_proj has 1160 tiles
+// for 512 slots, the out_proj 256), so whole-tile waves would leave up to half
+// of the chip idle in the last wave. Instead:
+//  * shared part: the tiles past the last whole round of G are cut into
+//    units of one 128-wide k-block, and the units are dealt to the workgroups
+//    in equal contiguous ranges, so every workgroup gets the same work. A tile
+//    whose k-blocks fall in two or more ranges is "split": each range stores
+//    its fp32 partial tile to a workspace slot;
+//  * full rounds: then, while at least G whole tiles remain, workgroup w
+//    computes tile r*G + w whole (r = 0, 1, ...);
+//  * a second kernel on the same stream adds the partial tiles of every
+//    split tile in k order (so the bits never depend on timing) and writes
+//    its BF16 result. The kernel boundary orders the two, so no workgroup
+//    ever waits for another and no atomics or flags are needed.
+// The shared part runs first so that the partial stores drain while the
+// workgroups go on with their whole tiles.
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "w8a16_device.h"
 #include "w8a16_host.h"
@@ -42,12 +63,15 @@ namespace {
 
 constexpr int TM = 128, TN = 128, TK = 64;
 constexpr int kThreads = 256;
+constexpr int kWgPerCu = 2;                          // resident workgroups per CU (2 x 72 KB of LDS)
 constexpr int kStages = 3;
 constexpr int kATileBytes = TM * TK * 2;            // 16 KB of BF16
 constexpr int kWTileBytes = TN * TK;                // 8 KB of E4M3
 constexpr int kStageBytes = kATileBytes + kWTileBytes;
 constexpr int kAChunksPerThread = kATileBytes / 16 / kThreads;   // 4
 constexpr int kWChunksPerThread = kWTileBytes / 16 / kThreads;   // 2
+constexpr int kTileFloats = TM * TN;                // one fp32 partial tile (64 KB)
+constexpr int kMinShareBlocks = 4;                  // fewest k-blocks a shared tile hands one workgroup
 constexpr uint32_t kOutOfRange = 0x80000000u;       // buffer offset that reads as zero
 constexpr int kBufferFlags = 0x00020000;            // raw buffer, 32-bit data format
 
@@ -55,19 +79,42 @@ static_assert(kScaleBlock % TN == 0 && kScaleBlock == 2 * TK, "two k-steps per s
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// How the output tiles are spread over the G workgroups (logical index w):
+// tiles [shared_tile0, tiles) form shared_units = (tiles - shared_tile0) *
+// k_blocks units (unit (t - shared_tile0) * k_blocks + kb is k-block kb of
+// tile t), and workgroup w < shared_groups takes units [start(w), start(w+1))
+// with start(w) = floor(w * shared_units / shared_groups); then full rounds
+// give workgroup w the tiles r * G + w, r < full_rounds.
+struct Schedule {
+    int tiles_m;         // tile t covers rows (t % tiles_m) * TM and columns (t / tiles_m) * TN
+    int k_blocks;        // ceil(K / 128)
+    int full_rounds;
+    int shared_groups;   // 0 when every tile is computed whole
+    int shared_tile0;
+    int shared_r;        // shared_units % shared_groups
+    int64_t shared_q;    // shared_units / shared_groups
+};
+
+// start(w) = w * q + floor(w * r / shared_groups), which equals
+// floor(w * shared_units / shared_groups) without a 64-bit division
+// (w * r < shared_groups^2 fits in 32 bits).
+__device__ __forceinline__ int64_t share_start(const Schedule& sc, int w) {
+    return static_cast<int64_t>(w) * sc.shared_q + (w * sc.shared_r) / sc.shared_groups;
+}
+
 // Byte offset of 16-byte chunk `c` of row `r` inside a staged tile.
 __device__ __forceinline__ int a_slot(int r, int c) { return r * (TK * 2) + ((c ^ ((r >> 1) & 7)) << 4); }
 __device__ __forceinline__ int w_slot(int r, int c) { return r * TK + ((c ^ ((r >> 2) & 3)) << 4); }
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8),
 // and each XCD has its own L2. Remap so that XCD x receives a contiguous range
-// of tile ids, ordered with the M-tile fastest: the M-tiles that share one
-// weight strip then run on the same XCD, and the strip is fetched into that
-// L2 once. The map is a bijection on [0, tiles).
+// of logical workgroups, which own neighbouring tiles (M-tile fastest): the
+// M-tiles that share one weight strip then run on the same XCD, and the strip
+// is fetched into that L2 once. The map is a bijection on [0, count).
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int xcd_tile(int b, int tiles) {
-    const int q = tiles / kXcds, r = tiles % kXcds;
+__device__ __forceinline__ int xcd_remap(int b, int count) {
+    const int q = count / kXcds, r = count % kXcds;
     const int x = b % kXcds;
     return x * q + min(x, r) + b / kXcds;
 }
@@ -87,31 +134,46 @@ __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-__global__ void __launch_bounds__(kThreads, 2)
+// A copy of x that the compiler cannot see through: values derived from it
+// are computed where they are used, instead of being hoisted to the top of
+// the kernel and kept in registers across the main loop.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Workgroup barrier for the stage hand-off. The memory clobbers keep the
+// compiler from moving LDS accesses across it; the hardware needs no fence
+// here, because each wave has already waited (s_waitcnt) for its own DMA and
+// its LDS reads complete before their MFMAs issue. A workgroup-scope fence
+// would also wait for every in-flight DMA load and serialize the pipeline.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__global__ void __launch_bounds__(kThreads, kWgPerCu)
 gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             const uint16_t* __restrict__ S, uint16_t* __restrict__ out,
-            int M, int N, int K, int tiles_m) {
+            float* __restrict__ partials, int M, int N, int K, Schedule sc) {
+    // One LDS array only: a second __shared__ variable makes the compiler
+    // attach alias scopes to LDS accesses, after which it waits for every
+    // in-flight DMA before each LDS read (the explicit waits below already
+    // order them).
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
 
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int tm = tile % tiles_m, tn = tile / tiles_m;
-    const int m0 = tm * TM, n0 = tn * TN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = gridDim.x;
+    const int w = xcd_remap(blockIdx.x, G);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int li = lane & 31, lg = lane >> 5;
-    const int k_blocks = (K + kScaleBlock - 1) / kScaleBlock;
+    const int k_blocks = sc.k_blocks;
     const int nk = (K + TK - 1) / TK;
 
-    // Buffer resources over this tile's rows of A and W: rows past M or N lie
-    // beyond num_records and read as zero.
-    const int rows_a = min(TM, M - m0), rows_w = min(TN, N - n0);
-    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(A + static_cast<int64_t>(m0) * K), 0, rows_a * K * 2, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, rows_w * K, kBufferFlags);
-
-    // Per-thread DMA source offsets at k0 = 0 (the lane's LDS destination is
-    // fixed by the instruction: base + 16 * lane).
+    // Per-thread DMA source offsets at k0 = 0, the same for every tile (the
+    // lane's LDS destination is fixed by the instruction: base + 16 * lane).
     uint32_t a_off[kAChunksPerThread], w_off[kWChunksPerThread];
     int a_k[kAChunksPerThread], w_k[kWChunksPerThread];
 #pragma unroll
@@ -129,33 +191,6 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
         w_off[i] = static_cast<uint32_t>(r * K + c * 16);
     }
 
-    // DMA of k-step kt into stage `slot`. A full k-step passes k0 as the
-    // scalar offset; the K-tail step checks each lane's k and sends lanes past
-    // K out of range (they load zeros).
-    auto issue = [&](int kt, int slot) {
-        const int k0 = kt * TK;
-        uint8_t* base = smem + slot * kStageBytes;
-        const bool full = k0 + TK <= K;
-#pragma unroll
-        for (int i = 0; i < kAChunksPerThread; ++i) {
-            lds_void* dst = (lds_void*)(base + i * (kThreads * 16) + wave * 1024);
-            if (full)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst, 16, a_off[i], k0 * 2, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc_a, dst, 16, (k0 + a_k[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < kWChunksPerThread; ++i) {
-            lds_void* dst = (lds_void*)(base + kATileBytes + i * (kThreads * 16) + wave * 1024);
-            if (full)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, dst, 16, w_off[i], k0, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc_w, dst, 16, (k0 + w_k[i] < K) ? w_off[i] + k0 : kOutOfRange, 0, 0, 0);
-        }
-    };
-
     // Lane-constant operand addresses inside a stage; the stage is added as
     // an immediate offset. A: [bi][j][h], W: [bj][j].
     int a_addr[2][2][2], w_addr[2][2];
@@ -170,115 +205,359 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
 #pragma unroll
         for (int j = 0; j < 2; ++j) w_addr[bj][j] = kATileBytes + w_slot(wn * 64 + bj * 32 + li, 2 * j + lg);
 
-    f32x16_t acc[2][2], blk[2][2];
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.0f;
     const f32x16_t zero = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
                            0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-
-    // One k-step on stage SLOT: 12 operand reads, 32 converts, 16 MFMAs. The
-    // first k-step of a scale block starts the block accumulator from zero.
-    auto compute = [&](auto slot_c, auto first_c) {
-        constexpr int kSlot = decltype(slot_c)::value;
-        constexpr bool kFirst = decltype(first_c)::value;
-        const uint8_t* stage = smem + kSlot * kStageBytes;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {               // two 32-wide k spans
-            bf16x8_t bw[2][2];                      // [bj][h]
-#pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const u32x4_t q = *reinterpret_cast<const u32x4_t*>(stage + w_addr[bj][j]);
-                bw[bj][0] = e4m3x8_to_bf16(q[0], q[1]);
-                bw[bj][1] = e4m3x8_to_bf16(q[2], q[3]);
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                bf16x8_t av[2];
-#pragma unroll
-                for (int bi = 0; bi < 2; ++bi)
-                    av[bi] = *reinterpret_cast<const bf16x8_t*>(stage + a_addr[bi][j][h]);
-#pragma unroll
-                for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                    for (int bj = 0; bj < 2; ++bj)
-                        blk[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            av[bi], bw[bj][h], (kFirst && j == 0 && h == 0) ? zero : blk[bi][bj], 0, 0, 0);
-            }
-        }
-    };
-
-    // The tile's scale row, 64 k-blocks at a time: lane l holds block base + l,
-    // so the main loop issues no vector memory operation besides the DMA.
-    const uint16_t* s_row = S + static_cast<int64_t>(tn) * k_blocks;
-    auto load_scales = [&](int base) {
-        return (base + lane < k_blocks) ? bf16_bits_to_f32(s_row[base + lane]) : 0.0f;
-    };
-    float s_lane = load_scales(0);
-
-    auto fold = [&](int kb) {
-        if ((kb & 63) == 0 && kb > 0) s_lane = load_scales(kb);
-        const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), kb & 63));
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[bi][bj][v] = fmaf(blk[bi][bj][v], s, acc[bi][bj][v]);
-    };
-
-    // k-step kt reads stage kt % 3. Before it: wait for this wave's DMA of kt
-    // (at most the next step's loads remain in flight), then a barrier, after
-    // which every wave's DMA of kt has landed and every wave is done reading
-    // stage (kt + 2) % 3 == (kt - 1) % 3, which is refilled with step kt + 2.
-    // FIRST: kt is even (the first k-step of a scale block); the unrolled
-    // loop below starts at multiples of 6, so the parity is static.
-    auto step = [&](auto slot_c, auto first_c, int kt) {
-        constexpr int kSlot = decltype(slot_c)::value;
-        constexpr bool kFirst = decltype(first_c)::value;
-        if (kt + 1 < nk)
-            wait_vmem<kAChunksPerThread + kWChunksPerThread>();
-        else
-            wait_vmem<0>();
-        __builtin_amdgcn_s_barrier();
-        if (kt + 2 < nk) issue(kt + 2, (kSlot + 2) % kStages);
-        compute(slot_c, first_c);
-        if (!kFirst || kt + 1 == nk) fold(kt >> 1);
-    };
-
-    issue(0, 0);
-    if (nk > 1) issue(1, 1);
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    using F = std::true_type;
-    using L = std::false_type;
-    for (int kt = 0; kt < nk; kt += 2 * kStages) {   // six k-steps: stages 0,1,2,0,1,2
-        step(S0{}, F{}, kt);
-        if (kt + 1 < nk) step(S1{}, L{}, kt + 1);
-        if (kt + 2 < nk) step(S2{}, F{}, kt + 2);
-        if (kt + 3 < nk) step(S0{}, L{}, kt + 3);
-        if (kt + 4 < nk) step(S1{}, F{}, kt + 4);
-        if (kt + 5 < nk) step(S2{}, L{}, kt + 5);
-    }
+    f32x16_t acc[2][2], blk[2][2];
 
     // 32x32 MFMA result layout: lane l holds column l % 32; value v is row
     // 8*(v/4) + 4*(l/32) + v%4 of the block.
+    auto store_tile = [&](const f32x16_t (&r)[2][2], int m0, int n0) {
+        const int l = opaque(lane), li = l & 31, lg = l >> 5;
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+        for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj) {
-            const int n = n0 + wn * 64 + bj * 32 + li;
+            for (int bj = 0; bj < 2; ++bj) {
+                const int n = n0 + wn * 64 + bj * 32 + li;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
-                if (m < M && n < N)
-                    out[static_cast<int64_t>(m) * N + n] = f32_to_bf16_bits(acc[bi][bj][v]);
+                for (int v = 0; v < 16; ++v) {
+                    const int m = m0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
+                    if (m < M && n < N)
+                        out[static_cast<int64_t>(m) * N + n] = f32_to_bf16_bits(r[bi][bj][v]);
+                }
+            }
+    };
+
+    // Shared-range state: this workgroup's units [u, u_end) and the local
+    // index of the first tile they touch.
+    int64_t u = 0, u_end = 0;
+    if (w < sc.shared_groups) {
+        u = share_start(sc, w);
+        u_end = share_start(sc, w + 1);
+    }
+    const int first_shared = static_cast<int>(u / k_blocks);
+    int round = 0;
+
+    for (;;) {
+        // Next piece of work: tile t, k-blocks [kb0, kb1).
+        int t, kb0, kb1;
+        if (u < u_end) {
+            const int ts = static_cast<int>(u / k_blocks);
+            kb0 = static_cast<int>(u - static_cast<int64_t>(ts) * k_blocks);
+            kb1 = static_cast<int>(min(static_cast<int64_t>(k_blocks), kb0 + (u_end - u)));
+            t = sc.shared_tile0 + ts;
+            u += kb1 - kb0;
+        } else if (round < sc.full_rounds) {
+            t = round * G + w;
+            kb0 = 0;
+            kb1 = k_blocks;
+            ++round;
+        } else {
+            break;
+        }
+        const int tm = t % sc.tiles_m, tn = t / sc.tiles_m;
+        const int m0 = tm * TM, n0 = tn * TN;
+        const int ks0 = 2 * kb0;                       // first k-step (even)
+        const int len = min(2 * kb1, nk) - ks0;        // k-steps in this piece (>= 1)
+
+        // Buffer resources over this tile's rows of A and W: rows past M or
+        // N lie beyond num_records and read as zero.
+        const int rows_a = min(TM, M - m0), rows_w = min(TN, N - n0);
+        const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(A + static_cast<int64_t>(m0) * K), 0, rows_a * K * 2, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, rows_w * K, kBufferFlags);
+
+        // DMA of k-step ks0 + kt into stage `slot`. A full k-step passes k0
+        // as the scalar offset; the K-tail step checks each lane's k and sends
+        // lanes past K out of range (they load zeros).
+        auto issue = [&](int kt, int slot) {
+            const int k0 = (ks0 + kt) * TK;
+            uint8_t* base = smem + slot * kStageBytes;
+            const bool full = k0 + TK <= K;
+#pragma unroll
+            for (int i = 0; i < kAChunksPerThread; ++i) {
+                lds_void* dst = (lds_void*)(base + i * (kThreads * 16) + wave * 1024);
+                if (full)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst, 16, a_off[i], k0 * 2, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rsrc_a, dst, 16, (k0 + a_k[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < kWChunksPerThread; ++i) {
+                lds_void* dst = (lds_void*)(base + kATileBytes + i * (kThreads * 16) + wave * 1024);
+                if (full)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, dst, 16, w_off[i], k0, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rsrc_w, dst, 16, (k0 + w_k[i] < K) ? w_off[i] + k0 : kOutOfRange, 0, 0, 0);
+            }
+        };
+
+        // One k-step on stage SLOT: 12 operand reads, 32 converts, 16 MFMAs.
+        // The first k-step of a scale block starts the block accumulator from
+        // zero.
+        auto compute = [&](auto slot_c, auto first_c) {
+            constexpr int kSlot = decltype(slot_c)::value;
+            constexpr bool kFirst = decltype(first_c)::value;
+            const uint8_t* stage = smem + kSlot * kStageBytes;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {               // two 32-wide k spans
+                bf16x8_t bw[2][2];                      // [bj][h]
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj) {
+                    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(stage + w_addr[bj][j]);
+                    bw[bj][0] = e4m3x8_to_bf16(q[0], q[1]);
+                    bw[bj][1] = e4m3x8_to_bf16(q[2], q[3]);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    bf16x8_t av[2];
+#pragma unroll
+                    for (int bi = 0; bi < 2; ++bi)
+                        av[bi] = *reinterpret_cast<const bf16x8_t*>(stage + a_addr[bi][j][h]);
+#pragma unroll
+                    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                        for (int bj = 0; bj < 2; ++bj)
+                            blk[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                av[bi], bw[bj][h], (kFirst && j == 0 && h == 0) ? zero : blk[bi][bj], 0, 0, 0);
+                }
+            }
+        };
+
+        // The tile's scale row, 64 k-blocks at a time: lane l holds block
+        // s_base + l, so the main loop issues no vector memory operation
+        // besides the DMA (one reload per 64 k-blocks).
+        const uint16_t* s_row = S + static_cast<int64_t>(tn) * k_blocks;
+        auto load_scales = [&](int base) {
+            return (base + lane < k_blocks) ? bf16_bits_to_f32(s_row[base + lane]) : 0.0f;
+        };
+        int s_base = kb0 & ~63;
+        float s_lane = load_scales(s_base);
+
+        auto fold = [&](int kb) {
+            if (kb - s_base >= 64) {
+                s_base += 64;
+                s_lane = load_scales(s_base);
+            }
+            const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), kb - s_base));
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[bi][bj][v] = fmaf(blk[bi][bj][v], s, acc[bi][bj][v]);
+        };
+
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = zero;
+
+        // k-step kt (relative to ks0) reads stage kt % 3. Before it: wait for
+        // this wave's DMA of kt (at most the next step's loads remain in
+        // flight), then a barrier, after which every wave's DMA of kt has
+        // landed and every wave is done reading stage (kt + 2) % 3 ==
+        // (kt - 1) % 3, which is refilled with step kt + 2. FIRST: kt is even
+        // (ks0 is even, so this is the first k-step of a scale block); the
+        // unrolled loop below starts at multiples of 6, so the parity is
+        // static.
+        auto step = [&](auto slot_c, auto first_c, int kt) {
+            constexpr int kSlot = decltype(slot_c)::value;
+            constexpr bool kFirst = decltype(first_c)::value;
+            if (kt + 1 < len)
+                wait_vmem<kAChunksPerThread + kWChunksPerThread>();
+            else
+                wait_vmem<0>();
+            lds_barrier();
+            if (kt + 2 < len) issue(kt + 2, (kSlot + 2) % kStages);
+            compute(slot_c, first_c);
+            if (!kFirst || kt + 1 == len) fold(kb0 + (kt >> 1));
+        };
+
+        // Every wave is done reading the stages of the previous piece.
+        lds_barrier();
+        issue(0, 0);
+        if (len > 1) issue(1, 1);
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        using F = std::true_type;
+        using L = std::false_type;
+        for (int kt = 0; kt < len; kt += 2 * kStages) {   // six k-steps: stages 0,1,2,0,1,2
+            step(S0{}, F{}, kt);
+            if (kt + 1 < len) step(S1{}, L{}, kt + 1);
+            if (kt + 2 < len) step(S2{}, F{}, kt + 2);
+            if (kt + 3 < len) step(S0{}, L{}, kt + 3);
+            if (kt + 4 < len) step(S1{}, F{}, kt + 4);
+            if (kt + 5 < len) step(S2{}, L{}, kt + 5);
+        }
+
+        if (kb0 == 0 && kb1 == k_blocks) {        // the whole tile: write it
+            store_tile(acc, m0, n0);
+            continue;
+        }
+
+        // Part of a split tile: store it row-major to this range's slot 0 if
+        // the tile is the first of the range, else to slot 1 (a range has at
+        // most two split tiles: its first and its last). Plain stores, no
+        // wait: the combine kernel reads them after this kernel has ended.
+        const int ts = t - sc.shared_tile0;
+        float* mine = partials + (2 * static_cast<int64_t>(w) + (ts == first_shared ? 0 : 1)) * kTileFloats;
+        const int l = opaque(lane), li = l & 31, lg = l >> 5;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj) {
+                const int col = wn * 64 + bj * 32 + li;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
+                    mine[row * TN + col] = acc[bi][bj][v];
+                }
+            }
+    }
+}
+
+// Combine of the split tiles. The host lists, for every split tile, the
+// workgroup that computed its first k-blocks (the tile is the last of that
+// workgroup's range). Workgroup (i, y) of the combine handles rows
+// 32y .. 32y+31 of split tile i: each thread adds four float4 (rows r, r+8,
+// r+16, r+24 at 4 consecutive columns) over the parts in k order, issuing
+// the loads of kCombineBatch parts before their additions, and writes BF16.
+constexpr int kMaxSplits = 1536;                       // list capacity (3 KB of kernel arguments)
+constexpr int kCombineRows = 32;
+constexpr int kCombineRowGroups = TM / kCombineRows;
+constexpr int kCombineBatch = 4;
+static_assert(kThreads == 8 * (TN / 4), "8 rows of float4 per pass");
+
+struct SplitList {
+    uint16_t first[kMaxSplits];
+};
+
+__global__ void __launch_bounds__(kThreads)
+combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, int M, int N,
+               Schedule sc, SplitList list) {
+    const int w = list.first[blockIdx.x];
+    const int k_blocks = sc.k_blocks;
+    const int ts = static_cast<int>((share_start(sc, w + 1) - 1) / k_blocks);
+    // Parts: workgroups w .. last, the ranges that intersect tile ts (w + 1
+    // starts inside it, since w ends inside it).
+    const int64_t tile_begin = static_cast<int64_t>(ts) * k_blocks, tile_end = tile_begin + k_blocks;
+    int last = w + 1;
+    while (last + 1 < sc.shared_groups && share_start(sc, last + 1) < tile_end) ++last;
+
+    const int t = sc.shared_tile0 + ts;
+    const int m0 = (t % sc.tiles_m) * TM, n0 = (t / sc.tiles_m) * TN;
+    const int row0 = blockIdx.y * kCombineRows + threadIdx.x / (TN / 4), col = (threadIdx.x % (TN / 4)) * 4;
+    f32x4_t sum[4];
+    for (int p0 = w; p0 <= last; p0 += kCombineBatch) {
+        f32x4_t x[kCombineBatch][4];
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+            const int p = p0 + i;
+            if (p <= last) {
+                // Slot 0 if tile ts is the first tile of p's range (the range
+                // starts inside it or at its start), else slot 1.
+                const int slot = share_start(sc, p) >= tile_begin ? 0 : 1;
+                const float* src = partials + (2 * static_cast<int64_t>(p) + slot) * kTileFloats + row0 * TN + col;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[i][r] = *reinterpret_cast<const f32x4_t*>(src + r * 8 * TN);
             }
         }
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+            const int p = p0 + i;
+            if (p <= last) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sum[r] = (p == w) ? x[i][r] : sum[r] + x[i][r];
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = m0 + row0 + r * 8;
+        if (m >= M) break;
+        uint16_t* dst = out + static_cast<int64_t>(m) * N + n0 + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n0 + col + e < N) dst[e] = f32_to_bf16_bits(sum[r][e]);
+    }
+}
+
+// Choose the schedule; returns the grid size. `slots` is the number of
+// workgroups resident at once (2 per CU). Whole tiles, one per workgroup,
+// when they fill the slots evenly or the last wave is at least a quarter full
+// (splitting k then costs more in partial-tile traffic than the idle slots);
+// otherwise whole rounds of `slots` tiles plus a shared part over the rest.
+int plan(int64_t tiles, int64_t tiles_m, int k_blocks, int slots, Schedule* sc) {
+    *sc = Schedule{};
+    sc->tiles_m = static_cast<int>(tiles_m);
+    sc->k_blocks = k_blocks;
+    const int64_t rounds = tiles / slots;
+    const int64_t rest = tiles - rounds * slots;
+    if (rest == 0 || (rounds > 0 && 4 * rest >= slots)) {
+        sc->full_rounds = 1;
+        return static_cast<int>(tiles);
+    }
+    const int64_t units = rest * k_blocks;
+    const int64_t groups = std::min<int64_t>(slots, std::max<int64_t>(rest, units / kMinShareBlocks));
+    sc->full_rounds = static_cast<int>(rounds);
+    sc->shared_tile0 = static_cast<int>(rounds * slots);
+    sc->shared_groups = static_cast<int>(groups);
+    sc->shared_q = units / groups;
+    sc->shared_r = static_cast<int>(units % groups);
+    return rounds > 0 ? slots : static_cast<int>(groups);
+}
+
+// Host copy of share_start.
+int64_t host_share_start(const Schedule& sc, int w) {
+    return static_cast<int64_t>(w) * sc.shared_q + (static_cast<int64_t>(w) * sc.shared_r) / sc.shared_groups;
+}
+
+// The split tiles, each named by the workgroup that computes its first
+// k-blocks: w whose range ends inside a tile that it also starts.
+int list_splits(const Schedule& sc, SplitList* list) {
+    int n = 0;
+    for (int w = 0; w + 1 < sc.shared_groups; ++w) {
+        const int64_t end = host_share_start(sc, w + 1);
+        if (end % sc.k_blocks == 0) continue;
+        const int64_t tile_begin = (end - 1) / sc.k_blocks * sc.k_blocks;
+        if (host_share_start(sc, w) <= tile_begin) list->first[n++] = static_cast<uint16_t>(w);
+    }
+    return n;
+}
+
+// Workspace of one (device, stream): two partial-tile slots per workgroup of
+// the largest grid. Allocated on first use and kept until the process ends.
+struct Workspace {
+    float* partials = nullptr;
+    int groups = 0;
+};
+
+int workspace_for(hipStream_t stream, int groups, Workspace* ws) {
+    static std::mutex mu;
+    static auto* cache = new std::map<std::pair<int, hipStream_t>, Workspace>();
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return W8A16_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache->find({dev, stream});
+    if (it != cache->end() && it->second.groups >= groups) {
+        *ws = it->second;
+        return W8A16_OK;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, static_cast<size_t>(2) * groups * kTileFloats * sizeof(float)) != hipSuccess)
+        return W8A16_ERR_MEMORY;
+    // A smaller workspace of the same key is only replaced, never freed: work
+    // already enqueued on the stream may still use it.
+    Workspace fresh;
+    fresh.partials = static_cast<float*>(p);
+    fresh.groups = groups;
+    (*cache)[{dev, stream}] = fresh;
+    *ws = fresh;
+    return W8A16_OK;
 }
 
 }  // namespace
@@ -295,9 +574,25 @@ extern "C" int w8a16_gemm(const void* A, const void* Wq, const void* scale, void
     const int64_t tiles_m = ceil_div(M, TM);
     const int64_t tiles = tiles_m * ceil_div(N, TN);
     if (tiles > INT32_MAX) return W8A16_ERR_SHAPE;
-    return launch(&gemm_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kThreads),
-                  static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(A),
-                  static_cast<const uint8_t*>(Wq), static_cast<const uint16_t*>(scale),
-                  static_cast<uint16_t*>(out), static_cast<int>(M), static_cast<int>(N),
-                  static_cast<int>(K), static_cast<int>(tiles_m));
+    const int k_blocks = static_cast<int>(ceil_div(K, kScaleBlockHost));
+    const int slots = std::min(kWgPerCu * device_cu_count(), kMaxSplits);
+    Schedule sc;
+    const int grid = plan(tiles, tiles_m, k_blocks, slots, &sc);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Workspace ws;
+    if (sc.shared_groups > 0) {
+        st = workspace_for(s, slots, &ws);
+        if (st != W8A16_OK) return st;
+    }
+    st = launch(&gemm_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), s,
+                static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq),
+                static_cast<const uint16_t*>(scale), static_cast<uint16_t*>(out), ws.partials,
+                static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), sc);
+    if (st != W8A16_OK || sc.shared_groups == 0) return st;
+    SplitList list;
+    const int splits = list_splits(sc, &list);
+    if (splits == 0) return W8A16_OK;
+    return launch(&combine_kernel, dim3(static_cast<unsigned>(splits), kCombineRowGroups), dim3(kThreads), s,
+                  static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), static_cast<int>(M),
+                  static_cast<int>(N), sc, list);
 }

@@ -23,8 +23,9 @@
  * buffer reads past its end (a device fault, not wrong numbers) - callers
  * must check the layout before calling, as the Python binding does.
  *
- * Ownership: the caller owns every buffer; the library allocates nothing and
- * keeps no pointer after a call returns.
+ * Ownership: the caller owns every buffer it passes; the library keeps no
+ * pointer to them after a call returns. The only memory the library allocates
+ * is the GEMM workspace described at w8a16_gemm.
  * Streams: `stream` is a hipStream_t (NULL = the legacy default stream). Every
  * call only enqueues work on it and returns without synchronizing; the result
  * is ready once the stream reaches that point.
@@ -49,7 +50,8 @@ enum w8a16_status {
     W8A16_ERR_ALIGN = -3,  /* A or Wq not 16-byte aligned; scale/out not 2-byte */
     W8A16_ERR_LAUNCH = -4, /* the HIP launch failed                             */
     W8A16_ERR_ALIAS = -5,  /* out overlaps an input                             */
-    W8A16_ERR_ARG = -6     /* another argument is invalid                       */
+    W8A16_ERR_ARG = -6,    /* another argument is invalid                       */
+    W8A16_ERR_MEMORY = -7  /* the GEMM workspace could not be allocated         */
 };
 
 /* Largest M the GEMV entry point accepts, and its largest K: 16384 when
@@ -76,6 +78,19 @@ int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
  * no-op. The E4M3 weight bytes of a tile are staged once per workgroup and
  * decoded in registers; the block scale is applied in fp32 per 128-wide
  * k-block, as in the GEMV.
+ * When there are fewer 128 x 128 output tiles than the GPU holds at once
+ * (2 workgroups per CU), or the last wave of tiles would be less than a
+ * quarter full, the k-blocks of the remaining tiles are split between
+ * workgroups; their fp32 partial sums are stored to a workspace and a second
+ * kernel, enqueued on the same stream, adds them in k order. The split
+ * depends only on M, N, K and the device's compute-unit count, so the bits
+ * are the same on every call.
+ * Workspace: the first call that splits tiles on a given (device, stream)
+ * allocates that pair's workspace (2 * 2 * CUs * 64 KB, 64 MB on a 256-CU
+ * device) and keeps it until the process ends; make that first call outside
+ * stream capture. Calls on one stream reuse it in stream order; calls on
+ * different streams never share one. Returns W8A16_ERR_MEMORY if it cannot
+ * be allocated (nothing is launched then).
  */
 int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
                int64_t M, int64_t N, int64_t K, void* stream);

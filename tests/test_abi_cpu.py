@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_covers_every_status():
     for st in (binding.OK, binding.ERR_NULL, binding.ERR_SHAPE, binding.ERR_ALIGN,
-               binding.ERR_LAUNCH, binding.ERR_ALIAS, binding.ERR_ARG):
+               binding.ERR_LAUNCH, binding.ERR_ALIAS, binding.ERR_ARG, binding.ERR_MEMORY):
         s = binding.strerror(st)
         assert s and "unknown" not in s
     assert "unknown" in binding.strerror(12345)
