@@ -26,6 +26,8 @@
 //    butterfly that halves the value count at every step (so the cost per
 //    output shrinks as RB*MR grows), then across the kw waves through LDS.
 //    The order of every sum is fixed: results are deterministic. No atomics.
+#include <algorithm>
+
 #include "w8a16_device.h"
 #include "w8a16_host.h"
 
@@ -278,12 +280,22 @@ extern "C" int w8a16_gemv(const void* A, const void* Wq, const void* scale, void
     const int j = K > static_cast<int64_t>(kWaveK) * kMaxWaves ? 2 : 1;
     const int nwaves = static_cast<int>(ceil_div(K, static_cast<int64_t>(kWaveK) * j));
     if (nwaves > kMaxWaves || j > max_chunks(mr)) return W8A16_ERR_SHAPE;
-    const Choice c = select_kernel(mr, j);
-
+    Choice c = select_kernel(mr, j);
+    const int64_t cus = device_cu_count();
+    int64_t per_block;
+    if (mr == 1 && j == 1) {
+        // Single-token decode, launch shape measured on the Mamba-2 projection
+        // shapes: 4-row groups while they number at least 8 per CU, else
+        // 8-row groups; one group per workgroup up to about 18 workgroups per
+        // CU, then several.
+        const int rb = ceil_div(N, 4) >= 8 * cus ? 4 : 8;
+        c = {rb == 4 ? &gemv_kernel<1, 1, 4> : &gemv_kernel<1, 1, 8>, rb};
+        per_block = std::max<int64_t>(1, ceil_div(N, rb) / (18 * cus));
+    } else {
+        const int64_t resident = cus * (kWavesPerCu / nwaves > 0 ? kWavesPerCu / nwaves : 1);
+        per_block = ceil_div(ceil_div(N, c.rows_per_group), resident);
+    }
     const int64_t groups = ceil_div(N, c.rows_per_group);
-    const int64_t resident = static_cast<int64_t>(device_cu_count()) *
-                             (kWavesPerCu / nwaves > 0 ? kWavesPerCu / nwaves : 1);
-    const int64_t per_block = ceil_div(groups, resident);
     const int64_t blocks = ceil_div(groups, per_block);
 
     return launch(c.fn, dim3(static_cast<unsigned>(blocks)), dim3(64 * nwaves),
