@@ -295,34 +295,43 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
         };
 
         // One k-step on stage SLOT: 12 operand reads, 32 converts, 16 MFMAs.
-        // The first k-step of a scale block starts the block accumulator from
-        // zero.
+        // All reads are issued first (the scheduling barrier keeps them
+        // there), so the MFMAs wait on them in order instead of on one read
+        // at a time. The first k-step of a scale block starts the block
+        // accumulator from zero.
         auto compute = [&](auto slot_c, auto first_c) {
             constexpr int kSlot = decltype(slot_c)::value;
             constexpr bool kFirst = decltype(first_c)::value;
             const uint8_t* stage = smem + kSlot * kStageBytes;
+            u32x4_t wq[2][2];                           // [bj][j]
+            bf16x8_t av[2][2][2];                       // [bi][j][h]
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj) wq[bj][j] = *reinterpret_cast<const u32x4_t*>(stage + w_addr[bj][j]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int bi = 0; bi < 2; ++bi)
+                        av[bi][j][h] = *reinterpret_cast<const bf16x8_t*>(stage + a_addr[bi][j][h]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {               // two 32-wide k spans
                 bf16x8_t bw[2][2];                      // [bj][h]
 #pragma unroll
                 for (int bj = 0; bj < 2; ++bj) {
-                    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(stage + w_addr[bj][j]);
-                    bw[bj][0] = e4m3x8_to_bf16(q[0], q[1]);
-                    bw[bj][1] = e4m3x8_to_bf16(q[2], q[3]);
+                    bw[bj][0] = e4m3x8_to_bf16(wq[bj][j][0], wq[bj][j][1]);
+                    bw[bj][1] = e4m3x8_to_bf16(wq[bj][j][2], wq[bj][j][3]);
                 }
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    bf16x8_t av[2];
-#pragma unroll
-                    for (int bi = 0; bi < 2; ++bi)
-                        av[bi] = *reinterpret_cast<const bf16x8_t*>(stage + a_addr[bi][j][h]);
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
                         for (int bj = 0; bj < 2; ++bj)
                             blk[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                av[bi], bw[bj][h], (kFirst && j == 0 && h == 0) ? zero : blk[bi][bj], 0, 0, 0);
-                }
+                                av[bi][j][h], bw[bj][h], (kFirst && j == 0 && h == 0) ? zero : blk[bi][bj], 0, 0, 0);
             }
         };
 
