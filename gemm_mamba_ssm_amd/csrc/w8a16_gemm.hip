@@ -61,21 +61,43 @@
 namespace w8a16 {
 namespace {
 
-constexpr int TM = 128, TN = 128, TK = 64;
-constexpr int kThreads = 256;
-constexpr int kWgPerCu = 2;                          // resident workgroups per CU (2 x 72 KB of LDS)
-constexpr int kStages = 3;
-constexpr int kATileBytes = TM * TK * 2;            // 16 KB of BF16
-constexpr int kWTileBytes = TN * TK;                // 8 KB of E4M3
-constexpr int kStageBytes = kATileBytes + kWTileBytes;
-constexpr int kAChunksPerThread = kATileBytes / 16 / kThreads;   // 4
-constexpr int kWChunksPerThread = kWTileBytes / 16 / kThreads;   // 2
-constexpr int kTileFloats = TM * TN;                // one fp32 partial tile (64 KB)
-constexpr int kMinShareBlocks = 4;                  // fewest k-blocks a shared tile hands one workgroup
+constexpr int TN = 128, TK = 64;                    // every tile is 128 columns: one scale block
+constexpr int kThreads = 256;                       // 4 waves
 constexpr uint32_t kOutOfRange = 0x80000000u;       // buffer offset that reads as zero
 constexpr int kBufferFlags = 0x00020000;            // raw buffer, 32-bit data format
 
-static_assert(kScaleBlock % TN == 0 && kScaleBlock == 2 * TK, "two k-steps per scale block");
+static_assert(kScaleBlock == TN && kScaleBlock == 2 * TK, "one scale block per tile column, two k-steps per block");
+
+// Tile shape of one kernel instance: the 4 waves form a WAVES_M x (4 /
+// WAVES_M) grid, each wave BI x BJ MFMA blocks of 32 x 32.
+//  * Big      (M > 64):  128 x 128, 2 x 2 waves of 64 x 64, 2 workgroups per CU;
+//  * Skinny64 (M <= 64):  64 x 128, 1 x 4 waves of 64 x 32, 3 workgroups per CU;
+//  * Skinny32 (M <= 32):  32 x 128, 1 x 4 waves of 32 x 32, 4 workgroups per CU.
+// The skinny tiles do not pad M to 128 rows (at M = 16 that would be 8x the
+// MFMA work) and keep more workgroups and more stages in flight per CU, since
+// there the weights stream from HBM with little work per byte.
+template <int WAVES_M, int BI_, int BJ_, int WG_PER_CU, int STAGES, int MIN_SHARE>
+struct TileShape {
+    static constexpr int WM = WAVES_M, WN = 4 / WAVES_M, BI = BI_, BJ = BJ_;
+    static constexpr int TM = WM * BI * 32;
+    static constexpr int kWgPerCu = WG_PER_CU;                 // resident workgroups per CU
+    static constexpr int kStages = STAGES;                     // LDS ring (kStages - 1 steps in flight)
+    static constexpr int kATileBytes = TM * TK * 2;            // BF16
+    static constexpr int kWTileBytes = TN * TK;                // E4M3
+    static constexpr int kStageBytes = kATileBytes + kWTileBytes;
+    static constexpr int kAChunksPerThread = kATileBytes / 16 / kThreads;
+    static constexpr int kWChunksPerThread = kWTileBytes / 16 / kThreads;
+    static constexpr int kChunks = kAChunksPerThread + kWChunksPerThread;
+    static constexpr int kTileFloats = TM * TN;                // one fp32 partial tile
+    static constexpr int kMinShareBlocks = MIN_SHARE;          // fewest k-blocks a shared tile hands one workgroup
+    static_assert(WN * BJ * 32 == TN, "4 waves cover the 128 columns");
+    static_assert(kAChunksPerThread >= 1 && kATileBytes % (16 * kThreads) == 0, "whole DMA chunks per thread");
+    static_assert(kStages * kStageBytes * kWgPerCu <= 160 * 1024, "LDS of the resident workgroups");
+    static_assert((kStages - 2) * kChunks < 64, "vmcnt field");
+};
+using BigTile = TileShape<2, 2, 2, 2, 3, 4>;
+using Skinny64 = TileShape<1, 2, 1, 3, 3, 4>;
+using Skinny32 = TileShape<1, 1, 1, 4, 3, 4>;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -153,10 +175,33 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-__global__ void __launch_bounds__(kThreads, kWgPerCu)
-gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
-            const uint16_t* __restrict__ S, uint16_t* __restrict__ out,
-            float* __restrict__ partials, int M, int N, int K, Schedule sc) {
+// Wait until at most `younger` later k-steps' DMA (C::kChunks loads each) of
+// this wave are in flight; younger <= C::kStages - 2.
+template <class C>
+__device__ __forceinline__ void wait_steps(int younger) {
+    static_assert(C::kStages == 3 || C::kStages == 4, "one or two later steps in flight");
+    if constexpr (C::kStages == 4) {
+        if (younger >= 2) {
+            wait_vmem<2 * C::kChunks>();
+            return;
+        }
+    }
+    if (younger >= 1)
+        wait_vmem<C::kChunks>();
+    else
+        wait_vmem<0>();
+}
+
+// The GEMM for tile shape C; each shape has its own kernel below (with its
+// own occupancy bound).
+template <class C>
+__device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
+                                          const uint16_t* __restrict__ S, uint16_t* __restrict__ out,
+                                          float* __restrict__ partials, int M, int N, int K, const Schedule& sc) {
+    constexpr int TM = C::TM, BI = C::BI, BJ = C::BJ, kStages = C::kStages;
+    constexpr int kAChunksPerThread = C::kAChunksPerThread, kWChunksPerThread = C::kWChunksPerThread;
+    constexpr int kATileBytes = C::kATileBytes, kStageBytes = C::kStageBytes;
+    constexpr int kWaveRows = BI * 32, kWaveCols = BJ * 32;
     // One LDS array only: a second __shared__ variable makes the compiler
     // attach alias scopes to LDS accesses, after which it waits for every
     // in-flight DMA before each LDS read (the explicit waits below already
@@ -167,7 +212,7 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     const int w = xcd_remap(blockIdx.x, G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WN, wn = wave % C::WN;
     const int li = lane & 31, lg = lane >> 5;
     const int k_blocks = sc.k_blocks;
     const int nk = (K + TK - 1) / TK;
@@ -193,34 +238,35 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
 
     // Lane-constant operand addresses inside a stage; the stage is added as
     // an immediate offset. A: [bi][j][h], W: [bj][j].
-    int a_addr[2][2][2], w_addr[2][2];
+    int a_addr[BI][2][2], w_addr[BJ][2];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) a_addr[bi][j][h] = a_slot(wm * 64 + bi * 32 + li, 4 * j + 2 * lg + h);
+            for (int h = 0; h < 2; ++h)
+                a_addr[bi][j][h] = a_slot(wm * kWaveRows + bi * 32 + li, 4 * j + 2 * lg + h);
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) w_addr[bj][j] = kATileBytes + w_slot(wn * 64 + bj * 32 + li, 2 * j + lg);
+        for (int j = 0; j < 2; ++j) w_addr[bj][j] = kATileBytes + w_slot(wn * kWaveCols + bj * 32 + li, 2 * j + lg);
 
     const f32x16_t zero = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
                            0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    f32x16_t acc[2][2], blk[2][2];
+    f32x16_t acc[BI][BJ], blk[BI][BJ];
 
     // 32x32 MFMA result layout: lane l holds column l % 32; value v is row
     // 8*(v/4) + 4*(l/32) + v%4 of the block.
-    auto store_tile = [&](const f32x16_t (&r)[2][2], int m0, int n0) {
+    auto store_tile = [&](const f32x16_t (&r)[BI][BJ], int m0, int n0) {
         const int l = opaque(lane), li = l & 31, lg = l >> 5;
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
+        for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const int n = n0 + wn * 64 + bj * 32 + li;
+            for (int bj = 0; bj < BJ; ++bj) {
+                const int n = n0 + wn * kWaveCols + bj * 32 + li;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int m = m0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
+                    const int m = m0 + wm * kWaveRows + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
                     if (m < M && n < N)
                         out[static_cast<int64_t>(m) * N + n] = f32_to_bf16_bits(r[bi][bj][v]);
                 }
@@ -294,42 +340,42 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             }
         };
 
-        // One k-step on stage SLOT: 12 operand reads, 32 converts, 16 MFMAs.
-        // All reads are issued first (the scheduling barrier keeps them
-        // there), so the MFMAs wait on them in order instead of on one read
-        // at a time. The first k-step of a scale block starts the block
-        // accumulator from zero.
+        // One k-step on stage SLOT: the operand reads, 4 * BJ * 4 converts and
+        // 4 * BI * BJ MFMAs. All reads are issued first (the scheduling
+        // barrier keeps them there), so the MFMAs wait on them in order
+        // instead of on one read at a time. The first k-step of a scale block
+        // starts the block accumulator from zero.
         auto compute = [&](auto slot_c, auto first_c) {
             constexpr int kSlot = decltype(slot_c)::value;
             constexpr bool kFirst = decltype(first_c)::value;
             const uint8_t* stage = smem + kSlot * kStageBytes;
-            u32x4_t wq[2][2];                           // [bj][j]
-            bf16x8_t av[2][2][2];                       // [bi][j][h]
+            u32x4_t wq[BJ][2];                          // [bj][j]
+            bf16x8_t av[BI][2][2];                      // [bi][j][h]
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
 #pragma unroll
-                for (int bj = 0; bj < 2; ++bj) wq[bj][j] = *reinterpret_cast<const u32x4_t*>(stage + w_addr[bj][j]);
+                for (int bj = 0; bj < BJ; ++bj) wq[bj][j] = *reinterpret_cast<const u32x4_t*>(stage + w_addr[bj][j]);
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int bi = 0; bi < 2; ++bi)
+                    for (int bi = 0; bi < BI; ++bi)
                         av[bi][j][h] = *reinterpret_cast<const bf16x8_t*>(stage + a_addr[bi][j][h]);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {               // two 32-wide k spans
-                bf16x8_t bw[2][2];                      // [bj][h]
+                bf16x8_t bw[BJ][2];                     // [bj][h]
 #pragma unroll
-                for (int bj = 0; bj < 2; ++bj) {
+                for (int bj = 0; bj < BJ; ++bj) {
                     bw[bj][0] = e4m3x8_to_bf16(wq[bj][j][0], wq[bj][j][1]);
                     bw[bj][1] = e4m3x8_to_bf16(wq[bj][j][2], wq[bj][j][3]);
                 }
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int bi = 0; bi < 2; ++bi)
+                    for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-                        for (int bj = 0; bj < 2; ++bj)
+                        for (int bj = 0; bj < BJ; ++bj)
                             blk[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                                 av[bi][j][h], bw[bj][h], (kFirst && j == 0 && h == 0) ? zero : blk[bi][bj], 0, 0, 0);
             }
@@ -352,55 +398,53 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             }
             const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), kb - s_base));
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
+            for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
+                for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) acc[bi][bj][v] = fmaf(blk[bi][bj][v], s, acc[bi][bj][v]);
         };
 
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
+        for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = zero;
+            for (int bj = 0; bj < BJ; ++bj) acc[bi][bj] = zero;
 
-        // k-step kt (relative to ks0) reads stage kt % 3. Before it: wait for
-        // this wave's DMA of kt (at most the next step's loads remain in
-        // flight), then a barrier, after which every wave's DMA of kt has
-        // landed and every wave is done reading stage (kt + 2) % 3 ==
-        // (kt - 1) % 3, which is refilled with step kt + 2. FIRST: kt is even
+        // k-step kt (relative to ks0) reads stage kt % kStages. Before it:
+        // wait for this wave's DMA of kt (the later steps' loads may remain
+        // in flight), then a barrier, after which every wave's DMA of kt has
+        // landed and every wave is done reading stage (kt - 1) % kStages,
+        // which is refilled with step kt + kStages - 1. FIRST: kt is even
         // (ks0 is even, so this is the first k-step of a scale block); the
-        // unrolled loop below starts at multiples of 6, so the parity is
-        // static.
+        // unrolled loop below starts at multiples of 2 * kStages, so the
+        // stage and the parity are static.
         auto step = [&](auto slot_c, auto first_c, int kt) {
             constexpr int kSlot = decltype(slot_c)::value;
             constexpr bool kFirst = decltype(first_c)::value;
-            if (kt + 1 < len)
-                wait_vmem<kAChunksPerThread + kWChunksPerThread>();
-            else
-                wait_vmem<0>();
+            wait_steps<C>(min(len - 1, kt + kStages - 2) - kt);
             lds_barrier();
-            if (kt + 2 < len) issue(kt + 2, (kSlot + 2) % kStages);
+            if (kt + kStages - 1 < len) issue(kt + kStages - 1, (kSlot + kStages - 1) % kStages);
             compute(slot_c, first_c);
             if (!kFirst || kt + 1 == len) fold(kb0 + (kt >> 1));
         };
 
         // Every wave is done reading the stages of the previous piece.
         lds_barrier();
-        issue(0, 0);
-        if (len > 1) issue(1, 1);
-        using S0 = std::integral_constant<int, 0>;
-        using S1 = std::integral_constant<int, 1>;
-        using S2 = std::integral_constant<int, 2>;
-        using F = std::true_type;
-        using L = std::false_type;
-        for (int kt = 0; kt < len; kt += 2 * kStages) {   // six k-steps: stages 0,1,2,0,1,2
-            step(S0{}, F{}, kt);
-            if (kt + 1 < len) step(S1{}, L{}, kt + 1);
-            if (kt + 2 < len) step(S2{}, F{}, kt + 2);
-            if (kt + 3 < len) step(S0{}, L{}, kt + 3);
-            if (kt + 4 < len) step(S1{}, F{}, kt + 4);
-            if (kt + 5 < len) step(S2{}, L{}, kt + 5);
+#pragma unroll
+        for (int i = 0; i + 1 < kStages; ++i)
+            if (i < len) issue(i, i);
+        constexpr int kUnroll = 2 * kStages;
+        for (int kt = 0; kt < len; kt += kUnroll) {    // stages 0 .. kStages-1, twice
+            step(std::integral_constant<int, 0>{}, std::true_type{}, kt);
+            if (kt + 1 < len) step(std::integral_constant<int, 1 % kStages>{}, std::false_type{}, kt + 1);
+            if (kt + 2 < len) step(std::integral_constant<int, 2 % kStages>{}, std::true_type{}, kt + 2);
+            if (kt + 3 < len) step(std::integral_constant<int, 3 % kStages>{}, std::false_type{}, kt + 3);
+            if (kt + 4 < len) step(std::integral_constant<int, 4 % kStages>{}, std::true_type{}, kt + 4);
+            if (kt + 5 < len) step(std::integral_constant<int, 5 % kStages>{}, std::false_type{}, kt + 5);
+            if constexpr (kUnroll > 6) {
+                if (kt + 6 < len) step(std::integral_constant<int, 6 % kStages>{}, std::true_type{}, kt + 6);
+                if (kt + 7 < len) step(std::integral_constant<int, 7 % kStages>{}, std::false_type{}, kt + 7);
+            }
         }
 
         if (kb0 == 0 && kb1 == k_blocks) {        // the whole tile: write it
@@ -413,21 +457,37 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
         // most two split tiles: its first and its last). Plain stores, no
         // wait: the combine kernel reads them after this kernel has ended.
         const int ts = t - sc.shared_tile0;
-        float* mine = partials + (2 * static_cast<int64_t>(w) + (ts == first_shared ? 0 : 1)) * kTileFloats;
+        float* mine = partials + (2 * static_cast<int64_t>(w) + (ts == first_shared ? 0 : 1)) * C::kTileFloats;
         const int l = opaque(lane), li = l & 31, lg = l >> 5;
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
+        for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const int col = wn * 64 + bj * 32 + li;
+            for (int bj = 0; bj < BJ; ++bj) {
+                const int col = wn * kWaveCols + bj * 32 + li;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int row = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
+                    const int row = wm * kWaveRows + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
                     mine[row * TN + col] = acc[bi][bj][v];
                 }
             }
     }
 }
+
+#define W8A16_GEMM_KERNEL(NAME, C)                                                                   \
+    __global__ void __launch_bounds__(kThreads, C::kWgPerCu)                                         \
+    NAME(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const uint16_t* __restrict__ S, \
+         uint16_t* __restrict__ out, float* __restrict__ partials, int M, int N, int K, Schedule sc) {  \
+        gemm_body<C>(A, W, S, out, partials, M, N, K, sc);                                           \
+    }
+W8A16_GEMM_KERNEL(gemm_kernel_128, BigTile)
+W8A16_GEMM_KERNEL(gemm_kernel_64, Skinny64)
+W8A16_GEMM_KERNEL(gemm_kernel_32, Skinny32)
+#undef W8A16_GEMM_KERNEL
+
+template <class C> struct GemmKernel;
+template <> struct GemmKernel<BigTile> { static constexpr auto fn = &gemm_kernel_128; };
+template <> struct GemmKernel<Skinny64> { static constexpr auto fn = &gemm_kernel_64; };
+template <> struct GemmKernel<Skinny32> { static constexpr auto fn = &gemm_kernel_32; };
 
 // Combine of the split tiles. The host lists, for every split tile, the
 // workgroup that computed its first k-blocks (the tile is the last of that
@@ -437,7 +497,6 @@ gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
 // the loads of kCombineBatch parts before their additions, and writes BF16.
 constexpr int kMaxSplits = 1536;                       // list capacity (3 KB of kernel arguments)
 constexpr int kCombineRows = 32;
-constexpr int kCombineRowGroups = TM / kCombineRows;
 constexpr int kCombineBatch = 4;
 static_assert(kThreads == 8 * (TN / 4), "8 rows of float4 per pass");
 
@@ -445,9 +504,11 @@ struct SplitList {
     uint16_t first[kMaxSplits];
 };
 
+template <class C>
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, int M, int N,
                Schedule sc, SplitList list) {
+    constexpr int TM = C::TM, kTileFloats = C::kTileFloats;
     const int w = list.first[blockIdx.x];
     const int k_blocks = sc.k_blocks;
     const int ts = static_cast<int>((share_start(sc, w + 1) - 1) / k_blocks);
@@ -496,11 +557,12 @@ combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, i
 }
 
 // Choose the schedule; returns the grid size. `slots` is the number of
-// workgroups resident at once (2 per CU). Whole tiles, one per workgroup,
-// when they fill the slots evenly or the last wave is at least a quarter full
-// (splitting k then costs more in partial-tile traffic than the idle slots);
-// otherwise whole rounds of `slots` tiles plus a shared part over the rest.
-int plan(int64_t tiles, int64_t tiles_m, int k_blocks, int slots, Schedule* sc) {
+// workgroups resident at once. Whole tiles, one per workgroup, when they fill
+// the slots evenly or the last wave is at least a quarter full (splitting k
+// then costs more in partial-tile traffic than the idle slots); otherwise
+// whole rounds of `slots` tiles plus a shared part over the rest, with at
+// least `min_share` k-blocks per workgroup.
+int plan(int64_t tiles, int64_t tiles_m, int k_blocks, int slots, int min_share, Schedule* sc) {
     *sc = Schedule{};
     sc->tiles_m = static_cast<int>(tiles_m);
     sc->k_blocks = k_blocks;
@@ -511,7 +573,7 @@ int plan(int64_t tiles, int64_t tiles_m, int k_blocks, int slots, Schedule* sc) 
         return static_cast<int>(tiles);
     }
     const int64_t units = rest * k_blocks;
-    const int64_t groups = std::min<int64_t>(slots, std::max<int64_t>(rest, units / kMinShareBlocks));
+    const int64_t groups = std::min<int64_t>(slots, std::max<int64_t>(rest, units / min_share));
     sc->full_rounds = static_cast<int>(rounds);
     sc->shared_tile0 = static_cast<int>(rounds * slots);
     sc->shared_groups = static_cast<int>(groups);
@@ -539,34 +601,67 @@ int list_splits(const Schedule& sc, SplitList* list) {
 }
 
 // Workspace of one (device, stream): two partial-tile slots per workgroup of
-// the largest grid. Allocated on first use and kept until the process ends.
+// the largest grid of any tile shape (at most 64 MB on a 256-CU device).
+// Allocated on first use, grown when a larger one is needed, and kept until
+// the process ends.
 struct Workspace {
     float* partials = nullptr;
-    int groups = 0;
+    size_t bytes = 0;
 };
 
-int workspace_for(hipStream_t stream, int groups, Workspace* ws) {
+int workspace_for(hipStream_t stream, size_t bytes, Workspace* ws) {
     static std::mutex mu;
     static auto* cache = new std::map<std::pair<int, hipStream_t>, Workspace>();
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return W8A16_ERR_LAUNCH;
     std::lock_guard<std::mutex> lock(mu);
     auto it = cache->find({dev, stream});
-    if (it != cache->end() && it->second.groups >= groups) {
+    if (it != cache->end() && it->second.bytes >= bytes) {
         *ws = it->second;
         return W8A16_OK;
     }
     void* p = nullptr;
-    if (hipMalloc(&p, static_cast<size_t>(2) * groups * kTileFloats * sizeof(float)) != hipSuccess)
-        return W8A16_ERR_MEMORY;
+    if (hipMalloc(&p, bytes) != hipSuccess) return W8A16_ERR_MEMORY;
     // A smaller workspace of the same key is only replaced, never freed: work
     // already enqueued on the stream may still use it.
     Workspace fresh;
     fresh.partials = static_cast<float*>(p);
-    fresh.groups = groups;
+    fresh.bytes = bytes;
     (*cache)[{dev, stream}] = fresh;
     *ws = fresh;
     return W8A16_OK;
+}
+
+// Plan and launch the GEMM (and, if tiles are split, the combine) with tile
+// shape C.
+template <class C>
+int run_gemm(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
+             hipStream_t s) {
+    // Buffer offsets are 32-bit: one tile's rows of A must span less than 2 GiB.
+    if (static_cast<int64_t>(C::TM) * K * 2 >= static_cast<int64_t>(kOutOfRange)) return W8A16_ERR_SHAPE;
+    const int64_t tiles_m = ceil_div(M, C::TM);
+    const int64_t tiles = tiles_m * ceil_div(N, TN);
+    if (tiles > INT32_MAX) return W8A16_ERR_SHAPE;
+    const int k_blocks = static_cast<int>(ceil_div(K, kScaleBlockHost));
+    const int slots = std::min(C::kWgPerCu * device_cu_count(), kMaxSplits);
+    Schedule sc;
+    const int grid = plan(tiles, tiles_m, k_blocks, slots, C::kMinShareBlocks, &sc);
+    Workspace ws;
+    if (sc.shared_groups > 0) {
+        const int st = workspace_for(s, static_cast<size_t>(2) * slots * C::kTileFloats * sizeof(float), &ws);
+        if (st != W8A16_OK) return st;
+    }
+    int st = launch(GemmKernel<C>::fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), s,
+                    static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq),
+                    static_cast<const uint16_t*>(scale), static_cast<uint16_t*>(out), ws.partials,
+                    static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), sc);
+    if (st != W8A16_OK || sc.shared_groups == 0) return st;
+    SplitList list;
+    const int splits = list_splits(sc, &list);
+    if (splits == 0) return W8A16_OK;
+    return launch(&combine_kernel<C>, dim3(static_cast<unsigned>(splits), C::TM / kCombineRows), dim3(kThreads), s,
+                  static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), static_cast<int>(M),
+                  static_cast<int>(N), sc, list);
 }
 
 }  // namespace
@@ -576,32 +671,13 @@ extern "C" int w8a16_gemm(const void* A, const void* Wq, const void* scale, void
                           int64_t M, int64_t N, int64_t K, void* stream) {
     using namespace w8a16;
     bool noop = false;
-    int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
+    const int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
     if (st != W8A16_OK || noop) return st;
-    // Buffer offsets are 32-bit: one tile's rows of A must span less than 2 GiB.
-    if (static_cast<int64_t>(TM) * K * 2 >= static_cast<int64_t>(kOutOfRange)) return W8A16_ERR_SHAPE;
-    const int64_t tiles_m = ceil_div(M, TM);
-    const int64_t tiles = tiles_m * ceil_div(N, TN);
-    if (tiles > INT32_MAX) return W8A16_ERR_SHAPE;
-    const int k_blocks = static_cast<int>(ceil_div(K, kScaleBlockHost));
-    const int slots = std::min(kWgPerCu * device_cu_count(), kMaxSplits);
-    Schedule sc;
-    const int grid = plan(tiles, tiles_m, k_blocks, slots, &sc);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    Workspace ws;
-    if (sc.shared_groups > 0) {
-        st = workspace_for(s, slots, &ws);
-        if (st != W8A16_OK) return st;
-    }
-    st = launch(&gemm_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), s,
-                static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq),
-                static_cast<const uint16_t*>(scale), static_cast<uint16_t*>(out), ws.partials,
-                static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), sc);
-    if (st != W8A16_OK || sc.shared_groups == 0) return st;
-    SplitList list;
-    const int splits = list_splits(sc, &list);
-    if (splits == 0) return W8A16_OK;
-    return launch(&combine_kernel, dim3(static_cast<unsigned>(splits), kCombineRowGroups), dim3(kThreads), s,
-                  static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), static_cast<int>(M),
-                  static_cast<int>(N), sc, list);
+#ifndef W8A16_TILED_SKINNY32
+    if (skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, out, M, N, K, s);
+#endif
+    if (M <= Skinny32::TM) return run_gemm<Skinny32>(A, Wq, scale, out, M, N, K, s);
+    if (M <= Skinny64::TM) return run_gemm<Skinny64>(A, Wq, scale, out, M, N, K, s);
+    return run_gemm<BigTile>(A, Wq, scale, out, M, N, K, s);
 }

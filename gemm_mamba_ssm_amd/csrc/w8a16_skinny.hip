@@ -1,0 +1,244 @@
+// Skinny GEMM for the w8a16 block-scaled FP8 projection, M <= 32 rows:
+//
+//   out[m][n] = sum_k A[m][k] * E4M3(W[n][k]) * scale[n/128][k/128]
+// (Qwen3SsmLayer docs, `set_fp8_decode_weights`; NemotronMamba2Layer docs,
+// `set_fp8_weights`). A few tokens at once (TransformerLayer docs,
+// `decode_multi_seq`, and the K-token verify of speculative decoding) read
+// every weight once for all rows, so the time is the weight stream from HBM.
+//
+// The layout follows the decode GEMV (keep many weight loads in flight, keep
+// the activations in registers) with the matrix cores doing the products:
+//  * K is split across the S waves of a workgroup: wave w owns a contiguous
+//    range of at most KB 128-wide k-blocks, and holds the activations of that
+//    range (all M rows, as MFMA A operands) in registers for the whole kernel;
+//  * a workgroup walks a contiguous range of 16-row weight blocks; for each,
+//    every wave streams its 16 x (KB * 128)-byte slice straight from HBM into
+//    registers, one block ahead (the loads of the next block are in flight
+//    while the current one is multiplied);
+//  * each k-block is two v_mfma_f32_16x16x32_bf16 steps per 16 rows of A;
+//    lane l carries row l % 16 and k = 64c + 16(l / 16) + 8h + [0, 8) of
+//    chunk c, step h, for both operands, so one 16-byte load of W feeds both
+//    steps of a chunk, and the block scale is applied exactly in fp32
+//    (acc += scale * blk);
+//  * the S partial 16 x 16 tiles of a block meet in LDS and are added in wave
+//    order (ascending k): the result is deterministic.
+#include <algorithm>
+
+#include "w8a16_device.h"
+#include "w8a16_host.h"
+
+namespace w8a16 {
+namespace {
+
+constexpr int kRows = 16;                  // weight rows per workgroup (one MFMA column block)
+constexpr int kMaxWaves = 16;              // per workgroup
+constexpr int kMaxBlocksPerWg = 32;        // 16-row weight blocks per workgroup at most
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
+static_assert(kScaleBlock % kRows == 0, "a workgroup's rows share one scale row");
+
+// 8 E4M3 codes (two dwords) -> 8 BF16, exact.
+__device__ __forceinline__ bf16x8_t e4m3x8(uint32_t lo, uint32_t hi) {
+    const bf16x2_t p0 = e4m3x2_to_bf16(lo, false), p1 = e4m3x2_to_bf16(lo, true);
+    const bf16x2_t p2 = e4m3x2_to_bf16(hi, false), p3 = e4m3x2_to_bf16(hi, true);
+    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// MB = 16-row blocks of A (1 for M <= 16, 2 for M <= 32); KB = k-blocks per
+// wave at most (the activations of KB k-blocks take 16 * MB * KB VGPRs); D =
+// weight blocks in flight per wave; MAXW = waves per workgroup at most.
+template <int MB, int KB, int D, int MAXW>
+__global__ void __launch_bounds__(64 * MAXW)
+skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
+              uint16_t* __restrict__ out, int M, int N, int K, int blocks_per_wg) {
+    // Partial tiles of the waves, double-buffered by block parity:
+    // [parity][wave][mb][lane] x 4 floats.
+    __shared__ f32x4_t red[2][MAXW * MB * 64];
+    // The workgroup's outputs, written out after the loop (so that the loop
+    // issues no vector-memory stores, which would share the loads' counter).
+    __shared__ uint16_t outs[kMaxBlocksPerWg * 256 * MB];
+
+    const int waves = blockDim.x / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int lane = threadIdx.x % 64;
+    const int r = lane % 16, g = lane / 16;
+    const int k_blocks = (K + kScaleBlock - 1) / kScaleBlock;
+    const int kb0 = wave * KB;                       // this wave's k-blocks: [kb0, kb0 + KB) within k_blocks
+    const int nblk = (N + kRows - 1) / kRows;
+    const int blk0 = blockIdx.x * blocks_per_wg, blk1 = min(nblk, blk0 + blocks_per_wg);
+    if (blk0 >= blk1) return;                        // uniform over the workgroup
+
+    // Lane's k of chunk c of the wave's j-th k-block (K % 16 == 0, so a
+    // lane's 16 bytes are all inside K or all outside).
+    auto kof = [&](int j, int c) { return (kb0 + j) * kScaleBlock + 64 * c + 16 * g; };
+    uint32_t w_off[KB][2];
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) w_off[j][c] = kof(j, c) < K ? static_cast<uint32_t>(r * K + kof(j, c)) : kOutOfRange;
+
+    // Activations of the wave's k-range, [mb][j][c][h]: 8 BF16 each.
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, M * K * 2, kBufferFlags);
+    u32x4_t a[MB][KB][2][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = kof(j, c) + 8 * h;
+                    a[mb][j][c][h] =
+                        __builtin_amdgcn_raw_buffer_load_b128(ra, k < K ? ((mb * 16 + r) * K + k) * 2 : kOutOfRange, 0, 0);
+                }
+
+    // Scales of the workgroup's rows and the wave's k-blocks: lane l holds
+    // scale row srow0 + l / KB, k-block kb0 + l % KB (a workgroup's rows span
+    // at most kMaxBlocksPerWg * 16 / 128 + 2 scale rows).
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(S), 0, ((N + kScaleBlock - 1) / kScaleBlock) * k_blocks * 2, kBufferFlags);
+    constexpr int kScaleRows = 64 / KB;
+    static_assert(kMaxBlocksPerWg * kRows / kScaleBlock + 2 <= kScaleRows, "one scale load per workgroup");
+    auto load_scales = [&](int srow0) {
+        const int srow = srow0 + lane / KB, kb = kb0 + lane % KB;
+        const bool ok = srow * kScaleBlock < N && kb < k_blocks;
+        return bf16_bits_to_f32(
+            __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? (srow * k_blocks + kb) * 2 : kOutOfRange, 0, 0));
+    };
+    const int srow0 = blk0 * kRows / kScaleBlock;
+    const float s_lane = load_scales(srow0);
+
+    // Weights of row block b into a ring slot: [j][c], 16 bytes each; rows
+    // past N read zeros (beyond the buffer's range). Blocks past the
+    // workgroup's range get an empty range and load zeros: the loads are the
+    // same in every step (so the waits are too, also the compiler's own).
+    u32x4_t wr[D][KB][2];
+    auto issue = [&](int b, u32x4_t (&dst)[KB][2]) {
+        const bool live = b < blk1;
+        const int n0 = (live ? b : blk0) * kRows;
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, live ? min(kRows, N - n0) * K : 0,
+            kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) dst[j][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[j][c], 0, 0);
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(blk0 + d, wr[d]);
+
+    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    int parity = 0;
+    // Block bb in ring slot d: wait for its loads (the later blocks' stay in
+    // flight), multiply, refill the slot with block bb + D, then reduce.
+    auto block = [&](int bb, u32x4_t (&w)[KB][2]) {
+        // Loads in flight, oldest first: this block, then the D - 1 later ones.
+        wait_vmem<(D - 1) * 2 * KB>();
+        __builtin_amdgcn_sched_barrier(0);
+        const int srow = bb * kRows / kScaleBlock;   // srow - srow0 < kScaleRows
+        f32x4_t acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = zero;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const float s =
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), (srow - srow0) * KB + j));
+            f32x4_t blk[MB];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const bf16x8_t bw0 = e4m3x8(w[j][c][0], w[j][c][1]), bw1 = e4m3x8(w[j][c][2], w[j][c][3]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        blk[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, a[mb][j][c][h]), h ? bw1 : bw0,
+                            (c == 0 && h == 0) ? zero : blk[mb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[mb][v] = fmaf(blk[mb][v], s, acc[mb][v]);
+        }
+        issue(bb + D, w);
+        // 16x16 MFMA result layout: lane l holds column l % 16, rows
+        // 4(l/16) + v. Thread t < 256 * MB then writes output (row, column) =
+        // (t / 16, t % 16): the sum over the waves in k order.
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) red[parity][(wave * MB + mb) * 64 + lane] = acc[mb];
+        __syncthreads();
+        if (threadIdx.x < 256 * MB) {                // blockDim.x >= 256 * MB
+            const int t = threadIdx.x;
+            const int row = t / 16, col = t % 16;
+            const int mb = row / 16, rr = row % 16;
+            const int l = col + 16 * (rr / 4), v = rr % 4;
+            float sum = red[parity][mb * 64 + l][v];
+            for (int w2 = 1; w2 < waves; ++w2) sum += red[parity][(w2 * MB + mb) * 64 + l][v];
+            if (bb < blk1) outs[(bb - blk0) * 256 * MB + t] = f32_to_bf16_bits(sum);
+        }
+        // red[parity] is written again two blocks later, after the next
+        // barrier, which every thread reaches only once done reading it.
+        parity ^= 1;
+    };
+    // D blocks per iteration, the last iteration padded with blocks past the
+    // range (their weights load as zeros and their outputs are dropped): the
+    // loads and waits are the same in every iteration.
+    static_assert(D >= 2 && D <= 4, "ring of 2 to 4 blocks");
+    for (int b = blk0; b < blk1; b += D) {
+        block(b, wr[0]);
+        block(b + 1, wr[1]);
+        if constexpr (D >= 3) block(b + 2, wr[2]);
+        if constexpr (D >= 4) block(b + 3, wr[3]);
+    }
+    wait_vmem<0>();                                  // the zero loads past the range
+    __syncthreads();
+    // Output (row, column n0 + col) of block b sits at outs[(b - blk0) * 256 *
+    // MB + row * 16 + col]; threads take 16-column runs of one row.
+    const int per_row = blk1 - blk0;
+    for (int i = threadIdx.x; i < per_row * 16 * 16 * MB; i += blockDim.x) {
+        const int row = i / (per_row * 16), rest = i % (per_row * 16);
+        const int b = rest / 16, col = rest % 16;
+        const int n = (blk0 + b) * kRows + col;
+        if (row < M && n < N) out[static_cast<int64_t>(row) * N + n] = outs[b * 256 * MB + row * 16 + col];
+    }
+}
+
+}  // namespace
+
+// M <= 16, K <= 4096. Waves per workgroup: enough that each holds at most
+// two k-blocks of activations, at least 4. The grid aims at about 16 resident
+// waves per CU, each workgroup taking a contiguous range of 16-row weight
+// blocks.
+int skinny_gemm(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
+                hipStream_t stream) {
+    if (M < 1 || M > kSkinnyMaxM) return W8A16_ERR_SHAPE;
+    if (!skinny_fits(M, K)) return W8A16_ERR_SHAPE;
+    const int kb_max = 2;
+    const int64_t k_blocks = ceil_div(K, kScaleBlockHost);
+    // Buffer offsets are 32-bit.
+    if (static_cast<int64_t>(kRows) * K >= static_cast<int64_t>(kOutOfRange)) return W8A16_ERR_SHAPE;
+    int waves = static_cast<int>(ceil_div(k_blocks, kb_max));
+    waves = std::max(waves, 4);
+    const int64_t nblk = ceil_div(N, kRows);
+    if (nblk > INT32_MAX) return W8A16_ERR_SHAPE;
+    const int64_t resident = std::max<int64_t>(1, 16 / waves) * device_cu_count();
+    const int64_t per_wg = std::min<int64_t>(kMaxBlocksPerWg, ceil_div(nblk, resident));
+    const dim3 grid(static_cast<unsigned>(ceil_div(nblk, per_wg))), block(64 * waves);
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K), p = static_cast<int>(per_wg);
+    auto a = static_cast<const uint16_t*>(A);
+    auto w = static_cast<const uint8_t*>(Wq);
+    auto s = static_cast<const uint16_t*>(scale);
+    auto o = static_cast<uint16_t*>(out);
+    return launch(&skinny_kernel<1, 2, 3, 16>, grid, block, stream, a, w, s, o, m, n, k, p);
+}
+
+}  // namespace w8a16

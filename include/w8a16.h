@@ -66,31 +66,37 @@ enum w8a16_status {
  * weights read once for all of them). 1 <= M <= 16, N >= 0, K % 16 == 0,
  * 16 <= K <= 16384 for M <= 8 and 16 <= K <= 8192 for M >= 9.
  * M == 0 or N == 0 is a no-op returning W8A16_OK.
- * Each weight byte is read from HBM once per call for all M rows.
+ * Each weight byte is read from HBM once per call for all M rows. From
+ * M = 4 on, with K <= 4096, the call runs the skinny path of w8a16_gemm
+ * (products on the matrix cores; same result contract).
  */
 int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
                int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Prefill GEMM: M prompt tokens at once (TransformerLayer docs, `prefill`:
- * the weights are read once for all N tokens as one GEMM with M = N).
+ * the weights are read once for all N tokens as one GEMM with M = N), and
+ * the skinny case of a few tokens (speculative verify, batched decode).
  * M >= 0 (any), N >= 0, 16 <= K < 2^23, K % 16 == 0; M == 0 or N == 0 is a
- * no-op. The E4M3 weight bytes of a tile are staged once per workgroup and
- * decoded in registers; the block scale is applied in fp32 per 128-wide
- * k-block, as in the GEMV.
- * When there are fewer 128 x 128 output tiles than the GPU holds at once
- * (2 workgroups per CU), or the last wave of tiles would be less than a
- * quarter full, the k-blocks of the remaining tiles are split between
- * workgroups; their fp32 partial sums are stored to a workspace and a second
- * kernel, enqueued on the same stream, adds them in k order. The split
- * depends only on M, N, K and the device's compute-unit count, so the bits
- * are the same on every call.
+ * no-op. The block scale is applied in fp32 per 128-wide k-block, as in the
+ * GEMV. Paths, chosen by M and K only:
+ *  - M <= 16 and K <= 4096: the weights stream from HBM straight into the
+ *    matrix-core operands (one kernel, no workspace);
+ *  - otherwise output tiles of 32 (M <= 32), 64 (M <= 64) or 128 rows by 128
+ *    columns: the E4M3 weight bytes of a tile are staged once per workgroup
+ *    and decoded in registers. When there are fewer tiles than the GPU holds
+ *    at once, or the last wave of tiles would be less than a quarter full,
+ *    the k-blocks of the remaining tiles are split between workgroups; their
+ *    fp32 partial sums are stored to a workspace and a second kernel,
+ *    enqueued on the same stream, adds them in k order.
+ * Every choice depends only on M, N, K and the device's compute-unit count,
+ * so the bits are the same on every call.
  * Workspace: the first call that splits tiles on a given (device, stream)
- * allocates that pair's workspace (2 * 2 * CUs * 64 KB, 64 MB on a 256-CU
- * device) and keeps it until the process ends; make that first call outside
- * stream capture. Calls on one stream reuse it in stream order; calls on
- * different streams never share one. Returns W8A16_ERR_MEMORY if it cannot
- * be allocated (nothing is launched then).
+ * allocates that pair's workspace (at most 64 MB on a 256-CU device; grown
+ * if a later shape needs more) and keeps it until the process ends; make
+ * that first call outside stream capture. Calls on one stream reuse it in
+ * stream order; calls on different streams never share one. Returns
+ * W8A16_ERR_MEMORY if it cannot be allocated (nothing is launched then).
  */
 int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
                int64_t M, int64_t N, int64_t K, void* stream);

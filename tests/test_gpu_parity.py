@@ -139,15 +139,27 @@ def test_gemv_k_edges(dev, M, N, K):
 
 # --- GEMM ------------------------------------------------------------------------
 
-# Shapes span whole tiles only (few tiles, short K), tiles whose k-blocks are
-# split between workgroups (fewer tiles than the grid's slots and K >= 1024),
-# and more tiles than one round of the 2-per-CU grid: N = 65704 and 78339 with
-# M <= 128 give 514 and 613 tiles (a whole round plus a split remainder),
-# N = 89603 gives 701 (whole tiles only, the last wave over a quarter full).
+# M <= 16 with K <= 4096 streams the weights through the skinny kernel (16-row
+# weight blocks, K split over 4 to 16 waves, ring of 3 blocks per wave; ragged
+# N, idle waves when K is short, several blocks per workgroup). Otherwise the
+# GEMM has three tile shapes: 32 x 128 for M <= 32 (4 workgroups per CU),
+# 64 x 128 for M <= 64 (3 per CU) and 128 x 128 above (2 per CU). For each,
+# the shapes span whole tiles only (few tiles, short K), tiles whose k-blocks
+# are split between workgroups (fewer tiles than the grid's slots), and more
+# tiles than one round of the grid on a 256-CU device:
+#  * 128 x 128: N = 65704 and 78339 with 65 <= M <= 128 give 514 and 613
+#    tiles (a whole round of 512 plus a split remainder), N = 89603 gives 701
+#    (whole tiles only, the last wave over a quarter full);
+#  * 32 x 128: N = 140000 gives 1094 tiles (a round of 1024 plus a split
+#    remainder), N = 166400 gives 1300 (whole tiles only);
+#  * 64 x 128: N = 98400 gives 769 tiles (a round of 768 plus one split tile).
 @pytest.mark.parametrize("M,N,K", [(1, 384, 256), (17, 130, 144), (127, 300, 272), (129, 1000, 1040),
                                    (300, 257, 4096), (256, 256, 128), (1, 1, 16), (64, 4096, 512),
-                                   (513, 640, 1024), (130, 18560, 128), (3, 65704, 1040),
-                                   (5, 78339, 2048), (5, 89603, 2048)])
+                                   (513, 640, 1024), (130, 18560, 128), (66, 65704, 1040),
+                                   (72, 78339, 1040), (65, 89603, 1040), (32, 18560, 4096), (20, 4096, 8192),
+                                   (3, 140000, 1040), (5, 166400, 528), (33, 1000, 1040), (48, 18560, 2048),
+                                   (40, 98400, 528), (31, 300, 4112), (16, 18560, 4096), (9, 1000, 4096),
+                                   (7, 1000, 8208), (2, 4100, 1936)])
 def test_gemm_every_element(dev, M, N, K):
     say(f"gemm M={M} N={N} K={K}")
     A = inputs.activations(M, K, 900 + M)
@@ -192,7 +204,7 @@ def test_gemv_matches_gemm_on_decode_shapes(dev):
 ENTRY = {"gemv": binding.w8a16_gemv, "gemm": binding.w8a16_gemm}
 
 
-@pytest.mark.parametrize("entry,M", [("gemv", 4), ("gemv", 16), ("gemm", 130)])
+@pytest.mark.parametrize("entry,M", [("gemv", 4), ("gemv", 16), ("gemm", 130), ("gemm", 20), ("gemm", 40)])
 def test_one_hot_rows_return_rounded_dequantized_columns(dev, entry, M):
     N, K = 300, 1040
     W, S = inputs.weights(N, K, 0.02, 31)
@@ -213,7 +225,7 @@ def test_zero_weights_give_exact_zero(dev, entry):
     assert np.all((got & 0x7FFF) == 0)
 
 
-@pytest.mark.parametrize("entry,M", [("gemv", 6), ("gemm", 200)])
+@pytest.mark.parametrize("entry,M", [("gemv", 6), ("gemm", 200), ("gemm", 24), ("gemm", 56)])
 def test_sign_scaling_permutation_and_determinism(dev, entry, M):
     N, K = 520, 2048
     A = inputs.activations(M, K, 51)
@@ -236,7 +248,7 @@ def test_sign_scaling_permutation_and_determinism(dev, entry, M):
     assert np.array_equal(got, base[perm])
 
 
-@pytest.mark.parametrize("entry,M", [("gemv", 3), ("gemm", 150)])
+@pytest.mark.parametrize("entry,M", [("gemv", 3), ("gemm", 150), ("gemm", 10), ("gemm", 60)])
 def test_scale_doubling_touches_only_its_block(dev, entry, M):
     N, K = 300, 1040
     A = inputs.activations(M, K, 61)
