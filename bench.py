@@ -19,9 +19,11 @@ TFLOP/s under `prefill`, each with a roofline object for its larger
 the GEMVs of one projection run back to back between two events (so the
 average launch duration is not inflated by per-event overhead), the GEMMs
 each between their own two events. `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workloads.
+bounded sample of the same workloads. `few_tokens` (outside the timed step)
+reports the same projections at M = 2..16 through the GEMV entry point (the
+multi-sequence decode workloads) and at M = 32..256 through the GEMM.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-few-tokens]
 
 Profile helpers (read rocprofv3 CSV output; no GPU needed):
     python bench.py --summarize-trace <dir>/<name>_kernel_trace.csv
@@ -161,7 +163,7 @@ def summarize_counters(fetch_csv, write_csv, layers=DEFAULT_LAYERS):
     fetch, f_fac = per_launch(fetch_csv, "FETCH_SIZE")
     write, w_fac = per_launch(write_csv, "WRITE_SIZE")
     rec = {"source": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, of "
-                     "`python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration`",
+                     "`python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-few-tokens --copy-calibration`",
            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4), "kernels": {}}
     for lab in fetch:
         kind = lab.split("_")[0]
@@ -212,6 +214,54 @@ class Projection:
                                 self.p_pre.M, self.p_pre.N, self.p_pre.K, stream)
 
 
+FEW_TOKEN_GEMV_M = (2, 4, 8, 16)            # multi-sequence decode (w8a16_gemv)
+FEW_TOKEN_GEMM_M = (32, 64, 128, 256)        # skinny prefill / verify (w8a16_gemm)
+
+
+def few_token_report(projs, device, stream, L, check, reps=10):
+    """Outside the timed step: the same projections at a few tokens, through
+    w8a16_gemv (M = 2..16, the multi-sequence decode workloads) and w8a16_gemm
+    (M = 32..256). Weight copies rotate as in the decode step; each figure is
+    the mean over `reps` runs of L back-to-back launches between two events."""
+    sh = stream.cuda_stream
+    out = {"unit": "us per launch; GB/s = algorithmic bytes / time; frac = of 8 TB/s",
+           "gemv": [], "gemm": []}
+    for entry, ms in (("gemv", FEW_TOKEN_GEMV_M), ("gemm", FEW_TOKEN_GEMM_M)):
+        raw = binding.gemv_raw if entry == "gemv" else binding.gemm_raw
+        for m in ms:
+            row = {"M": m}
+            for proj in projs:
+                p = proj.p_dec
+                if entry == "gemv":
+                    (q,) = [x for x in inputs.WORKLOADS[f"multiseq_m{m}"] if x.name == p.name]
+                    A = inputs.make(q)[0]
+                else:
+                    A = inputs.activations(m, p.K, 5000 + m)
+                dA = to_dev(A, torch.bfloat16, device)
+                dO = torch.empty((m, p.N), dtype=torch.bfloat16, device=device)
+
+                def launch(i):
+                    check(raw(dA.data_ptr(), proj.W[i % proj.copies].data_ptr(), proj.S[i % proj.copies].data_ptr(),
+                              dO.data_ptr(), m, p.N, p.K, sh), entry)
+
+                for i in range(L):
+                    launch(i)
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+                for r in range(reps):
+                    ev[2 * r].record(stream)
+                    for i in range(L):
+                        launch(r * L + i)
+                    ev[2 * r + 1].record(stream)
+                torch.cuda.synchronize()
+                t = np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e-3 for r in range(reps)]) / L
+                nbytes = p.N * p.K + 2 * (-(-p.N // 128)) * (-(-p.K // 128)) + 2 * m * p.K + 2 * m * p.N
+                row[p.name] = {"us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
+                               "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                               "TFLOP/s": round(2 * m * p.N * p.K / t / 1e12, 2)}
+            out[entry].append(row)
+    return out
+
+
 def cpu_baseline(budget_s: float):
     """Time the CPU oracle on a bounded sample of the same two workloads."""
     import oracle
@@ -257,6 +307,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-few-tokens", action="store_true",
+                    help="skip the few-token report (profiler runs: keeps the dispatch order that "
+                         "--summarize-trace / --summarize-counters label)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--layers", type=int, default=DEFAULT_LAYERS, help="decode layers (weight copies) per step")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -320,6 +373,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    few = None if args.no_few_tokens else few_token_report(projs, device, stream, L, check)
+
     if args.copy_calibration:
         src = torch.empty(CALIBRATION_BYTES // 4, dtype=torch.float32, device=device)   # read once, written once
         dst = torch.empty_like(src)
@@ -370,6 +425,7 @@ def main():
             "roofline": roof("mfma", f_in / mean[2] / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s",
                              measured_traffic("gemm", "gemm_in_proj")),
         },
+        "few_tokens": few,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget),
     }
     print(json.dumps(rec), flush=True)

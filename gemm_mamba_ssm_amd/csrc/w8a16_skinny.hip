@@ -1,4 +1,5 @@
-// Skinny GEMM for the w8a16 block-scaled FP8 projection, M <= 32 rows:
+// Skinny GEMM for the w8a16 block-scaled FP8 projection, M <= 16 rows and
+// K <= 4096:
 //
 //   out[m][n] = sum_k A[m][k] * E4M3(W[n][k]) * scale[n/128][k/128]
 // (Qwen3SsmLayer docs, `set_fp8_decode_weights`; NemotronMamba2Layer docs,
@@ -13,8 +14,8 @@
 //    range (all M rows, as MFMA A operands) in registers for the whole kernel;
 //  * a workgroup walks a contiguous range of 16-row weight blocks; for each,
 //    every wave streams its 16 x (KB * 128)-byte slice straight from HBM into
-//    registers, one block ahead (the loads of the next block are in flight
-//    while the current one is multiplied);
+//    registers, D - 1 blocks ahead (a ring of D blocks; D = 2 measured
+//    fastest on the Mamba-2 in_proj shape, D = 3 and 4 were slower);
 //  * each k-block is two v_mfma_f32_16x16x32_bf16 steps per 16 rows of A;
 //    lane l carries row l % 16 and k = 64c + 16(l / 16) + 8h + [0, 8) of
 //    chunk c, step h, for both operands, so one 16-byte load of W feeds both
@@ -238,7 +239,7 @@ int skinny_gemm(const void* A, const void* Wq, const void* scale, void* out, int
     auto w = static_cast<const uint8_t*>(Wq);
     auto s = static_cast<const uint16_t*>(scale);
     auto o = static_cast<uint16_t*>(out);
-    return launch(&skinny_kernel<1, 2, 3, 16>, grid, block, stream, a, w, s, o, m, n, k, p);
+    return launch(&skinny_kernel<1, 2, 2, 16>, grid, block, stream, a, w, s, o, m, n, k, p);
 }
 
 }  // namespace w8a16

@@ -140,7 +140,7 @@ def test_gemv_k_edges(dev, M, N, K):
 # --- GEMM ------------------------------------------------------------------------
 
 # M <= 16 with K <= 4096 streams the weights through the skinny kernel (16-row
-# weight blocks, K split over 4 to 16 waves, ring of 3 blocks per wave; ragged
+# weight blocks, K split over 4 to 16 waves, ring of 2 blocks per wave; ragged
 # N, idle waves when K is short, several blocks per workgroup). Otherwise the
 # GEMM has three tile shapes: 32 x 128 for M <= 32 (4 workgroups per CU),
 # 64 x 128 for M <= 64 (3 per CU) and 128 x 128 above (2 per CU). For each,
