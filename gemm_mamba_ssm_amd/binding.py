@@ -5,12 +5,19 @@ then calls the C ABI declared in ``include/w8a16.h`` on the current torch HIP
 stream. All arithmetic runs in the HIP kernels; there is no fallback path, and
 a missing library raises.
 
-The scale layout check mirrors the NemotronMamba2Layer docs
-(``set_fp8_weights``): block-scaled weights must carry the
-[ceil(N/128), ceil(K/128)] BF16 grid, since a per-row [N] or scalar scale
-would be read past its end inside the kernel. The Qwen3SsmLayer docs
-(``set_fp8_rowwise_prefill_weights``) make the same point the other way: a
-layout mix-up between formats is only caught by an explicit check.
+Scale formats (``scale_format``; by default taken from the scale tensor):
+
+* ``"block_bf16"`` - [ceil(N/128), ceil(K/128)] BF16 grid (NemotronMamba2Layer
+  docs, ``set_fp8_weights``);
+* ``"block_f32"``  - the same grid in FP32 (nemotron_mamba2.rs listing,
+  ``set_fp8_weights``, which takes an f32 scale grid);
+* ``"row_f32"``    - one FP32 scale per weight row, [N] (Qwen3SsmLayer docs,
+  ``set_fp8_rowwise_prefill_weights``).
+
+The layout check mirrors those pages: a scale tensor of the wrong shape would
+be read past its end inside the kernel, and the Qwen3SsmLayer docs note that
+a mix-up between the block and per-row formats is only caught by an explicit
+check, so the format must agree with the tensor's dtype and shape exactly.
 """
 from __future__ import annotations
 
@@ -23,7 +30,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw8a16.so")
 BLOCK = 128
 
-EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_dequant", "w8a16_strerror")
+EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_gemv_ex", "w8a16_gemm_ex", "w8a16_dequant", "w8a16_strerror")
+
+# enum w8a16_scale_format
+SCALE_BLOCK_BF16, SCALE_BLOCK_F32, SCALE_ROW_F32 = 0, 1, 2
+SCALE_FORMATS = {"block_bf16": SCALE_BLOCK_BF16, "block_f32": SCALE_BLOCK_F32, "row_f32": SCALE_ROW_F32}
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ALIAS, ERR_ARG, ERR_MEMORY = 0, -1, -2, -3, -4, -5, -6, -7
 GEMV_MAX_M = 16
@@ -54,6 +65,10 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P, P, P, P, I64, I64, I64, P]
+    for name in ("w8a16_gemv_ex", "w8a16_gemm_ex"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P, P, P, ctypes.c_int, P, I64, I64, I64, P]
     lib.w8a16_dequant.restype = ctypes.c_int
     lib.w8a16_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.w8a16_strerror.restype = ctypes.c_char_p
@@ -76,6 +91,16 @@ def gemm_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: int, stre
     return load().w8a16_gemm(A, Wq, scale, out, M, N, K, stream)
 
 
+def gemv_ex_raw(A: int, Wq: int, scale: int, scale_format: int, out: int, M: int, N: int, K: int,
+                stream: int = 0) -> int:
+    return load().w8a16_gemv_ex(A, Wq, scale, scale_format, out, M, N, K, stream)
+
+
+def gemm_ex_raw(A: int, Wq: int, scale: int, scale_format: int, out: int, M: int, N: int, K: int,
+                stream: int = 0) -> int:
+    return load().w8a16_gemm_ex(A, Wq, scale, scale_format, out, M, N, K, stream)
+
+
 def dequant_raw(Wq: int, scale: int, out: int, N: int, K: int, stream: int = 0) -> int:
     return load().w8a16_dequant(Wq, scale, out, N, K, stream)
 
@@ -91,13 +116,19 @@ def _need(cond: bool, msg: str):
         raise ValueError(msg)
 
 
-def _check_weights(Wq: torch.Tensor, scale: torch.Tensor) -> tuple[int, int]:
+def _check_codes(Wq: torch.Tensor) -> tuple[int, int]:
     _need(Wq.dtype in (torch.uint8, torch.float8_e4m3fn),
           f"Wq must hold E4M3 bytes (torch.uint8 or torch.float8_e4m3fn), got {Wq.dtype}")
     _need(Wq.dim() == 2, f"Wq must be [N, K], got shape {tuple(Wq.shape)}")
     N, K = Wq.shape
     _need(K >= 16 and K % 16 == 0, f"K must be a multiple of 16 and >= 16, got {K}")
     _need(Wq.is_contiguous(), "Wq must be contiguous (row-major [N, K])")
+    return N, K
+
+
+def _check_weights(Wq: torch.Tensor, scale: torch.Tensor) -> tuple[int, int]:
+    """E4M3 codes with the BF16 block grid (the dequant path's only format)."""
+    N, K = _check_codes(Wq)
     _need(scale.dtype == torch.bfloat16,
           f"scale must be the BF16 block-scale grid, got dtype {scale.dtype}")
     _need(tuple(scale.shape) == scale_grid(N, K),
@@ -105,6 +136,29 @@ def _check_weights(Wq: torch.Tensor, scale: torch.Tensor) -> tuple[int, int]:
           f"got shape {list(scale.shape)} (per-row or scalar scales are a different format)")
     _need(scale.is_contiguous(), "scale must be contiguous (row-major by n-block)")
     return N, K
+
+
+def scale_format_of(scale: torch.Tensor) -> str:
+    """The format a scale tensor's dtype and rank stand for."""
+    if scale.dtype == torch.bfloat16:
+        return "block_bf16"
+    if scale.dtype == torch.float32:
+        return "row_f32" if scale.dim() == 1 else "block_f32"
+    raise ValueError(f"scale must be bfloat16 (block grid) or float32 (block grid or per-row), got {scale.dtype}")
+
+
+def _check_scaled_weights(Wq: torch.Tensor, scale: torch.Tensor, scale_format: str | None) -> tuple[int, int, int]:
+    """(N, K, format code) for E4M3 codes and a scale tensor of any format."""
+    N, K = _check_codes(Wq)
+    fmt = scale_format_of(scale) if scale_format is None else scale_format
+    _need(fmt in SCALE_FORMATS, f"unknown scale_format {fmt!r} (one of {sorted(SCALE_FORMATS)})")
+    want_dtype = torch.bfloat16 if fmt == "block_bf16" else torch.float32
+    want_shape = (N,) if fmt == "row_f32" else scale_grid(N, K)
+    _need(scale.dtype == want_dtype and tuple(scale.shape) == want_shape,
+          f"{fmt} scales must be a {want_dtype} tensor of shape {list(want_shape)}, "
+          f"got {scale.dtype} {list(scale.shape)}")
+    _need(scale.is_contiguous(), "scale must be contiguous")
+    return N, K, SCALE_FORMATS[fmt]
 
 
 def _check_device(*tensors: torch.Tensor):
@@ -120,10 +174,10 @@ def _stream_handle(device: torch.device, stream) -> int:
     return int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
 
 
-def _product(fn_name: str, A, Wq, scale, out, stream, max_m=None):
+def _product(fn_name: str, A, Wq, scale, out, stream, max_m=None, scale_format=None):
     _need(A.dtype == torch.bfloat16, f"A must be bfloat16, got {A.dtype}")
     _need(A.dim() == 2, f"A must be [M, K], got shape {tuple(A.shape)}")
-    N, K = _check_weights(Wq, scale)
+    N, K, fmt = _check_scaled_weights(Wq, scale, scale_format)
     M = A.shape[0]
     _need(A.shape[1] == K, f"A is {list(A.shape)} but Wq is {list(Wq.shape)}")
     _need(A.is_contiguous(), "A must be contiguous (row-major [M, K])")
@@ -137,23 +191,34 @@ def _product(fn_name: str, A, Wq, scale, out, stream, max_m=None):
               f"out must be a contiguous bfloat16 [{M}, {N}] tensor")
         _check_device(A, Wq, scale, out)
     with torch.cuda.device(A.device):
-        st = getattr(load(), fn_name)(A.data_ptr(), Wq.data_ptr(), scale.data_ptr(), out.data_ptr(),
-                                      M, N, K, _stream_handle(A.device, stream))
+        handle = _stream_handle(A.device, stream)
+        if fmt == SCALE_BLOCK_BF16:
+            st = getattr(load(), fn_name)(A.data_ptr(), Wq.data_ptr(), scale.data_ptr(), out.data_ptr(),
+                                          M, N, K, handle)
+        else:
+            fn_name += "_ex"
+            st = getattr(load(), fn_name)(A.data_ptr(), Wq.data_ptr(), scale.data_ptr(), fmt, out.data_ptr(),
+                                          M, N, K, handle)
     if st != OK:
         raise W8A16Error(fn_name, st)
     return out
 
 
 def w8a16_gemv(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
-               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Decode GEMV, M = 1..16: out[M, N] = A[M, K] x dequant(Wq[N, K], scale)^T (BF16)."""
-    return _product("w8a16_gemv", A, Wq, scale, out, stream, max_m=GEMV_MAX_M)
+               out: torch.Tensor | None = None, stream=None, scale_format: str | None = None) -> torch.Tensor:
+    """Decode GEMV, M = 1..16: out[M, N] = A[M, K] x dequant(Wq[N, K], scale)^T (BF16).
+
+    ``scale`` is a BF16 or FP32 block grid or an FP32 per-row vector; see the
+    module docstring for ``scale_format``."""
+    return _product("w8a16_gemv", A, Wq, scale, out, stream, max_m=GEMV_MAX_M, scale_format=scale_format)
 
 
 def w8a16_gemm(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
-               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Prefill GEMM, any M: out[M, N] = A[M, K] x dequant(Wq[N, K], scale)^T (BF16)."""
-    return _product("w8a16_gemm", A, Wq, scale, out, stream)
+               out: torch.Tensor | None = None, stream=None, scale_format: str | None = None) -> torch.Tensor:
+    """Prefill GEMM, any M: out[M, N] = A[M, K] x dequant(Wq[N, K], scale)^T (BF16).
+
+    ``scale`` as for :func:`w8a16_gemv`."""
+    return _product("w8a16_gemm", A, Wq, scale, out, stream, scale_format=scale_format)
 
 
 def w8a16_dequant(Wq: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None,

@@ -77,6 +77,32 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// Scale formats (enum w8a16_scale_format): the kernels take one as a template
+// parameter.
+constexpr int kScaleBlockBf16 = 0, kScaleBlockF32 = 1, kScaleRowF32 = 2;
+
+// Scale of k-block `idx` of the block grid (index (n/128) * ceil(K/128) +
+// k/128) in format SF; 1 for the per-row format, whose scale multiplies the
+// finished row sum instead (row_scale).
+template <int SF>
+__device__ __forceinline__ float block_scale(const void* S, int64_t idx) {
+    if constexpr (SF == kScaleBlockBf16)
+        return bf16_bits_to_f32(static_cast<const uint16_t*>(S)[idx]);
+    else if constexpr (SF == kScaleBlockF32)
+        return static_cast<const float*>(S)[idx];
+    else
+        return 1.0f;
+}
+
+// Scale of weight row n in format SF: the FP32 [N] entry, 1 for the block formats.
+template <int SF>
+__device__ __forceinline__ float row_scale(const void* S, int64_t n) {
+    if constexpr (SF == kScaleRowF32)
+        return static_cast<const float*>(S)[n];
+    else
+        return 1.0f;
+}
+
 // 16-byte global load that bypasses cache retention (weights are streamed once).
 __device__ __forceinline__ u32x4_t load_stream16(const uint8_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));

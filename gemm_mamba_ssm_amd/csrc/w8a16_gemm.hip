@@ -192,11 +192,11 @@ __device__ __forceinline__ void wait_steps(int younger) {
         wait_vmem<0>();
 }
 
-// The GEMM for tile shape C; each shape has its own kernel below (with its
-// own occupancy bound).
-template <class C>
+// The GEMM for tile shape C and scale format SF; each pair has its own
+// kernel below (with its own occupancy bound).
+template <class C, int SF>
 __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
-                                          const uint16_t* __restrict__ S, uint16_t* __restrict__ out,
+                                          const void* __restrict__ S, uint16_t* __restrict__ out,
                                           float* __restrict__ partials, int M, int N, int K, const Schedule& sc) {
     constexpr int TM = C::TM, BI = C::BI, BJ = C::BJ, kStages = C::kStages;
     constexpr int kAChunksPerThread = C::kAChunksPerThread, kWChunksPerThread = C::kWChunksPerThread;
@@ -257,6 +257,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
 
     // 32x32 MFMA result layout: lane l holds column l % 32; value v is row
     // 8*(v/4) + 4*(l/32) + v%4 of the block.
+    // A per-row scale multiplies the finished sum (1 for the block formats).
     auto store_tile = [&](const f32x16_t (&r)[BI][BJ], int m0, int n0) {
         const int l = opaque(lane), li = l & 31, lg = l >> 5;
 #pragma unroll
@@ -264,11 +265,13 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
 #pragma unroll
             for (int bj = 0; bj < BJ; ++bj) {
                 const int n = n0 + wn * kWaveCols + bj * 32 + li;
+                float rs = 1.0f;
+                if constexpr (SF == kScaleRowF32) rs = n < N ? row_scale<SF>(S, n) : 0.0f;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = m0 + wm * kWaveRows + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
                     if (m < M && n < N)
-                        out[static_cast<int64_t>(m) * N + n] = f32_to_bf16_bits(r[bi][bj][v]);
+                        out[static_cast<int64_t>(m) * N + n] = f32_to_bf16_bits(r[bi][bj][v] * rs);
                 }
             }
     };
@@ -384,9 +387,9 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
         // The tile's scale row, 64 k-blocks at a time: lane l holds block
         // s_base + l, so the main loop issues no vector memory operation
         // besides the DMA (one reload per 64 k-blocks).
-        const uint16_t* s_row = S + static_cast<int64_t>(tn) * k_blocks;
+        const int64_t s_row = static_cast<int64_t>(tn) * k_blocks;
         auto load_scales = [&](int base) {
-            return (base + lane < k_blocks) ? bf16_bits_to_f32(s_row[base + lane]) : 0.0f;
+            return (base + lane < k_blocks) ? block_scale<SF>(S, s_row + base + lane) : 0.0f;
         };
         int s_base = kb0 & ~63;
         float s_lane = load_scales(s_base);
@@ -473,21 +476,29 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
     }
 }
 
-#define W8A16_GEMM_KERNEL(NAME, C)                                                                   \
+// One kernel per (tile shape, scale format); suffixes: s1 = FP32 block
+// scales, r = FP32 row scales.
+#define W8A16_GEMM_KERNEL(NAME, C, SF)                                                               \
     __global__ void __launch_bounds__(kThreads, C::kWgPerCu)                                         \
-    NAME(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const uint16_t* __restrict__ S, \
+    NAME(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,   \
          uint16_t* __restrict__ out, float* __restrict__ partials, int M, int N, int K, Schedule sc) {  \
-        gemm_body<C>(A, W, S, out, partials, M, N, K, sc);                                           \
-    }
-W8A16_GEMM_KERNEL(gemm_kernel_128, BigTile)
-W8A16_GEMM_KERNEL(gemm_kernel_64, Skinny64)
-W8A16_GEMM_KERNEL(gemm_kernel_32, Skinny32)
+        gemm_body<C, SF>(A, W, S, out, partials, M, N, K, sc);                                       \
+    }                                                                                                \
+    template <>                                                                                      \
+    struct GemmKernel<C, SF> {                                                                       \
+        static constexpr auto fn = &NAME;                                                            \
+    };
+template <class C, int SF> struct GemmKernel;
+W8A16_GEMM_KERNEL(gemm_kernel_128, BigTile, kScaleBlockBf16)
+W8A16_GEMM_KERNEL(gemm_kernel_64, Skinny64, kScaleBlockBf16)
+W8A16_GEMM_KERNEL(gemm_kernel_32, Skinny32, kScaleBlockBf16)
+W8A16_GEMM_KERNEL(gemm_kernel_128_s1, BigTile, kScaleBlockF32)
+W8A16_GEMM_KERNEL(gemm_kernel_64_s1, Skinny64, kScaleBlockF32)
+W8A16_GEMM_KERNEL(gemm_kernel_32_s1, Skinny32, kScaleBlockF32)
+W8A16_GEMM_KERNEL(gemm_kernel_128_r, BigTile, kScaleRowF32)
+W8A16_GEMM_KERNEL(gemm_kernel_64_r, Skinny64, kScaleRowF32)
+W8A16_GEMM_KERNEL(gemm_kernel_32_r, Skinny32, kScaleRowF32)
 #undef W8A16_GEMM_KERNEL
-
-template <class C> struct GemmKernel;
-template <> struct GemmKernel<BigTile> { static constexpr auto fn = &gemm_kernel_128; };
-template <> struct GemmKernel<Skinny64> { static constexpr auto fn = &gemm_kernel_64; };
-template <> struct GemmKernel<Skinny32> { static constexpr auto fn = &gemm_kernel_32; };
 
 // Combine of the split tiles. The host lists, for every split tile, the
 // workgroup that computed its first k-blocks (the tile is the last of that
@@ -504,10 +515,10 @@ struct SplitList {
     uint16_t first[kMaxSplits];
 };
 
-template <class C>
+template <class C, int SF>
 __global__ void __launch_bounds__(kThreads)
-combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, int M, int N,
-               Schedule sc, SplitList list) {
+combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, const void* __restrict__ S,
+               int M, int N, Schedule sc, SplitList list) {
     constexpr int TM = C::TM, kTileFloats = C::kTileFloats;
     const int w = list.first[blockIdx.x];
     const int k_blocks = sc.k_blocks;
@@ -545,6 +556,9 @@ combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, i
             }
         }
     }
+    float rs[4];                                       // per-row scales of the 4 columns (1 for block formats)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rs[e] = n0 + col + e < N ? row_scale<SF>(S, n0 + col + e) : 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int m = m0 + row0 + r * 8;
@@ -552,7 +566,7 @@ combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, i
         uint16_t* dst = out + static_cast<int64_t>(m) * N + n0 + col;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (n0 + col + e < N) dst[e] = f32_to_bf16_bits(sum[r][e]);
+            if (n0 + col + e < N) dst[e] = f32_to_bf16_bits(sum[r][e] * rs[e]);
     }
 }
 
@@ -633,8 +647,8 @@ int workspace_for(hipStream_t stream, size_t bytes, Workspace* ws) {
 }
 
 // Plan and launch the GEMM (and, if tiles are split, the combine) with tile
-// shape C.
-template <class C>
+// shape C and scale format SF.
+template <class C, int SF>
 int run_gemm(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
              hipStream_t s) {
     // Buffer offsets are 32-bit: one tile's rows of A must span less than 2 GiB.
@@ -651,33 +665,46 @@ int run_gemm(const void* A, const void* Wq, const void* scale, void* out, int64_
         const int st = workspace_for(s, static_cast<size_t>(2) * slots * C::kTileFloats * sizeof(float), &ws);
         if (st != W8A16_OK) return st;
     }
-    int st = launch(GemmKernel<C>::fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), s,
-                    static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq),
-                    static_cast<const uint16_t*>(scale), static_cast<uint16_t*>(out), ws.partials,
+    int st = launch(GemmKernel<C, SF>::fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), s,
+                    static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
+                    static_cast<uint16_t*>(out), ws.partials,
                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), sc);
     if (st != W8A16_OK || sc.shared_groups == 0) return st;
     SplitList list;
     const int splits = list_splits(sc, &list);
     if (splits == 0) return W8A16_OK;
-    return launch(&combine_kernel<C>, dim3(static_cast<unsigned>(splits), C::TM / kCombineRows), dim3(kThreads), s,
-                  static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), static_cast<int>(M),
-                  static_cast<int>(N), sc, list);
+    return launch(&combine_kernel<C, SF>, dim3(static_cast<unsigned>(splits), C::TM / kCombineRows), dim3(kThreads),
+                  s, static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), scale,
+                  static_cast<int>(M), static_cast<int>(N), sc, list);
+}
+
+template <int SF>
+int gemm_by_shape(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
+                  hipStream_t s) {
+    if (skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, SF, out, M, N, K, s);
+    if (M <= Skinny32::TM) return run_gemm<Skinny32, SF>(A, Wq, scale, out, M, N, K, s);
+    if (M <= Skinny64::TM) return run_gemm<Skinny64, SF>(A, Wq, scale, out, M, N, K, s);
+    return run_gemm<BigTile, SF>(A, Wq, scale, out, M, N, K, s);
 }
 
 }  // namespace
 }  // namespace w8a16
 
-extern "C" int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
-                          int64_t M, int64_t N, int64_t K, void* stream) {
+extern "C" int w8a16_gemm_ex(const void* A, const void* Wq, const void* scale, int scale_format, void* out,
+                             int64_t M, int64_t N, int64_t K, void* stream) {
     using namespace w8a16;
     bool noop = false;
-    const int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
+    const int st = check_product_args(A, Wq, scale, out, M, N, K, &noop, scale_format);
     if (st != W8A16_OK || noop) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-#ifndef W8A16_TILED_SKINNY32
-    if (skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, out, M, N, K, s);
-#endif
-    if (M <= Skinny32::TM) return run_gemm<Skinny32>(A, Wq, scale, out, M, N, K, s);
-    if (M <= Skinny64::TM) return run_gemm<Skinny64>(A, Wq, scale, out, M, N, K, s);
-    return run_gemm<BigTile>(A, Wq, scale, out, M, N, K, s);
+    switch (scale_format) {
+        case W8A16_SCALE_BLOCK_F32: return gemm_by_shape<kScaleBlockF32>(A, Wq, scale, out, M, N, K, s);
+        case W8A16_SCALE_ROW_F32: return gemm_by_shape<kScaleRowF32>(A, Wq, scale, out, M, N, K, s);
+        default: return gemm_by_shape<kScaleBlockBf16>(A, Wq, scale, out, M, N, K, s);
+    }
+}
+
+extern "C" int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
+                          int64_t M, int64_t N, int64_t K, void* stream) {
+    return w8a16_gemm_ex(A, Wq, scale, W8A16_SCALE_BLOCK_BF16, out, M, N, K, stream);
 }

@@ -66,7 +66,7 @@ __device__ __forceinline__ void butterfly(float (&v)[P], int lane) {
     }
 }
 
-template <int MR, int J, int RB>
+template <int MR, int J, int RB, int SF>
 struct Gemv {
     static constexpr int V = RB * MR;          // partial sums per lane per group
     static constexpr int P = pow2_ceil(V);     // padded to a power of two for the butterfly
@@ -80,7 +80,7 @@ struct Gemv {
     };
 
     __device__ static __forceinline__ void load(Regs& r, const uint8_t* __restrict__ W,
-                                                const uint16_t* __restrict__ S, int g, int N, int K,
+                                                const void* __restrict__ S, int g, int N, int K,
                                                 int k_blocks, const int (&kch)[J], const bool (&kvalid)[J]) {
         const int n0 = g * RB;
 #pragma unroll
@@ -95,13 +95,13 @@ struct Gemv {
         // All RB rows sit in scale row-block n0/128.
 #pragma unroll
         for (int j = 0; j < J; ++j)
-            r.s[j] = kvalid[j] ? bf16_bits_to_f32(S[scale_index(n0, kch[j], k_blocks)]) : 0.0f;
+            r.s[j] = kvalid[j] ? block_scale<SF>(S, scale_index(n0, kch[j], k_blocks)) : 0.0f;
     }
 
     __device__ static __forceinline__ void process(const Regs& r, const uint32_t (&a)[MR][J][8],
                                                    float (*red)[kMaxWaves][V], int parity,
-                                                   uint16_t* __restrict__ out, int g, int N,
-                                                   int lane, int wave, int nwaves) {
+                                                   uint16_t* __restrict__ out, const void* __restrict__ S,
+                                                   int g, int N, int lane, int wave, int nwaves) {
         float v[P];
 #pragma unroll
         for (int i = 0; i < P; ++i) v[i] = 0.0f;
@@ -129,7 +129,8 @@ struct Gemv {
         if (nwaves == 1) {
             if (holder) {
                 const int i = idx / MR, m = idx % MR;
-                if (n0 + i < N) out[static_cast<int64_t>(m) * N + n0 + i] = f32_to_bf16_bits(v[0]);
+                if (n0 + i < N)
+                    out[static_cast<int64_t>(m) * N + n0 + i] = f32_to_bf16_bits(v[0] * row_scale<SF>(S, n0 + i));
             }
         } else {
             if (holder) red[parity][wave][idx] = v[0];
@@ -138,7 +139,8 @@ struct Gemv {
                 float tot = 0.0f;
                 for (int w = 0; w < nwaves; ++w) tot += red[parity][w][lane];
                 const int i = lane / MR, m = lane % MR;
-                if (n0 + i < N) out[static_cast<int64_t>(m) * N + n0 + i] = f32_to_bf16_bits(tot);
+                if (n0 + i < N)
+                    out[static_cast<int64_t>(m) * N + n0 + i] = f32_to_bf16_bits(tot * row_scale<SF>(S, n0 + i));
             }
             // The next group writes red[parity ^ 1]; red[parity] is written
             // again only after the next barrier, which wave 0 reaches after
@@ -147,12 +149,12 @@ struct Gemv {
     }
 };
 
-template <int MR, int J, int RB>
+template <int MR, int J, int RB, int SF>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
-            const uint16_t* __restrict__ S, uint16_t* __restrict__ out,
+            const void* __restrict__ S, uint16_t* __restrict__ out,
             int N, int K, int groups_per_block) {
-    using G = Gemv<MR, J, RB>;
+    using G = Gemv<MR, J, RB, SF>;
     __shared__ float red[2][kMaxWaves][G::V];
 
     const int lane = threadIdx.x & 63;
@@ -198,16 +200,16 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     int parity = 0;
     for (int g = g_begin; g < g_end; g += 2) {
         if (g + 1 < g_end) G::load(rb, W, S, g + 1, N, K, k_blocks, kch, kvalid);
-        G::process(ra, a, red, parity, out, g, N, lane, wave, nwaves);
+        G::process(ra, a, red, parity, out, S, g, N, lane, wave, nwaves);
         parity ^= 1;
         if (g + 1 >= g_end) break;
         if (g + 2 < g_end) G::load(ra, W, S, g + 2, N, K, k_blocks, kch, kvalid);
-        G::process(rb, a, red, parity, out, g + 1, N, lane, wave, nwaves);
+        G::process(rb, a, red, parity, out, S, g + 1, N, lane, wave, nwaves);
         parity ^= 1;
     }
 }
 
-typedef void (*gemv_fn)(const uint16_t*, const uint8_t*, const uint16_t*, uint16_t*, int, int, int);
+typedef void (*gemv_fn)(const uint16_t*, const uint8_t*, const void*, uint16_t*, int, int, int);
 
 // Chunks per lane: 1 while K <= 8192 (8 waves of 1024), 2 up to 16384 (M <= 8).
 constexpr int max_chunks(int mr) { return mr <= 8 ? 2 : 1; }
@@ -221,16 +223,16 @@ constexpr int rows_per_group(int mr, int j) {
     return rb;
 }
 
-template <int MR, int J>
+template <int MR, int J, int SF>
 gemv_fn pick_j() {
-    return &gemv_kernel<MR, J, rows_per_group(MR, J)>;
+    return &gemv_kernel<MR, J, rows_per_group(MR, J), SF>;
 }
 
-template <int MR>
+template <int MR, int SF>
 gemv_fn pick(int j) {
     if constexpr (max_chunks(MR) >= 2)
-        if (j == 2) return pick_j<MR, 2>();
-    return pick_j<MR, 1>();
+        if (j == 2) return pick_j<MR, 2, SF>();
+    return pick_j<MR, 1, SF>();
 }
 
 struct Choice {
@@ -238,56 +240,42 @@ struct Choice {
     int rows_per_group;
 };
 
-template <int MR>
+template <int MR, int SF>
 Choice choose(int j) {
-    return {pick<MR>(j), j == 2 ? rows_per_group(MR, 2) : rows_per_group(MR, 1)};
+    return {pick<MR, SF>(j), j == 2 ? rows_per_group(MR, 2) : rows_per_group(MR, 1)};
 }
 
+template <int SF>
 Choice select_kernel(int mr, int j) {
     switch (mr) {
-        case 1: return choose<1>(j);
-        case 2: return choose<2>(j);
-        case 3: return choose<3>(j);
-        case 4: return choose<4>(j);
-        case 5: return choose<5>(j);
-        case 6: return choose<6>(j);
-        case 7: return choose<7>(j);
-        case 8: return choose<8>(j);
-        case 9: return choose<9>(j);
-        case 10: return choose<10>(j);
-        case 11: return choose<11>(j);
-        case 12: return choose<12>(j);
-        case 13: return choose<13>(j);
-        case 14: return choose<14>(j);
-        case 15: return choose<15>(j);
-        default: return choose<16>(j);
+        case 1: return choose<1, SF>(j);
+        case 2: return choose<2, SF>(j);
+        case 3: return choose<3, SF>(j);
+        case 4: return choose<4, SF>(j);
+        case 5: return choose<5, SF>(j);
+        case 6: return choose<6, SF>(j);
+        case 7: return choose<7, SF>(j);
+        case 8: return choose<8, SF>(j);
+        case 9: return choose<9, SF>(j);
+        case 10: return choose<10, SF>(j);
+        case 11: return choose<11, SF>(j);
+        case 12: return choose<12, SF>(j);
+        case 13: return choose<13, SF>(j);
+        case 14: return choose<14, SF>(j);
+        case 15: return choose<15, SF>(j);
+        default: return choose<16, SF>(j);
     }
 }
 
-}  // namespace
-}  // namespace w8a16
-
-extern "C" int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
-                          int64_t M, int64_t N, int64_t K, void* stream) {
-    using namespace w8a16;
-    bool noop = false;
-    int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
-    if (st != W8A16_OK || noop) return st;
-    if (M > W8A16_GEMV_MAX_M || K > (M <= 8 ? W8A16_GEMV_MAX_K_SMALL_M : W8A16_GEMV_MAX_K))
-        return W8A16_ERR_SHAPE;
-    // From 4 rows on, the products cost this kernel more VALU time than the
-    // weight stream takes; the skinny GEMM (same single weight pass, products
-    // on the matrix cores) is faster where it applies (measured on the
-    // Mamba-2 in_proj shape: 21 against 23 us at M = 4, 22 against 49 us at
-    // M = 16).
-    if (M >= 4 && skinny_fits(M, K))
-        return skinny_gemm(A, Wq, scale, out, M, N, K, static_cast<hipStream_t>(stream));
-
+// The launch of the GEMV for scale format SF (arguments checked).
+template <int SF>
+int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
+             hipStream_t stream) {
     const int mr = static_cast<int>(M);
     const int j = K > static_cast<int64_t>(kWaveK) * kMaxWaves ? 2 : 1;
     const int nwaves = static_cast<int>(ceil_div(K, static_cast<int64_t>(kWaveK) * j));
     if (nwaves > kMaxWaves || j > max_chunks(mr)) return W8A16_ERR_SHAPE;
-    Choice c = select_kernel(mr, j);
+    Choice c = select_kernel<SF>(mr, j);
     const int64_t cus = device_cu_count();
     int64_t per_block;
     if (mr == 1 && j == 1) {
@@ -296,7 +284,7 @@ extern "C" int w8a16_gemv(const void* A, const void* Wq, const void* scale, void
         // 8-row groups; one group per workgroup up to about 18 workgroups per
         // CU, then several.
         const int rb = ceil_div(N, 4) >= 8 * cus ? 4 : 8;
-        c = {rb == 4 ? &gemv_kernel<1, 1, 4> : &gemv_kernel<1, 1, 8>, rb};
+        c = {rb == 4 ? &gemv_kernel<1, 1, 4, SF> : &gemv_kernel<1, 1, 8, SF>, rb};
         per_block = std::max<int64_t>(1, ceil_div(N, rb) / (18 * cus));
     } else {
         const int64_t resident = cus * (kWavesPerCu / nwaves > 0 ? kWavesPerCu / nwaves : 1);
@@ -305,9 +293,38 @@ extern "C" int w8a16_gemv(const void* A, const void* Wq, const void* scale, void
     const int64_t groups = ceil_div(N, c.rows_per_group);
     const int64_t blocks = ceil_div(groups, per_block);
 
-    return launch(c.fn, dim3(static_cast<unsigned>(blocks)), dim3(64 * nwaves),
-                  static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(A),
-                  static_cast<const uint8_t*>(Wq), static_cast<const uint16_t*>(scale),
+    return launch(c.fn, dim3(static_cast<unsigned>(blocks)), dim3(64 * nwaves), stream,
+                  static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
                   static_cast<uint16_t*>(out), static_cast<int>(N), static_cast<int>(K),
                   static_cast<int>(per_block));
+}
+
+}  // namespace
+}  // namespace w8a16
+
+extern "C" int w8a16_gemv_ex(const void* A, const void* Wq, const void* scale, int scale_format, void* out,
+                             int64_t M, int64_t N, int64_t K, void* stream) {
+    using namespace w8a16;
+    bool noop = false;
+    const int st = check_product_args(A, Wq, scale, out, M, N, K, &noop, scale_format);
+    if (st != W8A16_OK || noop) return st;
+    if (M > W8A16_GEMV_MAX_M || K > (M <= 8 ? W8A16_GEMV_MAX_K_SMALL_M : W8A16_GEMV_MAX_K))
+        return W8A16_ERR_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // From 4 rows on, the products cost this kernel more VALU time than the
+    // weight stream takes; the skinny GEMM (same single weight pass, products
+    // on the matrix cores) is faster where it applies (measured on the
+    // Mamba-2 in_proj shape: 21 against 23 us at M = 4, 22 against 49 us at
+    // M = 16).
+    if (M >= 4 && skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, scale_format, out, M, N, K, s);
+    switch (scale_format) {
+        case W8A16_SCALE_BLOCK_F32: return run_gemv<kScaleBlockF32>(A, Wq, scale, out, M, N, K, s);
+        case W8A16_SCALE_ROW_F32: return run_gemv<kScaleRowF32>(A, Wq, scale, out, M, N, K, s);
+        default: return run_gemv<kScaleBlockBf16>(A, Wq, scale, out, M, N, K, s);
+    }
+}
+
+extern "C" int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
+                          int64_t M, int64_t N, int64_t K, void* stream) {
+    return w8a16_gemv_ex(A, Wq, scale, W8A16_SCALE_BLOCK_BF16, out, M, N, K, stream);
 }

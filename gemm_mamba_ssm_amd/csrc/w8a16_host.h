@@ -24,11 +24,22 @@ inline bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbyte
            b0 < a0 + static_cast<uintptr_t>(abytes);
 }
 
-// Checks shared by w8a16_gemv and w8a16_gemm. Returns W8A16_OK or an error;
-// *noop is set when there is nothing to compute (M == 0 or N == 0).
+inline bool scale_format_valid(int f) {
+    return f == W8A16_SCALE_BLOCK_BF16 || f == W8A16_SCALE_BLOCK_F32 || f == W8A16_SCALE_ROW_F32;
+}
+
+// Bytes of the scale buffer in format f.
+inline int64_t scale_bytes(int f, int64_t N, int64_t K) {
+    if (f == W8A16_SCALE_ROW_F32) return N * 4;
+    return ceil_div(N, kScaleBlockHost) * ceil_div(K, kScaleBlockHost) * (f == W8A16_SCALE_BLOCK_F32 ? 4 : 2);
+}
+
+// Checks shared by the GEMV and GEMM entry points. Returns W8A16_OK or an
+// error; *noop is set when there is nothing to compute (M == 0 or N == 0).
 inline int check_product_args(const void* A, const void* Wq, const void* scale, const void* out,
-                              int64_t M, int64_t N, int64_t K, bool* noop) {
+                              int64_t M, int64_t N, int64_t K, bool* noop, int fmt = W8A16_SCALE_BLOCK_BF16) {
     *noop = false;
+    if (!scale_format_valid(fmt)) return W8A16_ERR_ARG;
     if (M < 0 || N < 0 || K < 16 || (K % 16) != 0 || M > INT32_MAX || N > INT32_MAX ||
         K > INT32_MAX)
         return W8A16_ERR_SHAPE;
@@ -37,10 +48,11 @@ inline int check_product_args(const void* A, const void* Wq, const void* scale, 
         return W8A16_OK;
     }
     if (!A || !Wq || !scale || !out) return W8A16_ERR_NULL;
-    if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, 2) || !aligned(out, 2))
+    if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, fmt == W8A16_SCALE_BLOCK_BF16 ? 2 : 4) ||
+        !aligned(out, 2))
         return W8A16_ERR_ALIGN;
     const int64_t out_bytes = M * N * 2;
-    const int64_t scale_bytes = ceil_div(N, kScaleBlockHost) * ceil_div(K, kScaleBlockHost) * 2;
+    const int64_t scale_bytes = w8a16::scale_bytes(fmt, N, K);
     if (overlaps(out, out_bytes, A, M * K * 2) || overlaps(out, out_bytes, Wq, N * K) ||
         overlaps(out, out_bytes, scale, scale_bytes))
         return W8A16_ERR_ALIAS;
@@ -53,8 +65,8 @@ inline int check_product_args(const void* A, const void* Wq, const void* scale, 
 constexpr int64_t kSkinnyMaxM = 16;
 constexpr int64_t kSkinnyMaxK = 4096;
 inline bool skinny_fits(int64_t M, int64_t K) { return M >= 1 && M <= kSkinnyMaxM && K <= kSkinnyMaxK; }
-int skinny_gemm(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
-                hipStream_t stream);
+int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, void* out, int64_t M, int64_t N,
+                int64_t K, hipStream_t stream);
 
 // Launch `kernel` with exactly the argument types of its signature; the HIP
 // launch status becomes W8A16_OK / W8A16_ERR_LAUNCH.

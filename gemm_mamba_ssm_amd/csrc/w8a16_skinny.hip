@@ -22,7 +22,10 @@
 //    steps of a chunk, and the block scale is applied exactly in fp32
 //    (acc += scale * blk);
 //  * the S partial 16 x 16 tiles of a block meet in LDS and are added in wave
-//    order (ascending k): the result is deterministic.
+//    order (ascending k): the result is deterministic;
+//  * scale formats: BF16 or FP32 block grids are folded per k-block as above;
+//    an FP32 per-row scale multiplies the finished sum of its column before
+//    the BF16 rounding (the workgroup's row scales are staged in LDS).
 #include <algorithm>
 
 #include "w8a16_device.h"
@@ -54,17 +57,21 @@ __device__ __forceinline__ void wait_vmem() {
 
 // MB = 16-row blocks of A (1 for M <= 16, 2 for M <= 32); KB = k-blocks per
 // wave at most (the activations of KB k-blocks take 16 * MB * KB VGPRs); D =
-// weight blocks in flight per wave; MAXW = waves per workgroup at most.
-template <int MB, int KB, int D, int MAXW>
+// weight blocks in flight per wave; MAXW = waves per workgroup at most; SF =
+// scale format.
+template <int MB, int KB, int D, int MAXW, int SF>
 __global__ void __launch_bounds__(64 * MAXW)
-skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const uint16_t* __restrict__ S,
+skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,
               uint16_t* __restrict__ out, int M, int N, int K, int blocks_per_wg) {
+    constexpr bool kRowScale = SF == kScaleRowF32;
     // Partial tiles of the waves, double-buffered by block parity:
     // [parity][wave][mb][lane] x 4 floats.
     __shared__ f32x4_t red[2][MAXW * MB * 64];
     // The workgroup's outputs, written out after the loop (so that the loop
     // issues no vector-memory stores, which would share the loads' counter).
     __shared__ uint16_t outs[kMaxBlocksPerWg * 256 * MB];
+    // Per-row scales of the workgroup's weight rows (row format only).
+    __shared__ float row_s[kRowScale ? kMaxBlocksPerWg * kRows : 1];
 
     const int waves = blockDim.x / 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -102,21 +109,34 @@ skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, con
                         __builtin_amdgcn_raw_buffer_load_b128(ra, k < K ? ((mb * 16 + r) * K + k) * 2 : kOutOfRange, 0, 0);
                 }
 
-    // Scales of the workgroup's rows and the wave's k-blocks: lane l holds
-    // scale row srow0 + l / KB, k-block kb0 + l % KB (a workgroup's rows span
-    // at most kMaxBlocksPerWg * 16 / 128 + 2 scale rows).
+    // Block scales of the workgroup's rows and the wave's k-blocks: lane l
+    // holds scale row srow0 + l / KB, k-block kb0 + l % KB (a workgroup's rows
+    // span at most kMaxBlocksPerWg * 16 / 128 + 2 scale rows). With per-row
+    // scales, the workgroup's rows' scales go to LDS instead (read after the
+    // first barrier of the loop).
+    constexpr int kScaleBytes = SF == kScaleBlockBf16 ? 2 : 4;
+    const int scale_elems = kRowScale ? N : ((N + kScaleBlock - 1) / kScaleBlock) * k_blocks;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(S), 0, ((N + kScaleBlock - 1) / kScaleBlock) * k_blocks * 2, kBufferFlags);
+        const_cast<void*>(S), 0, scale_elems * kScaleBytes, kBufferFlags);
     constexpr int kScaleRows = 64 / KB;
     static_assert(kMaxBlocksPerWg * kRows / kScaleBlock + 2 <= kScaleRows, "one scale load per workgroup");
-    auto load_scales = [&](int srow0) {
+    const int srow0 = blk0 * kRows / kScaleBlock;
+    float s_lane = 1.0f;
+    if constexpr (SF == kScaleBlockBf16 || SF == kScaleBlockF32) {
         const int srow = srow0 + lane / KB, kb = kb0 + lane % KB;
         const bool ok = srow * kScaleBlock < N && kb < k_blocks;
-        return bf16_bits_to_f32(
-            __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? (srow * k_blocks + kb) * 2 : kOutOfRange, 0, 0));
-    };
-    const int srow0 = blk0 * kRows / kScaleBlock;
-    const float s_lane = load_scales(srow0);
+        const uint32_t off = ok ? static_cast<uint32_t>(srow * k_blocks + kb) * kScaleBytes : kOutOfRange;
+        if constexpr (SF == kScaleBlockBf16)
+            s_lane = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+        else
+            s_lane = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    } else {
+        for (int i = threadIdx.x; i < (blk1 - blk0) * kRows; i += blockDim.x) {
+            const int n = blk0 * kRows + i;
+            row_s[i] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rs, n < N ? static_cast<uint32_t>(n) * 4 : kOutOfRange, 0, 0));
+        }
+    }
 
     // Weights of row block b into a ring slot: [j][c], 16 bytes each; rows
     // past N read zeros (beyond the buffer's range). Blocks past the
@@ -184,6 +204,7 @@ skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, con
             const int l = col + 16 * (rr / 4), v = rr % 4;
             float sum = red[parity][mb * 64 + l][v];
             for (int w2 = 1; w2 < waves; ++w2) sum += red[parity][(w2 * MB + mb) * 64 + l][v];
+            if constexpr (kRowScale) sum *= row_s[((bb - blk0) * kRows + col) % (kMaxBlocksPerWg * kRows)];
             if (bb < blk1) outs[(bb - blk0) * 256 * MB + t] = f32_to_bf16_bits(sum);
         }
         // red[parity] is written again two blocks later, after the next
@@ -219,14 +240,16 @@ skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, con
 // two k-blocks of activations, at least 4. The grid aims at about 16 resident
 // waves per CU, each workgroup taking a contiguous range of 16-row weight
 // blocks.
-int skinny_gemm(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
-                hipStream_t stream) {
+int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, void* out, int64_t M, int64_t N,
+                int64_t K, hipStream_t stream) {
     if (M < 1 || M > kSkinnyMaxM) return W8A16_ERR_SHAPE;
     if (!skinny_fits(M, K)) return W8A16_ERR_SHAPE;
     const int kb_max = 2;
     const int64_t k_blocks = ceil_div(K, kScaleBlockHost);
-    // Buffer offsets are 32-bit.
-    if (static_cast<int64_t>(kRows) * K >= static_cast<int64_t>(kOutOfRange)) return W8A16_ERR_SHAPE;
+    // Buffer offsets and sizes are 32-bit.
+    if (static_cast<int64_t>(kRows) * K >= static_cast<int64_t>(kOutOfRange) ||
+        scale_bytes(fmt, N, K) >= static_cast<int64_t>(kOutOfRange))
+        return W8A16_ERR_SHAPE;
     int waves = static_cast<int>(ceil_div(k_blocks, kb_max));
     waves = std::max(waves, 4);
     const int64_t nblk = ceil_div(N, kRows);
@@ -237,9 +260,17 @@ int skinny_gemm(const void* A, const void* Wq, const void* scale, void* out, int
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K), p = static_cast<int>(per_wg);
     auto a = static_cast<const uint16_t*>(A);
     auto w = static_cast<const uint8_t*>(Wq);
-    auto s = static_cast<const uint16_t*>(scale);
     auto o = static_cast<uint16_t*>(out);
-    return launch(&skinny_kernel<1, 2, 2, 16>, grid, block, stream, a, w, s, o, m, n, k, p);
+    switch (fmt) {
+        case W8A16_SCALE_BLOCK_BF16:
+            return launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockBf16>, grid, block, stream, a, w, scale, o, m, n, k, p);
+        case W8A16_SCALE_BLOCK_F32:
+            return launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockF32>, grid, block, stream, a, w, scale, o, m, n, k, p);
+        case W8A16_SCALE_ROW_F32:
+            return launch(&skinny_kernel<1, 2, 2, 16, kScaleRowF32>, grid, block, stream, a, w, scale, o, m, n, k, p);
+        default:
+            return W8A16_ERR_ARG;
+    }
 }
 
 }  // namespace w8a16

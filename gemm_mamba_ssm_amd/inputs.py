@@ -22,6 +22,11 @@ hand-written round-to-nearest-even encoder.
 
 All arrays returned are raw bit patterns: A and scales as ``uint16`` BF16 bits,
 weights as ``uint8`` E4M3 codes.
+
+The FP32 scale formats (``weights_fmt``) use the same draws; ``block_f32``
+keeps ``max|w| / 448`` of each block in float32 (no BF16 rounding), and
+``row_f32`` takes it over each whole weight row instead, as a float32 [N]
+vector.
 """
 from __future__ import annotations
 
@@ -78,6 +83,60 @@ def quantize_blocks(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
         codes[r0:r1] = (torch.from_numpy(q).to(torch.float8_e4m3fn)
                         .view(torch.uint8).numpy())
     return codes, s_bits
+
+
+def _encode_e4m3(q: np.ndarray) -> np.ndarray:
+    q = np.clip(q, -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    return torch.from_numpy(np.ascontiguousarray(q)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def quantize_blocks_f32(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Block-quantize float32 w [N, K] to (E4M3 codes, float32 scale grid)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    nb, kb = scale_grid(N, K)
+    pad = np.zeros((nb * BLOCK, kb * BLOCK), np.float32)
+    pad[:N, :K] = w
+    amax = np.abs(pad.reshape(nb, BLOCK, kb, BLOCK)).max(axis=(1, 3))
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    codes = np.empty((N, K), np.uint8)
+    for bi in range(nb):
+        r0, r1 = bi * BLOCK, min(N, (bi + 1) * BLOCK)
+        s_cols = np.repeat(s[bi], BLOCK)[:K]
+        safe = np.where(s_cols == 0, np.float32(1), s_cols)
+        q = np.where(s_cols[None, :] == 0, np.float32(0), w[r0:r1] / safe[None, :])
+        codes[r0:r1] = _encode_e4m3(q)
+    return codes, s
+
+
+def quantize_rows_f32(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Row-quantize float32 w [N, K] to (E4M3 codes, float32 [N] row scales)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    s = (np.abs(w).max(axis=1) / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1), s)
+    codes = np.empty(w.shape, np.uint8)
+    for r0 in range(0, w.shape[0], BLOCK):
+        r1 = min(w.shape[0], r0 + BLOCK)
+        q = np.where(s[r0:r1, None] == 0, np.float32(0), w[r0:r1] / safe[r0:r1, None])
+        codes[r0:r1] = _encode_e4m3(q)
+    return codes, s
+
+
+SCALE_FORMATS = ("block_bf16", "block_f32", "row_f32")
+
+
+def weights_fmt(N: int, K: int, sigma: float, seed: int, fmt: str) -> tuple[np.ndarray, np.ndarray]:
+    """(Wq [N, K] E4M3 codes, scales in format fmt) from the same draws as weights()."""
+    if fmt == "block_bf16":
+        return weights(N, K, sigma, seed)
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((N, K), dtype=np.float32)
+    w *= np.float32(sigma)
+    if fmt == "block_f32":
+        return quantize_blocks_f32(w)
+    if fmt == "row_f32":
+        return quantize_rows_f32(w)
+    raise ValueError(f"unknown scale format {fmt!r}")
 
 
 def weights(N: int, K: int, sigma: float, seed: int) -> tuple[np.ndarray, np.ndarray]:

@@ -54,6 +54,28 @@ enum w8a16_status {
     W8A16_ERR_MEMORY = -7  /* the GEMM workspace could not be allocated         */
 };
 
+/*
+ * Scale formats of the _ex entry points. The two entry points above take the
+ * first; the others are the variants the pages name besides it:
+ *  - W8A16_SCALE_BLOCK_BF16: BF16 [ceil(N/128)][ceil(K/128)] (the grid above);
+ *  - W8A16_SCALE_BLOCK_F32: FP32, same grid and index (nemotron_mamba2.rs
+ *    source listing, `set_fp8_weights`: its format check names FP32 block
+ *    scales of that shape);
+ *  - W8A16_SCALE_ROW_F32: FP32 [N], one scale per weight row:
+ *    out[m][n] = sum_k A[m][k] * E4M3(Wq[n][k]) * scale[n] (Qwen3SsmLayer
+ *    docs, `set_fp8_rowwise_prefill_weights`: per-row FP8 weights, a layout
+ *    that must not reach a block-scaled kernel, since a mismatched buffer is
+ *    read in bounds and gives wrong numbers).
+ * The library cannot tell the formats apart from the pointer: the caller
+ * passes the format that matches the buffer (the Python binding checks the
+ * tensor's dtype and shape against it).
+ */
+enum w8a16_scale_format {
+    W8A16_SCALE_BLOCK_BF16 = 0,
+    W8A16_SCALE_BLOCK_F32 = 1,
+    W8A16_SCALE_ROW_F32 = 2
+};
+
 /* Largest M the GEMV entry point accepts, and its largest K: 16384 when
  * M <= 8, 8192 otherwise (w8a16_gemm takes any M and K). */
 #define W8A16_GEMV_MAX_M 16
@@ -100,6 +122,21 @@ int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
  */
 int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
                int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * The GEMV and the GEMM with the scale buffer in `scale_format` (an
+ * enum w8a16_scale_format value; anything else returns W8A16_ERR_ARG).
+ * Shapes, streams, paths and errors are those of w8a16_gemv / w8a16_gemm;
+ * FP32 scales must be 4-byte aligned. Block scales are applied in fp32 to
+ * each 128-wide k-block's partial sum; a row scale multiplies the finished
+ * fp32 row sum once, before the BF16 rounding.
+ * w8a16_gemv(...) is w8a16_gemv_ex(..., W8A16_SCALE_BLOCK_BF16, ...), and
+ * likewise for the GEMM.
+ */
+int w8a16_gemv_ex(const void* A, const void* Wq, const void* scale, int scale_format, void* out,
+                  int64_t M, int64_t N, int64_t K, void* stream);
+int w8a16_gemm_ex(const void* A, const void* Wq, const void* scale, int scale_format, void* out,
+                  int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Dequantize only (a test path that exposes the device E4M3 decode and the

@@ -14,6 +14,11 @@ NemotronMamba2Layer docs (``set_fp8_weights``):
 
 Arrays are raw bit patterns: A and S are ``uint16`` BF16 bits, W is ``uint8``
 E4M3 codes. Results are fp64.
+
+Scale formats (``fmt``): ``"block_bf16"`` (S as above), ``"block_f32"`` (S a
+``float32`` grid of the same shape; nemotron_mamba2.rs listing,
+``set_fp8_weights``) and ``"row_f32"`` (S a ``float32`` [N] vector, one scale
+per weight row; Qwen3SsmLayer docs, ``set_fp8_rowwise_prefill_weights``).
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "w8a16_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle_w8a16.so")
 BLOCK = 128
+FORMATS = {"block_bf16": 0, "block_f32": 1, "row_f32": 2}
 
 _lib = None
 
@@ -66,6 +72,13 @@ def _load():
     lib.oracle_w8a16.argtypes = [P, P, P, I64, I64, I64, P, P]
     lib.oracle_w8a16_points.restype = None
     lib.oracle_w8a16_points.argtypes = [P, P, P, I64, I64, I64, P, P, I64, P, P]
+    C = ctypes.c_int
+    lib.oracle_dequant_fmt.restype = None
+    lib.oracle_dequant_fmt.argtypes = [P, P, C, I64, I64, P]
+    lib.oracle_w8a16_fmt.restype = None
+    lib.oracle_w8a16_fmt.argtypes = [P, P, P, C, I64, I64, I64, P, P]
+    lib.oracle_w8a16_points_fmt.restype = None
+    lib.oracle_w8a16_points_fmt.argtypes = [P, P, P, C, I64, I64, I64, P, P, I64, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -88,18 +101,26 @@ def scale_grid(N: int, K: int) -> tuple[int, int]:
     return ((N + BLOCK - 1) // BLOCK, (K + BLOCK - 1) // BLOCK)
 
 
-def _check_operands(A, W, S):
+def _check_scales(S, fmt: str, N: int, K: int) -> np.ndarray:
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown scale format {fmt!r}")
+    S = _c(S, np.uint16 if fmt == "block_bf16" else np.float32)
+    want = (N,) if fmt == "row_f32" else scale_grid(N, K)
+    if S.shape != want:
+        raise ValueError(f"{fmt} scales must have shape {want}, got {S.shape}")
+    return S
+
+
+def _check_operands(A, W, S, fmt="block_bf16"):
     A = _c(A, np.uint16)
     W = _c(W, np.uint8)
-    S = _c(S, np.uint16)
-    if A.ndim != 2 or W.ndim != 2 or S.ndim != 2:
-        raise ValueError("A, W and S must be 2-D")
+    if A.ndim != 2 or W.ndim != 2:
+        raise ValueError("A and W must be 2-D")
     M, K = A.shape
     N, K2 = W.shape
     if K2 != K:
         raise ValueError(f"A is [{M},{K}] but W is [{N},{K2}]")
-    if S.shape != scale_grid(N, K):
-        raise ValueError(f"S must be {scale_grid(N, K)}, got {S.shape}")
+    S = _check_scales(S, fmt, N, K)
     return A, W, S, M, N, K
 
 
@@ -127,34 +148,40 @@ def bf16_rne(x) -> np.ndarray:
     return out
 
 
-def dequant(W, S) -> np.ndarray:
-    """Wdeq[n, k] = E4M3(W[n, k]) * S[n//128, k//128] in fp64 (exact)."""
+def dequant(W, S, fmt: str = "block_bf16") -> np.ndarray:
+    """Wdeq[n, k] = E4M3(W[n, k]) * its scale, in fp64 (exact).
+
+    The scale is S[n//128, k//128] for the block formats, S[n] for row_f32."""
     W = _c(W, np.uint8)
-    S = _c(S, np.uint16)
     N, K = W.shape
-    if S.shape != scale_grid(N, K):
-        raise ValueError(f"S must be {scale_grid(N, K)}, got {S.shape}")
+    S = _check_scales(S, fmt, N, K)
     out = np.empty((N, K), np.float64)
-    _load().oracle_dequant(_ptr(W), _ptr(S), N, K, _ptr(out))
+    if fmt == "block_bf16":
+        _load().oracle_dequant(_ptr(W), _ptr(S), N, K, _ptr(out))
+    else:
+        _load().oracle_dequant_fmt(_ptr(W), _ptr(S), FORMATS[fmt], N, K, _ptr(out))
     return out
 
 
-def w8a16(A, W, S) -> tuple[np.ndarray, np.ndarray]:
+def w8a16(A, W, S, fmt: str = "block_bf16") -> tuple[np.ndarray, np.ndarray]:
     """Whole result: (ref, den), each [M, N] fp64.
 
     ref[m, n] = sum_k A[m,k] * Wdeq[n,k] (k ascending, fp64);
     den[m, n] = sum_k |A[m,k] * Wdeq[n,k]|.
     """
-    A, W, S, M, N, K = _check_operands(A, W, S)
+    A, W, S, M, N, K = _check_operands(A, W, S, fmt)
     ref = np.empty((M, N), np.float64)
     den = np.empty((M, N), np.float64)
-    _load().oracle_w8a16(_ptr(A), _ptr(W), _ptr(S), M, N, K, _ptr(ref), _ptr(den))
+    if fmt == "block_bf16":
+        _load().oracle_w8a16(_ptr(A), _ptr(W), _ptr(S), M, N, K, _ptr(ref), _ptr(den))
+    else:
+        _load().oracle_w8a16_fmt(_ptr(A), _ptr(W), _ptr(S), FORMATS[fmt], M, N, K, _ptr(ref), _ptr(den))
     return ref, den
 
 
-def w8a16_points(A, W, S, mi, ni) -> tuple[np.ndarray, np.ndarray]:
+def w8a16_points(A, W, S, mi, ni, fmt: str = "block_bf16") -> tuple[np.ndarray, np.ndarray]:
     """(ref, den) at the listed output coordinates (mi[p], ni[p])."""
-    A, W, S, M, N, K = _check_operands(A, W, S)
+    A, W, S, M, N, K = _check_operands(A, W, S, fmt)
     mi = np.ascontiguousarray(np.asarray(mi, dtype=np.int64))
     ni = np.ascontiguousarray(np.asarray(ni, dtype=np.int64))
     if mi.shape != ni.shape or mi.ndim != 1:
@@ -163,8 +190,12 @@ def w8a16_points(A, W, S, mi, ni) -> tuple[np.ndarray, np.ndarray]:
         raise IndexError("output coordinate out of range")
     ref = np.empty(mi.size, np.float64)
     den = np.empty(mi.size, np.float64)
-    _load().oracle_w8a16_points(_ptr(A), _ptr(W), _ptr(S), M, N, K,
-                                _ptr(mi), _ptr(ni), mi.size, _ptr(ref), _ptr(den))
+    if fmt == "block_bf16":
+        _load().oracle_w8a16_points(_ptr(A), _ptr(W), _ptr(S), M, N, K,
+                                    _ptr(mi), _ptr(ni), mi.size, _ptr(ref), _ptr(den))
+    else:
+        _load().oracle_w8a16_points_fmt(_ptr(A), _ptr(W), _ptr(S), FORMATS[fmt], M, N, K,
+                                        _ptr(mi), _ptr(ni), mi.size, _ptr(ref), _ptr(den))
     return ref, den
 
 

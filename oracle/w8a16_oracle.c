@@ -17,9 +17,18 @@
  *        of element (n, k) sits at index (n / 128) * ceil(K/128) + (k / 128).
  *
  * Every product here is exact in fp64: a BF16 value has 8 significant bits,
- * an E4M3 value 4 and a BF16 scale 8, so A * E4M3 * S has at most 20. The sum
- * runs over k in ascending order in fp64. `den` is the same sum of absolute
- * values; it scales the parity tolerance.
+ * an E4M3 value 4 and a BF16 scale 8, so A * E4M3 * S has at most 20 (at
+ * most 36 with an FP32 scale). The sum runs over k in ascending order in
+ * fp64. `den` is the same sum of absolute values; it scales the parity
+ * tolerance.
+ *
+ * Scale formats (the `_fmt` functions; the others take format 0):
+ *   0  BF16 block grid, as above;
+ *   1  FP32 block grid, same shape and index (nemotron_mamba2.rs listing,
+ *      `set_fp8_weights`: its format check names FP32 block scales);
+ *   2  FP32 per-row scale R[n], [N] (Qwen3SsmLayer docs,
+ *      `set_fp8_rowwise_prefill_weights`: per-row FP8 weights). The
+ *      dequantized weight is then E4M3(W[n][k]) * R[n] for every k.
  *
  * Parity pins (the tests that tie this file to something other than itself):
  * E4M3 decode against the OCP 8-bit floating-point specification's special
@@ -103,30 +112,43 @@ uint16_t oracle_bf16_rne(double x)
 
 static int64_t ceil_blocks(int64_t n) { return (n + ORACLE_BLOCK - 1) / ORACLE_BLOCK; }
 
-/* Dequantized weight as a real: E4M3(W[n][k]) * S[n/128][k/128]. */
-static double wdeq(const uint8_t* W, const uint16_t* S, int64_t K, int64_t n, int64_t k)
+/* The scale that multiplies E4M3(W[n][k]) in format fmt (exact in fp64). */
+static double scale_of(const void* S, int fmt, int64_t K, int64_t n, int64_t k)
 {
-    int64_t kb = ceil_blocks(K);
-    double e = oracle_e4m3_value(W[n * K + k]);
-    double s = oracle_bf16_value(S[(n / ORACLE_BLOCK) * kb + (k / ORACLE_BLOCK)]);
-    return e * s;
+    int64_t idx = (n / ORACLE_BLOCK) * ceil_blocks(K) + (k / ORACLE_BLOCK);
+    if (fmt == 0)
+        return oracle_bf16_value(((const uint16_t*)S)[idx]);
+    if (fmt == 1)
+        return (double)((const float*)S)[idx];
+    return (double)((const float*)S)[n];
 }
 
-/* out[n*K + k] = E4M3(W[n][k]) * S[n/128][k/128], exact, [N][K] fp64. */
-void oracle_dequant(const uint8_t* W, const uint16_t* S, int64_t N, int64_t K, double* out)
+/* Dequantized weight as a real: E4M3(W[n][k]) times its scale. */
+static double wdeq(const uint8_t* W, const void* S, int fmt, int64_t K, int64_t n, int64_t k)
+{
+    return oracle_e4m3_value(W[n * K + k]) * scale_of(S, fmt, K, n, k);
+}
+
+/* out[n*K + k] = Wdeq[n][k], exact, [N][K] fp64. */
+void oracle_dequant_fmt(const uint8_t* W, const void* S, int fmt, int64_t N, int64_t K, double* out)
 {
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k)
-            out[n * K + k] = wdeq(W, S, K, n, k);
+            out[n * K + k] = wdeq(W, S, fmt, K, n, k);
+}
+
+void oracle_dequant(const uint8_t* W, const uint16_t* S, int64_t N, int64_t K, double* out)
+{
+    oracle_dequant_fmt(W, S, 0, N, K, out);
 }
 
 /* One output element: ref = sum_k A[m][k]*Wdeq[n][k] (k ascending), den = sum |.|. */
-static void dot_one(const uint16_t* A, const uint8_t* W, const uint16_t* S,
+static void dot_one(const uint16_t* A, const uint8_t* W, const void* S, int fmt,
                     int64_t K, int64_t m, int64_t n, double* ref, double* den)
 {
     double acc = 0.0, mag = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        double t = oracle_bf16_value(A[m * K + k]) * wdeq(W, S, K, n, k);
+        double t = oracle_bf16_value(A[m * K + k]) * wdeq(W, S, fmt, K, n, k);
         acc += t;
         mag += fabs(t);
     }
@@ -136,28 +158,42 @@ static void dot_one(const uint16_t* A, const uint8_t* W, const uint16_t* S,
 
 /* Every element of the [M][N] result. Elements are independent; the threads
  * split the (m, n) pairs and never reorder a sum. */
-void oracle_w8a16(const uint16_t* A, const uint8_t* W, const uint16_t* S,
-                  int64_t M, int64_t N, int64_t K, double* ref, double* den)
+void oracle_w8a16_fmt(const uint16_t* A, const uint8_t* W, const void* S, int fmt,
+                      int64_t M, int64_t N, int64_t K, double* ref, double* den)
 {
     int64_t total = M * N;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < total; ++i) {
         int64_t m = i / N, n = i % N;
-        dot_one(A, W, S, K, m, n, &ref[i], &den[i]);
+        dot_one(A, W, S, fmt, K, m, n, &ref[i], &den[i]);
     }
+}
+
+void oracle_w8a16(const uint16_t* A, const uint8_t* W, const uint16_t* S,
+                  int64_t M, int64_t N, int64_t K, double* ref, double* den)
+{
+    oracle_w8a16_fmt(A, W, S, 0, M, N, K, ref, den);
 }
 
 /* Selected elements (mi[p], ni[p]) of the result, for shapes too large to
  * compute whole. */
+void oracle_w8a16_points_fmt(const uint16_t* A, const uint8_t* W, const void* S, int fmt,
+                             int64_t M, int64_t N, int64_t K,
+                             const int64_t* mi, const int64_t* ni, int64_t npts,
+                             double* ref, double* den)
+{
+    (void)M; (void)N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npts; ++p)
+        dot_one(A, W, S, fmt, K, mi[p], ni[p], &ref[p], &den[p]);
+}
+
 void oracle_w8a16_points(const uint16_t* A, const uint8_t* W, const uint16_t* S,
                          int64_t M, int64_t N, int64_t K,
                          const int64_t* mi, const int64_t* ni, int64_t npts,
                          double* ref, double* den)
 {
-    (void)M; (void)N;
-#pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t p = 0; p < npts; ++p)
-        dot_one(A, W, S, K, mi[p], ni[p], &ref[p], &den[p]);
+    oracle_w8a16_points_fmt(A, W, S, 0, M, N, K, mi, ni, npts, ref, den);
 }
 
 /* Element-wise array forms of the scalar conversions above. */

@@ -72,6 +72,28 @@ def test_rejections_before_any_hip_call(fn):
     assert call(out=FAKE + (2 << 30) - 2 * 4 * 256 + 16) == binding.ERR_ALIAS
 
 
+@pytest.mark.parametrize("fn", [binding.gemv_ex_raw, binding.gemm_ex_raw])
+def test_scale_format_rejections(fn):
+    A, W, S, O = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    M, N, K = 4, 256, 256
+    for bad in (-1, 3, 1000):
+        assert fn(A, W, S, bad, O, M, N, K, 0) == binding.ERR_ARG
+        assert fn(A, W, S, bad, O, 0, N, K, 0) == binding.ERR_ARG      # checked even for a no-op
+    for fmt in (binding.SCALE_BLOCK_BF16, binding.SCALE_BLOCK_F32, binding.SCALE_ROW_F32):
+        assert fn(A, W, S, fmt, O, 0, N, K, 0) == binding.OK
+        assert fn(A, W, 0, fmt, O, M, N, K, 0) == binding.ERR_NULL
+        assert fn(A, W, S + 1, fmt, O, M, N, K, 0) == binding.ERR_ALIGN
+    # FP32 scales need 4-byte alignment, BF16 ones only 2
+    assert fn(A, W, S + 2, binding.SCALE_BLOCK_F32, O, M, N, K, 0) == binding.ERR_ALIGN
+    assert fn(A, W, S + 2, binding.SCALE_ROW_F32, O, M, N, K, 0) == binding.ERR_ALIGN
+    # the overlap check uses each format's own size: N*4 bytes of row
+    # scales, 2x2 blocks of 4 (FP32) or 2 (BF16) bytes
+    out_row_end = S + 4 * N - 2                          # out's first element inside the row scales
+    assert fn(A, W, S, binding.SCALE_ROW_F32, out_row_end, M, N, K, 0) == binding.ERR_ALIAS
+    out_f32_end = S + 4 * 4 - 2
+    assert fn(A, W, S, binding.SCALE_BLOCK_F32, out_f32_end, M, N, K, 0) == binding.ERR_ALIAS
+
+
 def test_gemv_limits():
     F = FAKE
     args = (F, F + (1 << 30), F + (2 << 30), F + (3 << 30))
@@ -103,14 +125,29 @@ def test_binding_refuses_wrong_layouts():
         torch.zeros((N,), dtype=torch.bfloat16),                       # per-row [N]
         torch.zeros((), dtype=torch.bfloat16),                         # scalar
         torch.zeros((1,), dtype=torch.float32),                        # raw 4-byte scalar
-        torch.zeros(binding.scale_grid(N, K), dtype=torch.float32),    # fp32 grid
+        torch.zeros((N + 1,), dtype=torch.float32),                    # per-row, wrong length
+        torch.zeros(binding.scale_grid(N, K)[::-1], dtype=torch.float32),    # transposed fp32 grid
         torch.zeros(binding.scale_grid(N, K)[::-1], dtype=torch.bfloat16),   # transposed shape
         torch.zeros((3, 4), dtype=torch.bfloat16)[:, :2],              # right shape, not contiguous
+        torch.zeros((2 * N,), dtype=torch.float32)[::2],               # per-row, not contiguous
+        torch.zeros(binding.scale_grid(N, K), dtype=torch.float16),    # no such format
     ]
     for s in bad_scales:
         for fn in (binding.w8a16_gemv, binding.w8a16_gemm):
-            with pytest.raises(ValueError):
+            with pytest.raises(ValueError, match="scale"):
                 fn(A, W, s)
+    grid32 = torch.zeros(binding.scale_grid(N, K), dtype=torch.float32)
+    row32 = torch.zeros((N,), dtype=torch.float32)
+    for s, fmt in [(grid32, "row_f32"), (row32, "block_f32"), (S, "block_f32"), (grid32, "block_bf16"),
+                   (S, "per_tensor")]:
+        with pytest.raises(ValueError, match="scale"):
+            binding.w8a16_gemm(A, W, s, scale_format=fmt)             # explicit format disagrees
+    assert binding.scale_format_of(S) == "block_bf16"
+    assert binding.scale_format_of(grid32) == "block_f32"
+    assert binding.scale_format_of(row32) == "row_f32"
+    for s in (S, grid32, row32):                                        # valid layouts reach the device check
+        with pytest.raises(ValueError, match="HIP device"):
+            binding.w8a16_gemm(A, W, s)
     with pytest.raises(ValueError):
         binding.w8a16_gemm(A.float(), W, S)                            # A not bf16
     with pytest.raises(ValueError):
