@@ -23,6 +23,10 @@ hand-written round-to-nearest-even encoder.
 All arrays returned are raw bit patterns: A and scales as ``uint16`` BF16 bits,
 weights as ``uint8`` E4M3 codes.
 
+Norm inputs: the layer input, the gate z and the residual are drawn like A
+(N(0, 1) rounded to BF16); a norm weight is ``1 + 0.1 * N(0, 1)`` rounded to
+BF16; epsilon is ``NORM_EPS``.
+
 The FP32 scale formats (``weights_fmt``) use the same draws; ``block_f32``
 keeps ``max|w| / 448`` of each block in float32 (no BF16 rounding), and
 ``row_f32`` takes it over each whole weight row instead, as a float32 [N]
@@ -123,6 +127,17 @@ def quantize_rows_f32(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 
 
 SCALE_FORMATS = ("block_bf16", "block_f32", "row_f32")
+
+# Norm epsilon of the layer's RMSNorms (the pages do not give it; 1e-5 is the
+# usual value for this model family).
+NORM_EPS = 1e-5
+
+
+def norm_weight(K: int, seed: int) -> np.ndarray:
+    """A norm's weight [K] as BF16 bits: 1 + 0.1 * N(0, 1), rounded to BF16."""
+    rng = np.random.default_rng(seed)
+    w = np.float32(1) + np.float32(0.1) * rng.standard_normal(K, dtype=np.float32)
+    return _f32_to_bf16_bits(w)
 
 
 def weights_fmt(N: int, K: int, sigma: float, seed: int, fmt: str) -> tuple[np.ndarray, np.ndarray]:

@@ -79,6 +79,12 @@ def _load():
     lib.oracle_w8a16_fmt.argtypes = [P, P, P, C, I64, I64, I64, P, P]
     lib.oracle_w8a16_points_fmt.restype = None
     lib.oracle_w8a16_points_fmt.argtypes = [P, P, P, C, I64, I64, I64, P, P, I64, P, P]
+    lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_silu.argtypes = [ctypes.c_double]
+    lib.oracle_rmsnorm.restype = None
+    lib.oracle_rmsnorm.argtypes = [P, P, P, ctypes.c_double, I64, I64, P, P]
+    lib.oracle_residual_add.restype = None
+    lib.oracle_residual_add.argtypes = [P, P, I64, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -197,6 +203,45 @@ def w8a16_points(A, W, S, mi, ni, fmt: str = "block_bf16") -> tuple[np.ndarray, 
         _load().oracle_w8a16_points_fmt(_ptr(A), _ptr(W), _ptr(S), FORMATS[fmt], M, N, K,
                                         _ptr(mi), _ptr(ni), mi.size, _ptr(ref), _ptr(den))
     return ref, den
+
+
+def silu(z: float) -> float:
+    """z / (1 + exp(-z)) in fp64."""
+    return float(_load().oracle_silu(float(z)))
+
+
+def rmsnorm(x, weight, eps: float, gate=None) -> tuple[np.ndarray, np.ndarray]:
+    """Row-wise RMSNorm of BF16 x [M, K] times BF16 weight [K] (times silu(gate)).
+
+    Returns (exact fp64 values [M, K], their BF16 bits [M, K]); the norm is
+    one over each whole row (nemotron_mamba2.rs module docs, forward steps 1
+    and 6)."""
+    x = _c(x, np.uint16)
+    w = _c(weight, np.uint16)
+    if x.ndim != 2 or w.shape != (x.shape[1],):
+        raise ValueError(f"x must be [M, K] and weight [K], got {x.shape} and {w.shape}")
+    g = None
+    if gate is not None:
+        g = _c(gate, np.uint16)
+        if g.shape != x.shape:
+            raise ValueError(f"gate must match x {x.shape}, got {g.shape}")
+    M, K = x.shape
+    exact = np.empty((M, K), np.float64)
+    bits = np.empty((M, K), np.uint16)
+    _load().oracle_rmsnorm(_ptr(x), _ptr(g) if g is not None else None, _ptr(w), float(eps), M, K,
+                           _ptr(exact), _ptr(bits))
+    return exact, bits
+
+
+def residual_add(residual, ref) -> np.ndarray:
+    """BF16 bits of residual + bf16(ref): the residual add after the projection."""
+    r = _c(residual, np.uint16)
+    f = np.ascontiguousarray(np.asarray(ref, dtype=np.float64))
+    if r.shape != f.shape:
+        raise ValueError(f"residual {r.shape} and ref {f.shape} differ")
+    out = np.empty(r.shape, np.uint16)
+    _load().oracle_residual_add(_ptr(r), _ptr(f), r.size, _ptr(out))
+    return out
 
 
 def num_threads() -> int:

@@ -196,6 +196,62 @@ void oracle_w8a16_points(const uint16_t* A, const uint8_t* W, const uint16_t* S,
     oracle_w8a16_points_fmt(A, W, S, 0, M, N, K, mi, ni, npts, ref, den);
 }
 
+/*
+ * Norm prologues and the residual epilogue around the projection (the
+ * Mamba-2 layer's forward steps in the nemotron_mamba2.rs module docs: step 1,
+ * RMS norm scaled by its weight, before in_proj; step 6, the gated norm
+ * rms_norm(y, ssm_norm) * silu(z), before out_proj; step 8, the residual add
+ * after out_proj). The pages give neither epsilon nor the norm's grouping; the
+ * reading taken here is one norm over the whole row of K values, with epsilon
+ * an argument.
+ *
+ *   r        = 1 / sqrt( (sum_k x[k]^2) / K + eps )
+ *   v[k]     = x[k] * r * weight[k]                  (RMSNorm)
+ *   v[k]     = x[k] * r * weight[k] * silu(z[k])     (gated RMSNorm)
+ *   silu(z)  = z / (1 + exp(-z))
+ *
+ * computed in fp64; `exact` receives v and `bits` its BF16 rounding (the
+ * activation the projection then reads).
+ */
+double oracle_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+void oracle_rmsnorm(const uint16_t* x, const uint16_t* gate, const uint16_t* weight, double eps,
+                    int64_t M, int64_t K, double* exact, uint16_t* bits)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = oracle_bf16_value(x[m * K + k]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k) {
+            double v = oracle_bf16_value(x[m * K + k]) * r * oracle_bf16_value(weight[k]);
+            if (gate)
+                v *= oracle_silu(oracle_bf16_value(gate[m * K + k]));
+            exact[m * K + k] = v;
+            bits[m * K + k] = oracle_bf16_rne(v);
+        }
+    }
+}
+
+/*
+ * Residual epilogue: the projection's output is a BF16 tensor, and the
+ * residual add sums two BF16 tensors into a BF16 one:
+ *   out[i] = bf16( residual[i] + bf16(ref[i]) ).
+ */
+void oracle_residual_add(const uint16_t* residual, const double* ref, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double y = oracle_bf16_value(oracle_bf16_rne(ref[i]));
+        out[i] = oracle_bf16_rne(oracle_bf16_value(residual[i]) + y);
+    }
+}
+
 /* Element-wise array forms of the scalar conversions above. */
 void oracle_e4m3_values(const uint8_t* codes, int64_t n, double* out)
 {
