@@ -8,5 +8,8 @@ kernels in ``libw8a16.so`` (C ABI: ``include/w8a16.h``).
 * ``w8a16_gemv``    - decode, M = 1..16 rows
 * ``w8a16_gemm``    - prefill, any M
 * ``w8a16_dequant`` - dequantize only (test path for the decode and scale index)
+* ``w8a16_rmsnorm``, ``w8a16_gemv_fused``, ``w8a16_gemm_residual`` - the
+  layer's norm prologues and residual epilogue around the projections
 """
-from .binding import W8A16Error, w8a16_dequant, w8a16_gemm, w8a16_gemv  # noqa: F401
+from .binding import (W8A16Error, w8a16_dequant, w8a16_gemm, w8a16_gemm_residual,  # noqa: F401
+                      w8a16_gemv, w8a16_gemv_fused, w8a16_rmsnorm)

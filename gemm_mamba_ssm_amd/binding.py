@@ -30,7 +30,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw8a16.so")
 BLOCK = 128
 
-EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_gemv_ex", "w8a16_gemm_ex", "w8a16_dequant", "w8a16_strerror")
+EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_gemv_ex", "w8a16_gemm_ex", "w8a16_rmsnorm", "w8a16_gemv_fused",
+           "w8a16_gemm_residual", "w8a16_dequant", "w8a16_strerror")
 
 # enum w8a16_scale_format
 SCALE_BLOCK_BF16, SCALE_BLOCK_F32, SCALE_ROW_F32 = 0, 1, 2
@@ -40,6 +41,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ALIAS, ERR_ARG, ERR_MEMORY =
 GEMV_MAX_M = 16
 GEMV_MAX_K_SMALL_M = 16384   # M <= 8
 GEMV_MAX_K = 8192            # M >= 9
+FUSED_MAX_M = 8              # w8a16_gemv_fused: M <= 4 with K <= 16384, M <= 8 with K <= 8192
+FUSED_MAX_M_LONG_K = 4
 
 _lib = None
 
@@ -69,6 +72,13 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P, P, P, ctypes.c_int, P, I64, I64, I64, P]
+    F = ctypes.c_float
+    lib.w8a16_rmsnorm.restype = ctypes.c_int
+    lib.w8a16_rmsnorm.argtypes = [P, P, P, F, P, I64, I64, P]
+    lib.w8a16_gemv_fused.restype = ctypes.c_int
+    lib.w8a16_gemv_fused.argtypes = [P, P, P, F, P, P, P, P, I64, I64, I64, P]
+    lib.w8a16_gemm_residual.restype = ctypes.c_int
+    lib.w8a16_gemm_residual.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.w8a16_dequant.restype = ctypes.c_int
     lib.w8a16_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.w8a16_strerror.restype = ctypes.c_char_p
@@ -99,6 +109,21 @@ def gemv_ex_raw(A: int, Wq: int, scale: int, scale_format: int, out: int, M: int
 def gemm_ex_raw(A: int, Wq: int, scale: int, scale_format: int, out: int, M: int, N: int, K: int,
                 stream: int = 0) -> int:
     return load().w8a16_gemm_ex(A, Wq, scale, scale_format, out, M, N, K, stream)
+
+
+def rmsnorm_raw(x: int, gate: int, weight: int, eps: float, out: int, M: int, K: int, stream: int = 0) -> int:
+    return load().w8a16_rmsnorm(x, gate or None, weight, eps, out, M, K, stream)
+
+
+def gemv_fused_raw(A: int, gate: int, norm_weight: int, eps: float, Wq: int, scale: int, residual: int,
+                   out: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    return load().w8a16_gemv_fused(A, gate or None, norm_weight or None, eps, Wq, scale, residual or None,
+                                   out, M, N, K, stream)
+
+
+def gemm_residual_raw(A: int, Wq: int, scale: int, residual: int, out: int, M: int, N: int, K: int,
+                      stream: int = 0) -> int:
+    return load().w8a16_gemm_residual(A, Wq, scale, residual, out, M, N, K, stream)
 
 
 def dequant_raw(Wq: int, scale: int, out: int, N: int, K: int, stream: int = 0) -> int:
@@ -237,4 +262,102 @@ def w8a16_dequant(Wq: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | Non
                                   _stream_handle(Wq.device, stream))
     if st != OK:
         raise W8A16Error("w8a16_dequant", st)
+    return out
+
+
+# --- norm prologues and the residual epilogue ----------------------------------
+# (nemotron_mamba2.rs module docs, forward steps 1, 6 and 8.)
+
+def _check_bf16(t: torch.Tensor, name: str, shape: tuple):
+    _need(t.dtype == torch.bfloat16, f"{name} must be bfloat16, got {t.dtype}")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must be {list(shape)}, got {list(t.shape)}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _eps(eps) -> float:
+    e = float(eps)
+    _need(e >= 0.0 and e < 3.0e38, f"eps must be finite and >= 0, got {eps}")
+    return e
+
+
+def w8a16_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, gate: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16(x * rsqrt(mean(x^2) + eps) * weight [* silu(gate)]) per row of x [M, K] (BF16)."""
+    _need(x.dim() == 2, f"x must be [M, K], got shape {tuple(x.shape)}")
+    M, K = x.shape
+    _check_bf16(x, "x", (M, K))
+    _check_bf16(weight, "weight", (K,))
+    if gate is not None:
+        _check_bf16(gate, "gate", (M, K))
+    e = _eps(eps)
+    if out is None:
+        _check_device(*[t for t in (x, weight, gate) if t is not None])
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_bf16(out, "out", (M, K))
+        _check_device(*[t for t in (x, weight, gate, out) if t is not None])
+    with torch.cuda.device(x.device):
+        st = load().w8a16_rmsnorm(x.data_ptr(), gate.data_ptr() if gate is not None else None, weight.data_ptr(),
+                                  e, out.data_ptr(), M, K, _stream_handle(x.device, stream))
+    if st != OK:
+        raise W8A16Error("w8a16_rmsnorm", st)
+    return out
+
+
+def w8a16_gemv_fused(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
+                     norm_weight: torch.Tensor | None = None, eps: float = 1e-5,
+                     gate: torch.Tensor | None = None, residual: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode GEMV with the norm prologue (norm_weight, optional gate) and the
+    residual epilogue fused: out = [residual +] (norm(A) x dequant(Wq)^T), BF16."""
+    _need(A.dim() == 2, f"A must be [M, K], got shape {tuple(A.shape)}")
+    N, K = _check_weights(Wq, scale)
+    M = A.shape[0]
+    _check_bf16(A, "A", (M, K))
+    _need(gate is None or norm_weight is not None, "a gate needs a norm weight")
+    if norm_weight is not None:
+        _check_bf16(norm_weight, "norm_weight", (K,))
+    if gate is not None:
+        _check_bf16(gate, "gate", (M, K))
+    if residual is not None:
+        _check_bf16(residual, "residual", (M, N))
+    e = _eps(eps)
+    _need(M <= FUSED_MAX_M and (K <= GEMV_MAX_K if M > FUSED_MAX_M_LONG_K else K <= GEMV_MAX_K_SMALL_M),
+          f"w8a16_gemv_fused takes M <= 4 with K <= {GEMV_MAX_K_SMALL_M} or M <= 8 with K <= {GEMV_MAX_K}, "
+          f"got M={M}, K={K} (use w8a16_rmsnorm + w8a16_gemm_residual)")
+    ins = [t for t in (A, Wq, scale, norm_weight, gate, residual) if t is not None]
+    if out is None:
+        _check_device(*ins)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    else:
+        _check_bf16(out, "out", (M, N))
+        _check_device(*ins, out)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    with torch.cuda.device(A.device):
+        st = load().w8a16_gemv_fused(A.data_ptr(), ptr(gate), ptr(norm_weight), e, Wq.data_ptr(), scale.data_ptr(),
+                                     ptr(residual), out.data_ptr(), M, N, K, _stream_handle(A.device, stream))
+    if st != OK:
+        raise W8A16Error("w8a16_gemv_fused", st)
+    return out
+
+
+def w8a16_gemm_residual(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor, residual: torch.Tensor,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Prefill GEMM with the residual epilogue: out = bf16(residual + bf16(A x dequant(Wq)^T))."""
+    _need(A.dim() == 2, f"A must be [M, K], got shape {tuple(A.shape)}")
+    N, K = _check_weights(Wq, scale)
+    M = A.shape[0]
+    _check_bf16(A, "A", (M, K))
+    _check_bf16(residual, "residual", (M, N))
+    if out is None:
+        _check_device(A, Wq, scale, residual)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    else:
+        _check_bf16(out, "out", (M, N))
+        _check_device(A, Wq, scale, residual, out)
+    with torch.cuda.device(A.device):
+        st = load().w8a16_gemm_residual(A.data_ptr(), Wq.data_ptr(), scale.data_ptr(), residual.data_ptr(),
+                                        out.data_ptr(), M, N, K, _stream_handle(A.device, stream))
+    if st != OK:
+        raise W8A16Error("w8a16_gemm_residual", st)
     return out

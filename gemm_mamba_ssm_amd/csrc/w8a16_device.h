@@ -112,4 +112,67 @@ __device__ __forceinline__ u32x4_t load16(const void* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+// --- norm prologues and the residual epilogue (nemotron_mamba2.rs module
+// docs, forward steps 1, 6 and 8) ---
+
+// What a fused projection does around the product (kernel argument): a
+// norm prologue on the activations when `weight` is set (gated by silu(gate)
+// when `gate` is set too), and a residual epilogue when `residual` is set.
+struct Fusion {
+    const uint16_t* gate;       // [M][K] BF16, or nullptr
+    const uint16_t* weight;     // [K] BF16 norm weight, or nullptr (no norm)
+    const uint16_t* residual;   // [M][N] BF16, or nullptr
+    float eps;
+};
+
+// SiLU in fp32: z / (1 + e^-z).
+__device__ __forceinline__ float silu(float z) {
+    return z / (1.0f + expf(-z));
+}
+
+// Sum of squares of 8 BF16 values (4 packed pairs).
+__device__ __forceinline__ float sumsq8(u32x4_t x) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_bits_to_f32(x[i] & 0xFFFFu), hi = bf16_bits_to_f32(x[i] >> 16);
+        s = fmaf(lo, lo, s);
+        s = fmaf(hi, hi, s);
+    }
+    return s;
+}
+
+// 8 normalized activations: bf16(x * r * w), or bf16(x * r * w * silu(g))
+// when GATED, in fp32 with one rounding at the end.
+template <bool GATED>
+__device__ __forceinline__ u32x4_t norm8(u32x4_t x, u32x4_t w, u32x4_t g, float r) {
+    u32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float lo = bf16_bits_to_f32(x[i] & 0xFFFFu) * r * bf16_bits_to_f32(w[i] & 0xFFFFu);
+        float hi = bf16_bits_to_f32(x[i] >> 16) * r * bf16_bits_to_f32(w[i] >> 16);
+        if constexpr (GATED) {
+            lo *= silu(bf16_bits_to_f32(g[i] & 0xFFFFu));
+            hi *= silu(bf16_bits_to_f32(g[i] >> 16));
+        }
+        o[i] = static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+    }
+    return o;
+}
+
+// 1 / sqrt(mean of squares + eps) of a row of K values.
+__device__ __forceinline__ float rms_factor(float sumsq, int K, float eps) {
+    return 1.0f / sqrtf(sumsq / static_cast<float>(K) + eps);
+}
+
+// The residual add after the projection: both operands are BF16 tensors, so
+// the projection's sum is rounded to BF16 first (y), then the sum of the two.
+__device__ __forceinline__ uint16_t residual_add_bits(uint16_t y, uint16_t residual) {
+    return f32_to_bf16_bits(bf16_bits_to_f32(residual) + bf16_bits_to_f32(y));
+}
+
+__device__ __forceinline__ uint16_t residual_out(float sum, uint16_t residual) {
+    return residual_add_bits(f32_to_bf16_bits(sum), residual);
+}
+
 }  // namespace w8a16

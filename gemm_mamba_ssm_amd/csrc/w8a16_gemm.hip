@@ -192,11 +192,14 @@ __device__ __forceinline__ void wait_steps(int younger) {
         wait_vmem<0>();
 }
 
-// The GEMM for tile shape C and scale format SF; each pair has its own
-// kernel below (with its own occupancy bound).
-template <class C, int SF>
+// The GEMM for tile shape C and scale format SF, with the residual epilogue
+// out = bf16(res + bf16(sum)) when RES (nemotron_mamba2.rs module docs,
+// forward step 8); each combination has its own kernel below (with its own
+// occupancy bound).
+template <class C, int SF, bool RES>
 __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
-                                          const void* __restrict__ S, uint16_t* __restrict__ out,
+                                          const void* __restrict__ S, const uint16_t* __restrict__ res,
+                                          uint16_t* __restrict__ out,
                                           float* __restrict__ partials, int M, int N, int K, const Schedule& sc) {
     constexpr int TM = C::TM, BI = C::BI, BJ = C::BJ, kStages = C::kStages;
     constexpr int kAChunksPerThread = C::kAChunksPerThread, kWChunksPerThread = C::kWChunksPerThread;
@@ -270,8 +273,13 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = m0 + wm * kWaveRows + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
-                    if (m < M && n < N)
-                        out[static_cast<int64_t>(m) * N + n] = f32_to_bf16_bits(r[bi][bj][v] * rs);
+                    if (m < M && n < N) {
+                        const int64_t o = static_cast<int64_t>(m) * N + n;
+                        if constexpr (RES)
+                            out[o] = residual_out(r[bi][bj][v] * rs, res[o]);
+                        else
+                            out[o] = f32_to_bf16_bits(r[bi][bj][v] * rs);
+                    }
                 }
             }
     };
@@ -476,28 +484,32 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
     }
 }
 
-// One kernel per (tile shape, scale format); suffixes: s1 = FP32 block
-// scales, r = FP32 row scales.
-#define W8A16_GEMM_KERNEL(NAME, C, SF)                                                               \
+// One kernel per (tile shape, scale format, residual); suffixes: s1 = FP32
+// block scales, r = FP32 row scales, res = residual epilogue.
+#define W8A16_GEMM_KERNEL(NAME, C, SF, RES)                                                          \
     __global__ void __launch_bounds__(kThreads, C::kWgPerCu)                                         \
     NAME(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,   \
-         uint16_t* __restrict__ out, float* __restrict__ partials, int M, int N, int K, Schedule sc) {  \
-        gemm_body<C, SF>(A, W, S, out, partials, M, N, K, sc);                                       \
+         const uint16_t* __restrict__ res, uint16_t* __restrict__ out, float* __restrict__ partials,  \
+         int M, int N, int K, Schedule sc) {                                                         \
+        gemm_body<C, SF, RES>(A, W, S, res, out, partials, M, N, K, sc);                             \
     }                                                                                                \
     template <>                                                                                      \
-    struct GemmKernel<C, SF> {                                                                       \
+    struct GemmKernel<C, SF, RES> {                                                                  \
         static constexpr auto fn = &NAME;                                                            \
     };
-template <class C, int SF> struct GemmKernel;
-W8A16_GEMM_KERNEL(gemm_kernel_128, BigTile, kScaleBlockBf16)
-W8A16_GEMM_KERNEL(gemm_kernel_64, Skinny64, kScaleBlockBf16)
-W8A16_GEMM_KERNEL(gemm_kernel_32, Skinny32, kScaleBlockBf16)
-W8A16_GEMM_KERNEL(gemm_kernel_128_s1, BigTile, kScaleBlockF32)
-W8A16_GEMM_KERNEL(gemm_kernel_64_s1, Skinny64, kScaleBlockF32)
-W8A16_GEMM_KERNEL(gemm_kernel_32_s1, Skinny32, kScaleBlockF32)
-W8A16_GEMM_KERNEL(gemm_kernel_128_r, BigTile, kScaleRowF32)
-W8A16_GEMM_KERNEL(gemm_kernel_64_r, Skinny64, kScaleRowF32)
-W8A16_GEMM_KERNEL(gemm_kernel_32_r, Skinny32, kScaleRowF32)
+template <class C, int SF, bool RES> struct GemmKernel;
+W8A16_GEMM_KERNEL(gemm_kernel_128, BigTile, kScaleBlockBf16, false)
+W8A16_GEMM_KERNEL(gemm_kernel_64, Skinny64, kScaleBlockBf16, false)
+W8A16_GEMM_KERNEL(gemm_kernel_32, Skinny32, kScaleBlockBf16, false)
+W8A16_GEMM_KERNEL(gemm_kernel_128_s1, BigTile, kScaleBlockF32, false)
+W8A16_GEMM_KERNEL(gemm_kernel_64_s1, Skinny64, kScaleBlockF32, false)
+W8A16_GEMM_KERNEL(gemm_kernel_32_s1, Skinny32, kScaleBlockF32, false)
+W8A16_GEMM_KERNEL(gemm_kernel_128_r, BigTile, kScaleRowF32, false)
+W8A16_GEMM_KERNEL(gemm_kernel_64_r, Skinny64, kScaleRowF32, false)
+W8A16_GEMM_KERNEL(gemm_kernel_32_r, Skinny32, kScaleRowF32, false)
+W8A16_GEMM_KERNEL(gemm_kernel_128_res, BigTile, kScaleBlockBf16, true)
+W8A16_GEMM_KERNEL(gemm_kernel_64_res, Skinny64, kScaleBlockBf16, true)
+W8A16_GEMM_KERNEL(gemm_kernel_32_res, Skinny32, kScaleBlockBf16, true)
 #undef W8A16_GEMM_KERNEL
 
 // Combine of the split tiles. The host lists, for every split tile, the
@@ -515,10 +527,10 @@ struct SplitList {
     uint16_t first[kMaxSplits];
 };
 
-template <class C, int SF>
+template <class C, int SF, bool RES>
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, const void* __restrict__ S,
-               int M, int N, Schedule sc, SplitList list) {
+               const uint16_t* __restrict__ res, int M, int N, Schedule sc, SplitList list) {
     constexpr int TM = C::TM, kTileFloats = C::kTileFloats;
     const int w = list.first[blockIdx.x];
     const int k_blocks = sc.k_blocks;
@@ -563,10 +575,15 @@ combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, c
     for (int r = 0; r < 4; ++r) {
         const int m = m0 + row0 + r * 8;
         if (m >= M) break;
-        uint16_t* dst = out + static_cast<int64_t>(m) * N + n0 + col;
+        const int64_t o = static_cast<int64_t>(m) * N + n0 + col;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (n0 + col + e < N) dst[e] = f32_to_bf16_bits(sum[r][e] * rs[e]);
+            if (n0 + col + e < N) {
+                if constexpr (RES)
+                    out[o + e] = residual_out(sum[r][e] * rs[e], res[o + e]);
+                else
+                    out[o + e] = f32_to_bf16_bits(sum[r][e] * rs[e]);
+            }
     }
 }
 
@@ -648,9 +665,9 @@ int workspace_for(hipStream_t stream, size_t bytes, Workspace* ws) {
 
 // Plan and launch the GEMM (and, if tiles are split, the combine) with tile
 // shape C and scale format SF.
-template <class C, int SF>
-int run_gemm(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
-             hipStream_t s) {
+template <class C, int SF, bool RES>
+int run_gemm(const void* A, const void* Wq, const void* scale, const void* residual, void* out, int64_t M,
+             int64_t N, int64_t K, hipStream_t s) {
     // Buffer offsets are 32-bit: one tile's rows of A must span less than 2 GiB.
     if (static_cast<int64_t>(C::TM) * K * 2 >= static_cast<int64_t>(kOutOfRange)) return W8A16_ERR_SHAPE;
     const int64_t tiles_m = ceil_div(M, C::TM);
@@ -665,26 +682,26 @@ int run_gemm(const void* A, const void* Wq, const void* scale, void* out, int64_
         const int st = workspace_for(s, static_cast<size_t>(2) * slots * C::kTileFloats * sizeof(float), &ws);
         if (st != W8A16_OK) return st;
     }
-    int st = launch(GemmKernel<C, SF>::fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), s,
+    int st = launch(GemmKernel<C, SF, RES>::fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), s,
                     static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
-                    static_cast<uint16_t*>(out), ws.partials,
+                    static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out), ws.partials,
                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), sc);
     if (st != W8A16_OK || sc.shared_groups == 0) return st;
     SplitList list;
     const int splits = list_splits(sc, &list);
     if (splits == 0) return W8A16_OK;
-    return launch(&combine_kernel<C, SF>, dim3(static_cast<unsigned>(splits), C::TM / kCombineRows), dim3(kThreads),
-                  s, static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), scale,
-                  static_cast<int>(M), static_cast<int>(N), sc, list);
+    return launch(&combine_kernel<C, SF, RES>, dim3(static_cast<unsigned>(splits), C::TM / kCombineRows),
+                  dim3(kThreads), s, static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), scale,
+                  static_cast<const uint16_t*>(residual), static_cast<int>(M), static_cast<int>(N), sc, list);
 }
 
-template <int SF>
-int gemm_by_shape(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
-                  hipStream_t s) {
-    if (skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, SF, out, M, N, K, s);
-    if (M <= Skinny32::TM) return run_gemm<Skinny32, SF>(A, Wq, scale, out, M, N, K, s);
-    if (M <= Skinny64::TM) return run_gemm<Skinny64, SF>(A, Wq, scale, out, M, N, K, s);
-    return run_gemm<BigTile, SF>(A, Wq, scale, out, M, N, K, s);
+template <int SF, bool RES>
+int gemm_by_shape(const void* A, const void* Wq, const void* scale, const void* residual, void* out, int64_t M,
+                  int64_t N, int64_t K, hipStream_t s) {
+    if (skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
+    if (M <= Skinny32::TM) return run_gemm<Skinny32, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
+    if (M <= Skinny64::TM) return run_gemm<Skinny64, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
+    return run_gemm<BigTile, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
 }
 
 }  // namespace
@@ -698,13 +715,30 @@ extern "C" int w8a16_gemm_ex(const void* A, const void* Wq, const void* scale, i
     if (st != W8A16_OK || noop) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (scale_format) {
-        case W8A16_SCALE_BLOCK_F32: return gemm_by_shape<kScaleBlockF32>(A, Wq, scale, out, M, N, K, s);
-        case W8A16_SCALE_ROW_F32: return gemm_by_shape<kScaleRowF32>(A, Wq, scale, out, M, N, K, s);
-        default: return gemm_by_shape<kScaleBlockBf16>(A, Wq, scale, out, M, N, K, s);
+        case W8A16_SCALE_BLOCK_F32:
+            return gemm_by_shape<kScaleBlockF32, false>(A, Wq, scale, nullptr, out, M, N, K, s);
+        case W8A16_SCALE_ROW_F32:
+            return gemm_by_shape<kScaleRowF32, false>(A, Wq, scale, nullptr, out, M, N, K, s);
+        default:
+            return gemm_by_shape<kScaleBlockBf16, false>(A, Wq, scale, nullptr, out, M, N, K, s);
     }
 }
 
 extern "C" int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
                           int64_t M, int64_t N, int64_t K, void* stream) {
     return w8a16_gemm_ex(A, Wq, scale, W8A16_SCALE_BLOCK_BF16, out, M, N, K, stream);
+}
+
+extern "C" int w8a16_gemm_residual(const void* A, const void* Wq, const void* scale, const void* residual,
+                                   void* out, int64_t M, int64_t N, int64_t K, void* stream) {
+    using namespace w8a16;
+    bool noop = false;
+    const int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
+    if (st != W8A16_OK || noop) return st;
+    if (!residual) return W8A16_ERR_NULL;
+    if (!aligned(residual, 2)) return W8A16_ERR_ALIGN;
+    const int64_t out_bytes = M * N * 2;
+    if (overlaps(out, out_bytes, residual, out_bytes)) return W8A16_ERR_ALIAS;
+    return gemm_by_shape<kScaleBlockBf16, true>(A, Wq, scale, residual, out, M, N, K,
+                                                static_cast<hipStream_t>(stream));
 }

@@ -26,6 +26,11 @@
 //    butterfly that halves the value count at every step (so the cost per
 //    output shrinks as RB*MR grows), then across the kw waves through LDS.
 //    The order of every sum is fixed: results are deterministic. No atomics.
+//  * Fused form (w8a16_gemv_fused; nemotron_mamba2.rs module docs, forward
+//    steps 1, 6 and 8): the activations a lane holds are normalized in place
+//    before the loop (the row's sum of squares is reduced over the workgroup
+//    in a fixed order; the norm weight and the gate are read for the lane's
+//    chunks only), and the residual is added at the output store.
 #include <algorithm>
 
 #include "w8a16_device.h"
@@ -66,7 +71,7 @@ __device__ __forceinline__ void butterfly(float (&v)[P], int lane) {
     }
 }
 
-template <int MR, int J, int RB, int SF>
+template <int MR, int J, int RB, int SF, bool FUSED>
 struct Gemv {
     static constexpr int V = RB * MR;          // partial sums per lane per group
     static constexpr int P = pow2_ceil(V);     // padded to a power of two for the butterfly
@@ -98,9 +103,21 @@ struct Gemv {
             r.s[j] = kvalid[j] ? block_scale<SF>(S, scale_index(n0, kch[j], k_blocks)) : 0.0f;
     }
 
+    // The output element o: BF16 of the sum, or the residual epilogue.
+    __device__ static __forceinline__ void store(uint16_t* __restrict__ out, const uint16_t* __restrict__ res,
+                                                 int64_t o, float val) {
+        if constexpr (FUSED)
+            if (res) {
+                out[o] = residual_out(val, res[o]);
+                return;
+            }
+        out[o] = f32_to_bf16_bits(val);
+    }
+
     __device__ static __forceinline__ void process(const Regs& r, const uint32_t (&a)[MR][J][8],
                                                    float (*red)[kMaxWaves][V], int parity,
-                                                   uint16_t* __restrict__ out, const void* __restrict__ S,
+                                                   uint16_t* __restrict__ out, const uint16_t* __restrict__ res,
+                                                   const void* __restrict__ S,
                                                    int g, int N, int lane, int wave, int nwaves) {
         float v[P];
 #pragma unroll
@@ -130,7 +147,7 @@ struct Gemv {
             if (holder) {
                 const int i = idx / MR, m = idx % MR;
                 if (n0 + i < N)
-                    out[static_cast<int64_t>(m) * N + n0 + i] = f32_to_bf16_bits(v[0] * row_scale<SF>(S, n0 + i));
+                    store(out, res, static_cast<int64_t>(m) * N + n0 + i, v[0] * row_scale<SF>(S, n0 + i));
             }
         } else {
             if (holder) red[parity][wave][idx] = v[0];
@@ -140,7 +157,7 @@ struct Gemv {
                 for (int w = 0; w < nwaves; ++w) tot += red[parity][w][lane];
                 const int i = lane / MR, m = lane % MR;
                 if (n0 + i < N)
-                    out[static_cast<int64_t>(m) * N + n0 + i] = f32_to_bf16_bits(tot * row_scale<SF>(S, n0 + i));
+                    store(out, res, static_cast<int64_t>(m) * N + n0 + i, tot * row_scale<SF>(S, n0 + i));
             }
             // The next group writes red[parity ^ 1]; red[parity] is written
             // again only after the next barrier, which wave 0 reaches after
@@ -149,12 +166,68 @@ struct Gemv {
     }
 };
 
-template <int MR, int J, int RB, int SF>
+// Normalize the activations a lane holds (rows of MR, chunks kch[j]) in
+// place: a = bf16(x * r * weight [* silu(gate)]), r from the row's sum of
+// squares over all K, reduced over the wave, then over the waves in order.
+template <int MR, int J>
+__device__ __forceinline__ void norm_prologue(uint32_t (&a)[MR][J][8], const Fusion& fu, int K,
+                                              const int (&kch)[J], const bool (&kvalid)[J],
+                                              int lane, int wave, int nwaves) {
+    __shared__ float ssq[kMaxWaves][16];
+    float r[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            ss += sumsq8(u32x4_t{a[m][j][0], a[m][j][1], a[m][j][2], a[m][j][3]});
+            ss += sumsq8(u32x4_t{a[m][j][4], a[m][j][5], a[m][j][6], a[m][j][7]});
+        }
+        r[m] = wave_sum(ss);
+    }
+    if (lane == 0)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) ssq[wave][m] = r[m];
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        float t = 0.0f;
+        for (int w = 0; w < nwaves; ++w) t += ssq[w][m];
+        r[m] = rms_factor(t, K, fu.eps);
+    }
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        if (!kvalid[j]) continue;
+        const u32x4_t wl = load16(fu.weight + kch[j]), wh = load16(fu.weight + kch[j] + 8);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const u32x4_t xl = {a[m][j][0], a[m][j][1], a[m][j][2], a[m][j][3]};
+            const u32x4_t xh = {a[m][j][4], a[m][j][5], a[m][j][6], a[m][j][7]};
+            u32x4_t nl, nh;
+            if (fu.gate) {
+                const uint16_t* g = fu.gate + static_cast<int64_t>(m) * K + kch[j];
+                nl = norm8<true>(xl, wl, load16(g), r[m]);
+                nh = norm8<true>(xh, wh, load16(g + 8), r[m]);
+            } else {
+                nl = norm8<false>(xl, wl, zero, r[m]);
+                nh = norm8<false>(xh, wh, zero, r[m]);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                a[m][j][t] = nl[t];
+                a[m][j][4 + t] = nh[t];
+            }
+        }
+    }
+}
+
+template <int MR, int J, int RB, int SF, bool FUSED>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             const void* __restrict__ S, uint16_t* __restrict__ out,
-            int N, int K, int groups_per_block) {
-    using G = Gemv<MR, J, RB, SF>;
+            int N, int K, int groups_per_block, Fusion fu) {
+    using G = Gemv<MR, J, RB, SF, FUSED>;
     __shared__ float red[2][kMaxWaves][G::V];
 
     const int lane = threadIdx.x & 63;
@@ -197,19 +270,25 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             }
         }
 
+    const uint16_t* res = nullptr;
+    if constexpr (FUSED) {
+        if (fu.weight) norm_prologue<MR, J>(a, fu, K, kch, kvalid, lane, wave, nwaves);
+        res = fu.residual;
+    }
+
     int parity = 0;
     for (int g = g_begin; g < g_end; g += 2) {
         if (g + 1 < g_end) G::load(rb, W, S, g + 1, N, K, k_blocks, kch, kvalid);
-        G::process(ra, a, red, parity, out, S, g, N, lane, wave, nwaves);
+        G::process(ra, a, red, parity, out, res, S, g, N, lane, wave, nwaves);
         parity ^= 1;
         if (g + 1 >= g_end) break;
         if (g + 2 < g_end) G::load(ra, W, S, g + 2, N, K, k_blocks, kch, kvalid);
-        G::process(rb, a, red, parity, out, S, g + 1, N, lane, wave, nwaves);
+        G::process(rb, a, red, parity, out, res, S, g + 1, N, lane, wave, nwaves);
         parity ^= 1;
     }
 }
 
-typedef void (*gemv_fn)(const uint16_t*, const uint8_t*, const void*, uint16_t*, int, int, int);
+typedef void (*gemv_fn)(const uint16_t*, const uint8_t*, const void*, uint16_t*, int, int, int, Fusion);
 
 // Chunks per lane: 1 while K <= 8192 (8 waves of 1024), 2 up to 16384 (M <= 8).
 constexpr int max_chunks(int mr) { return mr <= 8 ? 2 : 1; }
@@ -223,16 +302,25 @@ constexpr int rows_per_group(int mr, int j) {
     return rb;
 }
 
-template <int MR, int J, int SF>
+template <int MR, int J, int SF, bool FU>
 gemv_fn pick_j() {
-    return &gemv_kernel<MR, J, rows_per_group(MR, J), SF>;
+    return &gemv_kernel<MR, J, rows_per_group(MR, J), SF, FU>;
 }
 
-template <int MR, int SF>
+// The fused kernels hold the norm's operands beside the activations; they
+// fit in registers without spilling for M <= 4 (any K up to 16384) and for
+// M <= 8 with K <= 8192 (one chunk per lane).
+constexpr int64_t kFusedMaxM = 8, kFusedMaxMTwoChunks = 4;
+inline bool fused_fits(int64_t M, int64_t K) {
+    return M >= 1 && (M <= kFusedMaxMTwoChunks ? K <= W8A16_GEMV_MAX_K_SMALL_M
+                                               : M <= kFusedMaxM && K <= kWaveK * kMaxWaves);
+}
+
+template <int MR, int SF, bool FU>
 gemv_fn pick(int j) {
-    if constexpr (max_chunks(MR) >= 2)
-        if (j == 2) return pick_j<MR, 2, SF>();
-    return pick_j<MR, 1, SF>();
+    if constexpr (max_chunks(MR) >= 2 && (!FU || MR <= kFusedMaxMTwoChunks))
+        if (j == 2) return pick_j<MR, 2, SF, FU>();
+    return pick_j<MR, 1, SF, FU>();
 }
 
 struct Choice {
@@ -240,42 +328,64 @@ struct Choice {
     int rows_per_group;
 };
 
-template <int MR, int SF>
+template <int MR, int SF, bool FU>
 Choice choose(int j) {
-    return {pick<MR, SF>(j), j == 2 ? rows_per_group(MR, 2) : rows_per_group(MR, 1)};
+    return {pick<MR, SF, FU>(j), j == 2 ? rows_per_group(MR, 2) : rows_per_group(MR, 1)};
 }
 
 template <int SF>
+Choice select_plain(int mr, int j);
+
+template <int SF, bool FU>
 Choice select_kernel(int mr, int j) {
-    switch (mr) {
-        case 1: return choose<1, SF>(j);
-        case 2: return choose<2, SF>(j);
-        case 3: return choose<3, SF>(j);
-        case 4: return choose<4, SF>(j);
-        case 5: return choose<5, SF>(j);
-        case 6: return choose<6, SF>(j);
-        case 7: return choose<7, SF>(j);
-        case 8: return choose<8, SF>(j);
-        case 9: return choose<9, SF>(j);
-        case 10: return choose<10, SF>(j);
-        case 11: return choose<11, SF>(j);
-        case 12: return choose<12, SF>(j);
-        case 13: return choose<13, SF>(j);
-        case 14: return choose<14, SF>(j);
-        case 15: return choose<15, SF>(j);
-        default: return choose<16, SF>(j);
+    if constexpr (FU) {
+        switch (mr) {
+            case 1: return choose<1, SF, FU>(j);
+            case 2: return choose<2, SF, FU>(j);
+            case 3: return choose<3, SF, FU>(j);
+            case 4: return choose<4, SF, FU>(j);
+            case 5: return choose<5, SF, FU>(j);
+            case 6: return choose<6, SF, FU>(j);
+            case 7: return choose<7, SF, FU>(j);
+            default: return choose<8, SF, FU>(j);
+        }
+    } else {
+        return select_plain<SF>(mr, j);
     }
 }
 
-// The launch of the GEMV for scale format SF (arguments checked).
 template <int SF>
+Choice select_plain(int mr, int j) {
+    switch (mr) {
+        case 1: return choose<1, SF, false>(j);
+        case 2: return choose<2, SF, false>(j);
+        case 3: return choose<3, SF, false>(j);
+        case 4: return choose<4, SF, false>(j);
+        case 5: return choose<5, SF, false>(j);
+        case 6: return choose<6, SF, false>(j);
+        case 7: return choose<7, SF, false>(j);
+        case 8: return choose<8, SF, false>(j);
+        case 9: return choose<9, SF, false>(j);
+        case 10: return choose<10, SF, false>(j);
+        case 11: return choose<11, SF, false>(j);
+        case 12: return choose<12, SF, false>(j);
+        case 13: return choose<13, SF, false>(j);
+        case 14: return choose<14, SF, false>(j);
+        case 15: return choose<15, SF, false>(j);
+        default: return choose<16, SF, false>(j);
+    }
+}
+
+// The launch of the GEMV for scale format SF, fused or not (arguments
+// checked).
+template <int SF, bool FU>
 int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
-             hipStream_t stream) {
+             hipStream_t stream, Fusion fu = Fusion{nullptr, nullptr, nullptr, 0.0f}) {
     const int mr = static_cast<int>(M);
     const int j = K > static_cast<int64_t>(kWaveK) * kMaxWaves ? 2 : 1;
     const int nwaves = static_cast<int>(ceil_div(K, static_cast<int64_t>(kWaveK) * j));
     if (nwaves > kMaxWaves || j > max_chunks(mr)) return W8A16_ERR_SHAPE;
-    Choice c = select_kernel<SF>(mr, j);
+    Choice c = select_kernel<SF, FU>(mr, j);
     const int64_t cus = device_cu_count();
     int64_t per_block;
     if (mr == 1 && j == 1) {
@@ -284,7 +394,7 @@ int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_
         // 8-row groups; one group per workgroup up to about 18 workgroups per
         // CU, then several.
         const int rb = ceil_div(N, 4) >= 8 * cus ? 4 : 8;
-        c = {rb == 4 ? &gemv_kernel<1, 1, 4, SF> : &gemv_kernel<1, 1, 8, SF>, rb};
+        c = {rb == 4 ? &gemv_kernel<1, 1, 4, SF, FU> : &gemv_kernel<1, 1, 8, SF, FU>, rb};
         per_block = std::max<int64_t>(1, ceil_div(N, rb) / (18 * cus));
     } else {
         const int64_t resident = cus * (kWavesPerCu / nwaves > 0 ? kWavesPerCu / nwaves : 1);
@@ -296,7 +406,7 @@ int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_
     return launch(c.fn, dim3(static_cast<unsigned>(blocks)), dim3(64 * nwaves), stream,
                   static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
                   static_cast<uint16_t*>(out), static_cast<int>(N), static_cast<int>(K),
-                  static_cast<int>(per_block));
+                  static_cast<int>(per_block), fu);
 }
 
 }  // namespace
@@ -316,15 +426,40 @@ extern "C" int w8a16_gemv_ex(const void* A, const void* Wq, const void* scale, i
     // on the matrix cores) is faster where it applies (measured on the
     // Mamba-2 in_proj shape: 21 against 23 us at M = 4, 22 against 49 us at
     // M = 16).
-    if (M >= 4 && skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, scale_format, out, M, N, K, s);
+    if (M >= 4 && skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, scale_format, nullptr, out, M, N, K, s);
     switch (scale_format) {
-        case W8A16_SCALE_BLOCK_F32: return run_gemv<kScaleBlockF32>(A, Wq, scale, out, M, N, K, s);
-        case W8A16_SCALE_ROW_F32: return run_gemv<kScaleRowF32>(A, Wq, scale, out, M, N, K, s);
-        default: return run_gemv<kScaleBlockBf16>(A, Wq, scale, out, M, N, K, s);
+        case W8A16_SCALE_BLOCK_F32: return run_gemv<kScaleBlockF32, false>(A, Wq, scale, out, M, N, K, s);
+        case W8A16_SCALE_ROW_F32: return run_gemv<kScaleRowF32, false>(A, Wq, scale, out, M, N, K, s);
+        default: return run_gemv<kScaleBlockBf16, false>(A, Wq, scale, out, M, N, K, s);
     }
 }
 
 extern "C" int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
                           int64_t M, int64_t N, int64_t K, void* stream) {
     return w8a16_gemv_ex(A, Wq, scale, W8A16_SCALE_BLOCK_BF16, out, M, N, K, stream);
+}
+
+extern "C" int w8a16_gemv_fused(const void* A, const void* gate, const void* norm_weight, float eps,
+                                const void* Wq, const void* scale, const void* residual, void* out,
+                                int64_t M, int64_t N, int64_t K, void* stream) {
+    using namespace w8a16;
+    bool noop = false;
+    int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
+    if (st != W8A16_OK) return st;
+    if (gate && !norm_weight) return W8A16_ERR_ARG;            // a gate belongs to the norm
+    if (norm_weight && (!(eps >= 0.0f) || eps > 3.0e38f)) return W8A16_ERR_ARG;   // also NaN
+    if (noop) return W8A16_OK;
+    if (!fused_fits(M, K)) return W8A16_ERR_SHAPE;
+    if (norm_weight && (!aligned(norm_weight, 16) || (gate && !aligned(gate, 16)))) return W8A16_ERR_ALIGN;
+    const int64_t out_bytes = M * N * 2;
+    if (residual) {
+        if (!aligned(residual, 2)) return W8A16_ERR_ALIGN;
+        if (overlaps(out, out_bytes, residual, out_bytes)) return W8A16_ERR_ALIAS;
+    }
+    if ((norm_weight && overlaps(out, out_bytes, norm_weight, K * 2)) ||
+        (gate && overlaps(out, out_bytes, gate, M * K * 2)))
+        return W8A16_ERR_ALIAS;
+    const Fusion fu{static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(norm_weight),
+                    static_cast<const uint16_t*>(residual), eps};
+    return run_gemv<kScaleBlockBf16, true>(A, Wq, scale, out, M, N, K, static_cast<hipStream_t>(stream), fu);
 }

@@ -59,14 +59,20 @@ inline int check_product_args(const void* A, const void* Wq, const void* scale, 
     return W8A16_OK;
 }
 
+// Checks of the norm arguments (w8a16_norm.hip): shapes, eps, NULL,
+// 16-byte alignment, and `out` [M][K] overlapping an input.
+int check_norm_args(const void* x, const void* gate, const void* weight, float eps, const void* out,
+                    int64_t M, int64_t K, bool* noop);
+
 // Skinny GEMM (w8a16_skinny.hip): 1 <= M <= kSkinnyMaxM rows, K <= kSkinnyMaxK, weights
 // streamed from HBM straight into the matrix-core operands. Arguments as for
 // w8a16_gemm (already checked by the caller); enqueues one kernel on `stream`.
 constexpr int64_t kSkinnyMaxM = 16;
 constexpr int64_t kSkinnyMaxK = 4096;
 inline bool skinny_fits(int64_t M, int64_t K) { return M >= 1 && M <= kSkinnyMaxM && K <= kSkinnyMaxK; }
-int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, void* out, int64_t M, int64_t N,
-                int64_t K, hipStream_t stream);
+// `residual` ([M][N] BF16, or nullptr) adds the residual epilogue.
+int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
+                int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // Launch `kernel` with exactly the argument types of its signature; the HIP
 // launch status becomes W8A16_OK / W8A16_ERR_LAUNCH.

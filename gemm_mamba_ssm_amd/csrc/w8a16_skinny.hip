@@ -62,7 +62,8 @@ __device__ __forceinline__ void wait_vmem() {
 template <int MB, int KB, int D, int MAXW, int SF>
 __global__ void __launch_bounds__(64 * MAXW)
 skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,
-              uint16_t* __restrict__ out, int M, int N, int K, int blocks_per_wg) {
+              const uint16_t* __restrict__ res, uint16_t* __restrict__ out, int M, int N, int K,
+              int blocks_per_wg) {
     constexpr bool kRowScale = SF == kScaleRowF32;
     // Partial tiles of the waves, double-buffered by block parity:
     // [parity][wave][mb][lane] x 4 floats.
@@ -230,7 +231,11 @@ skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, con
         const int row = i / (per_row * 16), rest = i % (per_row * 16);
         const int b = rest / 16, col = rest % 16;
         const int n = (blk0 + b) * kRows + col;
-        if (row < M && n < N) out[static_cast<int64_t>(row) * N + n] = outs[b * 256 * MB + row * 16 + col];
+        if (row < M && n < N) {
+            const int64_t o = static_cast<int64_t>(row) * N + n;
+            const uint16_t y = outs[b * 256 * MB + row * 16 + col];
+            out[o] = res ? residual_add_bits(y, res[o]) : y;      // residual epilogue, if any
+        }
     }
 }
 
@@ -240,8 +245,8 @@ skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, con
 // two k-blocks of activations, at least 4. The grid aims at about 16 resident
 // waves per CU, each workgroup taking a contiguous range of 16-row weight
 // blocks.
-int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, void* out, int64_t M, int64_t N,
-                int64_t K, hipStream_t stream) {
+int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
+                int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M < 1 || M > kSkinnyMaxM) return W8A16_ERR_SHAPE;
     if (!skinny_fits(M, K)) return W8A16_ERR_SHAPE;
     const int kb_max = 2;
@@ -261,13 +266,14 @@ int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, void*
     auto a = static_cast<const uint16_t*>(A);
     auto w = static_cast<const uint8_t*>(Wq);
     auto o = static_cast<uint16_t*>(out);
+    auto r = static_cast<const uint16_t*>(residual);
     switch (fmt) {
         case W8A16_SCALE_BLOCK_BF16:
-            return launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockBf16>, grid, block, stream, a, w, scale, o, m, n, k, p);
+            return launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockBf16>, grid, block, stream, a, w, scale, r, o, m, n, k, p);
         case W8A16_SCALE_BLOCK_F32:
-            return launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockF32>, grid, block, stream, a, w, scale, o, m, n, k, p);
+            return launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockF32>, grid, block, stream, a, w, scale, r, o, m, n, k, p);
         case W8A16_SCALE_ROW_F32:
-            return launch(&skinny_kernel<1, 2, 2, 16, kScaleRowF32>, grid, block, stream, a, w, scale, o, m, n, k, p);
+            return launch(&skinny_kernel<1, 2, 2, 16, kScaleRowF32>, grid, block, stream, a, w, scale, r, o, m, n, k, p);
         default:
             return W8A16_ERR_ARG;
     }

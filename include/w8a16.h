@@ -139,6 +139,54 @@ int w8a16_gemm_ex(const void* A, const void* Wq, const void* scale, int scale_fo
                   int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * Norm prologues and the residual epilogue of the Mamba-2 layer around its
+ * two projections (nemotron_mamba2.rs module docs, forward pass: step 1, RMS
+ * norm scaled by its weight, before in_proj; step 6, the gated norm
+ * rms_norm(y, ssm_norm) * silu(z), before out_proj; step 8, the residual add
+ * after out_proj). The pages give neither epsilon nor a grouping of the
+ * norm: here the norm runs over each whole row of K values and epsilon is an
+ * argument (finite, >= 0; anything else returns W8A16_ERR_ARG):
+ *
+ *   r[m]    = 1 / sqrt( (sum_k x[m][k]^2) / K + eps )
+ *   a[m][k] = bf16( x[m][k] * r[m] * weight[k] [* silu(gate[m][k])] )
+ *   silu(z) = z / (1 + e^-z)
+ *
+ * computed in fp32 with one rounding to BF16 at the end. The residual add
+ * sums two BF16 tensors: out = bf16(residual + bf16(product)).
+ *
+ * w8a16_rmsnorm: a into out, all [M][K] BF16 (x, gate, out 16-byte aligned;
+ * weight [K] BF16, 16-byte aligned; gate may be NULL for the plain norm). M
+ * >= 0, K % 16 == 0, K >= 16. The prefill path: the GEMM then reads `out`.
+ * out must not overlap an input (W8A16_ERR_ALIAS).
+ */
+int w8a16_rmsnorm(const void* x, const void* gate, const void* weight, float eps, void* out,
+                  int64_t M, int64_t K, void* stream);
+
+/*
+ * Decode GEMV with the prologue and epilogue fused (one launch per
+ * projection): A is the layer input x (in_proj, norm_weight set, gate NULL)
+ * or the SSM output y (out_proj, gate = z); norm_weight NULL means no norm
+ * (then gate must be NULL too, else W8A16_ERR_ARG). residual ([M][N] BF16,
+ * 2-byte aligned, or NULL) adds the epilogue; it must not overlap out.
+ * The scale is the BF16 block grid; errors as for w8a16_gemv. Shapes: 1 <= M
+ * <= 4 with K <= 16384, or 5 <= M <= 8 with K <= 8192 (the norm's operands
+ * then fit in registers beside the activations); otherwise W8A16_ERR_SHAPE,
+ * and the two-step form w8a16_rmsnorm + w8a16_gemm_residual applies. Every
+ * M runs the GEMV kernel (the skinny path of w8a16_gemv is not fused).
+ */
+int w8a16_gemv_fused(const void* A, const void* gate, const void* norm_weight, float eps,
+                     const void* Wq, const void* scale, const void* residual, void* out,
+                     int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Prefill GEMM with the residual epilogue: out = bf16(residual +
+ * bf16(A x dequant(Wq)^T)), residual [M][N] BF16, 2-byte aligned, not NULL,
+ * not overlapping out. Everything else as for w8a16_gemm (BF16 block grid).
+ */
+int w8a16_gemm_residual(const void* A, const void* Wq, const void* scale, const void* residual,
+                        void* out, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Dequantize only (a test path that exposes the device E4M3 decode and the
  * block-scale indexing the two entry points above use). out is FP32 [N][K]:
  *   out[n][k] = float(E4M3(Wq[n][k])) * scale[n/128][k/128]

@@ -160,3 +160,71 @@ def test_binding_refuses_wrong_layouts():
         binding.w8a16_gemm(A, W, S)                                    # CPU tensors
     with pytest.raises(ValueError):
         binding.w8a16_dequant(W, S[:, :1])
+
+
+def test_norm_and_fused_rejections():
+    F = FAKE
+    X, G, Wn, O = F, F + (1 << 30), F + (2 << 30), F + (3 << 30)
+    nan = float("nan")
+    # w8a16_rmsnorm(x, gate, weight, eps, out, M, K)
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 4, 8, 0) == binding.ERR_SHAPE          # K < 16
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 4, 264, 0) == binding.ERR_SHAPE          # K % 16
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, -1, 256, 0) == binding.ERR_SHAPE
+    assert binding.rmsnorm_raw(X, G, Wn, nan, O, 4, 256, 0) == binding.ERR_ARG
+    assert binding.rmsnorm_raw(X, G, Wn, -1.0, O, 4, 256, 0) == binding.ERR_ARG
+    assert binding.rmsnorm_raw(X, G, Wn, float("inf"), O, 4, 256, 0) == binding.ERR_ARG
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 0, 256, 0) == binding.OK               # no-op
+    assert binding.rmsnorm_raw(0, G, Wn, 1e-5, O, 4, 256, 0) == binding.ERR_NULL
+    assert binding.rmsnorm_raw(X, G, 0, 1e-5, O, 4, 256, 0) == binding.ERR_NULL
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, 0, 4, 256, 0) == binding.ERR_NULL
+    assert binding.rmsnorm_raw(X + 2, G, Wn, 1e-5, O, 4, 256, 0) == binding.ERR_ALIGN
+    assert binding.rmsnorm_raw(X, G + 2, Wn, 1e-5, O, 4, 256, 0) == binding.ERR_ALIGN
+    assert binding.rmsnorm_raw(X, G, Wn + 8, 1e-5, O, 4, 256, 0) == binding.ERR_ALIGN
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, X + 16, 4, 256, 0) == binding.ERR_ALIAS   # out over x
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, G, 4, 256, 0) == binding.ERR_ALIAS        # out over gate
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, Wn - 16, 4, 256, 0) == binding.ERR_ALIAS  # out reaches weight
+    # w8a16_gemv_fused(A, gate, norm_weight, eps, Wq, scale, residual, out, M, N, K)
+    A, Wq, S = F + (4 << 30), F + (5 << 30), F + (6 << 30)
+    R = F + (7 << 30)
+    fused = binding.gemv_fused_raw
+    assert fused(A, G, 0, 1e-5, Wq, S, R, O, 1, 256, 256, 0) == binding.ERR_ARG       # gate without norm
+    assert fused(A, 0, Wn, nan, Wq, S, R, O, 1, 256, 256, 0) == binding.ERR_ARG
+    assert fused(A, 0, Wn, 1e-5, Wq, S, R, O, 9, 256, 256, 0) == binding.ERR_SHAPE    # M > 8
+    assert fused(A, 0, Wn, 1e-5, Wq, S, R, O, 5, 256, 8192 + 16, 0) == binding.ERR_SHAPE
+    assert fused(A, 0, Wn, 1e-5, Wq, S, R, O, 4, 256, 16384 + 16, 0) == binding.ERR_SHAPE
+    assert fused(A, 0, Wn, 1e-5, Wq, S, R, O, 0, 256, 256, 0) == binding.OK           # no-op
+    assert fused(A, 0, Wn + 8, 1e-5, Wq, S, R, O, 1, 256, 256, 0) == binding.ERR_ALIGN
+    assert fused(A, G + 8, Wn, 1e-5, Wq, S, R, O, 1, 256, 256, 0) == binding.ERR_ALIGN
+    assert fused(A, 0, Wn, 1e-5, Wq, S, R + 1, O, 1, 256, 256, 0) == binding.ERR_ALIGN
+    assert fused(A, 0, Wn, 1e-5, Wq, S, O, O, 1, 256, 256, 0) == binding.ERR_ALIAS    # residual is out
+    assert fused(A, 0, O + 64, 1e-5, Wq, S, R, O, 1, 256, 256, 0) == binding.ERR_ALIAS   # out over norm weight
+    assert fused(A, G, Wn, 1e-5, Wq, S, R, G + 2, 1, 256, 256, 0) == binding.ERR_ALIAS    # out over gate
+    assert fused(A, 0, 0, 1e-5, Wq, S, 0, A, 1, 256, 256, 0) == binding.ERR_ALIAS        # out over A
+    # w8a16_gemm_residual(A, Wq, scale, residual, out, M, N, K)
+    assert binding.gemm_residual_raw(A, Wq, S, 0, O, 4, 256, 256, 0) == binding.ERR_NULL
+    assert binding.gemm_residual_raw(A, Wq, S, R + 1, O, 4, 256, 256, 0) == binding.ERR_ALIGN
+    assert binding.gemm_residual_raw(A, Wq, S, O + 256, O, 4, 256, 256, 0) == binding.ERR_ALIAS
+    assert binding.gemm_residual_raw(A, Wq, S, R, O, 0, 256, 256, 0) == binding.OK
+
+
+def test_binding_refuses_bad_norm_arguments():
+    A, W, S = _cpu_operands(M=2, N=300, K=256)
+    w = torch.ones(256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="weight"):
+        binding.w8a16_rmsnorm(A, w[:128], 1e-5)
+    with pytest.raises(ValueError, match="gate"):
+        binding.w8a16_rmsnorm(A, w, 1e-5, gate=A[:1])
+    with pytest.raises(ValueError, match="eps"):
+        binding.w8a16_rmsnorm(A, w, float("nan"))
+    with pytest.raises(ValueError, match="eps"):
+        binding.w8a16_gemv_fused(A, W, S, norm_weight=w, eps=-1.0)
+    with pytest.raises(ValueError, match="gate needs"):
+        binding.w8a16_gemv_fused(A, W, S, gate=A)
+    with pytest.raises(ValueError, match="residual"):
+        binding.w8a16_gemv_fused(A, W, S, residual=torch.zeros((2, 299), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="M <= 4"):
+        binding.w8a16_gemv_fused(torch.zeros((9, 256), dtype=torch.bfloat16), W, S)
+    with pytest.raises(ValueError, match="residual"):
+        binding.w8a16_gemm_residual(A, W, S, torch.zeros((2, 300), dtype=torch.float32))
+    with pytest.raises(ValueError, match="HIP device"):
+        binding.w8a16_gemm_residual(A, W, S, torch.zeros((2, 300), dtype=torch.bfloat16))
