@@ -22,8 +22,12 @@ each between their own two events. `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workloads. `few_tokens` (outside the timed step)
 reports the same projections at M = 2..16 through the GEMV entry point (the
 multi-sequence decode workloads) and at M = 32..256 through the GEMM.
+`layer_ends` (outside the timed step) times the norm prologues and the
+residual epilogue: fused into the decode GEMV against the unfused chain, and
+the prefill norms and residual GEMM at M = 1024.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-few-tokens]
+                    [--no-layer-ends]
 
 Profile helpers (read rocprofv3 CSV output; no GPU needed):
     python bench.py --summarize-trace <dir>/<name>_kernel_trace.csv
@@ -163,7 +167,7 @@ def summarize_counters(fetch_csv, write_csv, layers=DEFAULT_LAYERS):
     fetch, f_fac = per_launch(fetch_csv, "FETCH_SIZE")
     write, w_fac = per_launch(write_csv, "WRITE_SIZE")
     rec = {"source": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, of "
-                     "`python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-few-tokens --copy-calibration`",
+                     "`python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-few-tokens --no-layer-ends --copy-calibration`",
            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4), "kernels": {}}
     for lab in fetch:
         kind = lab.split("_")[0]
@@ -262,6 +266,114 @@ def few_token_report(projs, device, stream, L, check, reps=10):
     return out
 
 
+def layer_ends_report(projs, device, stream, L, check, reps=10):
+    """Outside the timed step: the layer's norm prologues and residual epilogue
+    around the projections (forward steps 1, 6 and 8 of the Mamba-2 layer).
+
+    Decode (M = 1): in_proj with its RMSNorm fused (w8a16_gemv_fused) against
+    w8a16_rmsnorm + w8a16_gemv; out_proj with the gated norm and the residual
+    fused against w8a16_rmsnorm + w8a16_gemv + a torch BF16 add (the unfused
+    chain). Prefill (M = 1024): the standalone norms (HBM-bound: x, z read
+    once, the activations written once) and the out_proj GEMM with and
+    without the residual epilogue. Weight copies rotate as in the decode step;
+    times are means over `reps` runs of L launches (or chains) between two
+    events, in us."""
+    sh = stream.cuda_stream
+    eps = inputs.NORM_EPS
+    pin, pout = projs
+    K_in, K_out = pin.p_dec.K, pout.p_dec.K
+    x1 = to_dev(inputs.activations(1, K_in, 6001), torch.bfloat16, device)
+    y1 = to_dev(inputs.activations(1, K_out, 6002), torch.bfloat16, device)
+    z1 = to_dev(inputs.activations(1, K_out, 6003), torch.bfloat16, device)
+    w_in = to_dev(inputs.norm_weight(K_in, 6004), torch.bfloat16, device)
+    w_out = to_dev(inputs.norm_weight(K_out, 6005), torch.bfloat16, device)
+    r1 = to_dev(inputs.activations(1, pout.p_dec.N, 6006), torch.bfloat16, device)
+    a_in = torch.empty((1, K_in), dtype=torch.bfloat16, device=device)
+    a_out = torch.empty((1, K_out), dtype=torch.bfloat16, device=device)
+    o_in = torch.empty((1, pin.p_dec.N), dtype=torch.bfloat16, device=device)
+    o_out = torch.empty((1, pout.p_dec.N), dtype=torch.bfloat16, device=device)
+    o_sum = torch.empty_like(o_out)
+
+    def W(p, i):
+        return p.W[i % p.copies].data_ptr(), p.S[i % p.copies].data_ptr()
+
+    def in_fused(i):
+        w, s_ = W(pin, i)
+        check(binding.gemv_fused_raw(x1.data_ptr(), 0, w_in.data_ptr(), eps, w, s_, 0, o_in.data_ptr(),
+                                     1, pin.p_dec.N, K_in, sh), "gemv_fused")
+
+    def in_chain(i):
+        w, s_ = W(pin, i)
+        check(binding.rmsnorm_raw(x1.data_ptr(), 0, w_in.data_ptr(), eps, a_in.data_ptr(), 1, K_in, sh), "rmsnorm")
+        check(binding.gemv_raw(a_in.data_ptr(), w, s_, o_in.data_ptr(), 1, pin.p_dec.N, K_in, sh), "gemv")
+
+    def out_fused(i):
+        w, s_ = W(pout, i)
+        check(binding.gemv_fused_raw(y1.data_ptr(), z1.data_ptr(), w_out.data_ptr(), eps, w, s_, r1.data_ptr(),
+                                     o_out.data_ptr(), 1, pout.p_dec.N, K_out, sh), "gemv_fused")
+
+    def out_chain(i):
+        w, s_ = W(pout, i)
+        check(binding.rmsnorm_raw(y1.data_ptr(), z1.data_ptr(), w_out.data_ptr(), eps, a_out.data_ptr(), 1, K_out,
+                                  sh), "rmsnorm")
+        check(binding.gemv_raw(a_out.data_ptr(), w, s_, o_out.data_ptr(), 1, pout.p_dec.N, K_out, sh), "gemv")
+        torch.add(r1, o_out, out=o_sum)
+
+    def timed(fn):
+        for i in range(L):
+            fn(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for r in range(reps):
+            ev[2 * r].record(stream)
+            for i in range(L):
+                fn(r * L + i)
+            ev[2 * r + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e3 for r in range(reps)]) / L)
+
+    out = {"unit": "us per launch (or per chain of launches)",
+           "decode_in_proj": {"fused_norm_gemv": round(timed(in_fused), 2),
+                              "rmsnorm_then_gemv": round(timed(in_chain), 2)},
+           "decode_out_proj": {"fused_gated_norm_gemv_residual": round(timed(out_fused), 2),
+                               "rmsnorm_then_gemv_then_add": round(timed(out_chain), 2)}}
+
+    # prefill: standalone norms and the residual epilogue at M = 1024
+    Mp = pin.p_pre.M
+    xp = to_dev(inputs.activations(Mp, K_in, 6011), torch.bfloat16, device)
+    yp = to_dev(inputs.activations(Mp, K_out, 6012), torch.bfloat16, device)
+    zp = to_dev(inputs.activations(Mp, K_out, 6013), torch.bfloat16, device)
+    ap_in = torch.empty_like(xp)
+    ap_out = torch.empty_like(yp)
+    rp = to_dev(inputs.activations(Mp, pout.p_pre.N, 6014), torch.bfloat16, device)
+    op = torch.empty((Mp, pout.p_pre.N), dtype=torch.bfloat16, device=device)
+
+    def norm_in(i):
+        check(binding.rmsnorm_raw(xp.data_ptr(), 0, w_in.data_ptr(), eps, ap_in.data_ptr(), Mp, K_in, sh), "rmsnorm")
+
+    def norm_out(i):
+        check(binding.rmsnorm_raw(yp.data_ptr(), zp.data_ptr(), w_out.data_ptr(), eps, ap_out.data_ptr(), Mp, K_out,
+                                  sh), "rmsnorm")
+
+    def gemm_plain(i):
+        w, s_ = W(pout, i)
+        check(binding.gemm_raw(ap_out.data_ptr(), w, s_, op.data_ptr(), Mp, pout.p_pre.N, K_out, sh), "gemm")
+
+    def gemm_res(i):
+        w, s_ = W(pout, i)
+        check(binding.gemm_residual_raw(ap_out.data_ptr(), w, s_, rp.data_ptr(), op.data_ptr(), Mp, pout.p_pre.N,
+                                        K_out, sh), "gemm_residual")
+
+    t_ni, t_no = timed(norm_in), timed(norm_out)
+    b_ni = 2 * Mp * K_in * 2 + 2 * K_in              # x read, a written, weight
+    b_no = 3 * Mp * K_out * 2 + 2 * K_out            # y, z read, a written, weight
+    out["prefill_rmsnorm_in"] = {"us": round(t_ni, 2), "GB/s": round(b_ni / t_ni / 1e3, 1),
+                                 "frac": round(b_ni / t_ni / 1e3 / HBM_PEAK_GBS, 4)}
+    out["prefill_gated_rmsnorm_out"] = {"us": round(t_no, 2), "GB/s": round(b_no / t_no / 1e3, 1),
+                                        "frac": round(b_no / t_no / 1e3 / HBM_PEAK_GBS, 4)}
+    out["prefill_out_proj_gemm"] = {"plain": round(timed(gemm_plain), 2), "with_residual": round(timed(gemm_res), 2)}
+    return out
+
+
 def cpu_baseline(budget_s: float):
     """Time the CPU oracle on a bounded sample of the same two workloads."""
     import oracle
@@ -310,6 +422,8 @@ def main():
     ap.add_argument("--no-few-tokens", action="store_true",
                     help="skip the few-token report (profiler runs: keeps the dispatch order that "
                          "--summarize-trace / --summarize-counters label)")
+    ap.add_argument("--no-layer-ends", action="store_true",
+                    help="skip the norm prologue / residual epilogue timings (profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--layers", type=int, default=DEFAULT_LAYERS, help="decode layers (weight copies) per step")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -374,6 +488,7 @@ def main():
     wall = time.perf_counter() - t0
 
     few = None if args.no_few_tokens else few_token_report(projs, device, stream, L, check)
+    ends = None if args.no_layer_ends else layer_ends_report(projs, device, stream, L, check)
 
     if args.copy_calibration:
         src = torch.empty(CALIBRATION_BYTES // 4, dtype=torch.float32, device=device)   # read once, written once
@@ -426,6 +541,7 @@ def main():
                              measured_traffic("gemm", "gemm_in_proj")),
         },
         "few_tokens": few,
+        "layer_ends": ends,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget),
     }
     print(json.dumps(rec), flush=True)

@@ -71,7 +71,12 @@ __device__ __forceinline__ void butterfly(float (&v)[P], int lane) {
     }
 }
 
-template <int MR, int J, int RB, int SF, bool FUSED>
+// What a kernel fuses around the product (w8a16_gemv_fused): nothing (the
+// plain GEMV), the residual epilogue only, or the RMSNorm / gated RMSNorm
+// prologue (each with the residual epilogue when one is passed).
+constexpr int kFuseNone = 0, kFuseResidual = 1, kFuseNorm = 2, kFuseGated = 3;
+
+template <int MR, int J, int RB, int SF, int FU>
 struct Gemv {
     static constexpr int V = RB * MR;          // partial sums per lane per group
     static constexpr int P = pow2_ceil(V);     // padded to a power of two for the butterfly
@@ -106,7 +111,7 @@ struct Gemv {
     // The output element o: BF16 of the sum, or the residual epilogue.
     __device__ static __forceinline__ void store(uint16_t* __restrict__ out, const uint16_t* __restrict__ res,
                                                  int64_t o, float val) {
-        if constexpr (FUSED)
+        if constexpr (FU != kFuseNone)
             if (res) {
                 out[o] = residual_out(val, res[o]);
                 return;
@@ -166,68 +171,109 @@ struct Gemv {
     }
 };
 
-// Normalize the activations a lane holds (rows of MR, chunks kch[j]) in
-// place: a = bf16(x * r * weight [* silu(gate)]), r from the row's sum of
-// squares over all K, reduced over the wave, then over the waves in order.
-template <int MR, int J>
-__device__ __forceinline__ void norm_prologue(uint32_t (&a)[MR][J][8], const Fusion& fu, int K,
-                                              const int (&kch)[J], const bool (&kvalid)[J],
-                                              int lane, int wave, int nwaves) {
-    __shared__ float ssq[kMaxWaves][16];
-    float r[MR];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-        float ss = 0.0f;
+// The norm prologue on the activations a lane holds (rows of MR, chunks
+// kch[j]), in place: a = bf16(x * r * weight [* silu(gate)]), r from the
+// row's sum of squares over all K, reduced over the wave, then over the
+// waves in order. issue() loads the norm weight (and, for one or two rows,
+// the gate) while registers allow; the kernel calls it before the first
+// weight group's loads, so that waiting for the activations and these
+// operands never waits for the weight stream, and the reduction overlaps
+// the weights' HBM latency.
+template <int MR, int J, bool GATED>
+struct NormOps {
+    static constexpr bool kEarlyGate = GATED && MR * J <= 2, kEarlyWeight = MR * J < 8;
+    u32x4_t wv[J][2];
+    u32x4_t gv[kEarlyGate ? MR : 1][J][2];
+
+    __device__ __forceinline__ void load_weight(const Fusion& fu, const int (&kch)[J], const bool (&kvalid)[J],
+                                                int j) {
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        wv[j][0] = kvalid[j] ? load16(fu.weight + kch[j]) : zero;
+        wv[j][1] = kvalid[j] ? load16(fu.weight + kch[j] + 8) : zero;
+    }
+
+    __device__ __forceinline__ void issue(const Fusion& fu, int K, const int (&kch)[J], const bool (&kvalid)[J]) {
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            ss += sumsq8(u32x4_t{a[m][j][0], a[m][j][1], a[m][j][2], a[m][j][3]});
-            ss += sumsq8(u32x4_t{a[m][j][4], a[m][j][5], a[m][j][6], a[m][j][7]});
+            if constexpr (kEarlyWeight) load_weight(fu, kch, kvalid, j);
+            if constexpr (kEarlyGate)
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    const uint16_t* g = fu.gate + static_cast<int64_t>(m) * K + kch[j];
+                    gv[m][j][0] = kvalid[j] ? load16(g) : zero;
+                    gv[m][j][1] = kvalid[j] ? load16(g + 8) : zero;
+                }
         }
-        r[m] = wave_sum(ss);
     }
-    if (lane == 0)
-#pragma unroll
-        for (int m = 0; m < MR; ++m) ssq[wave][m] = r[m];
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-        float t = 0.0f;
-        for (int w = 0; w < nwaves; ++w) t += ssq[w][m];
-        r[m] = rms_factor(t, K, fu.eps);
-    }
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        if (!kvalid[j]) continue;
-        const u32x4_t wl = load16(fu.weight + kch[j]), wh = load16(fu.weight + kch[j] + 8);
+
+    __device__ __forceinline__ void apply(uint32_t (&a)[MR][J][8], const Fusion& fu, int K, const int (&kch)[J],
+                                          const bool (&kvalid)[J], int lane, int wave, int nwaves) {
+        __shared__ float ssq[kMaxWaves][16];
+        float r[MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-            const u32x4_t xl = {a[m][j][0], a[m][j][1], a[m][j][2], a[m][j][3]};
-            const u32x4_t xh = {a[m][j][4], a[m][j][5], a[m][j][6], a[m][j][7]};
-            u32x4_t nl, nh;
-            if (fu.gate) {
-                const uint16_t* g = fu.gate + static_cast<int64_t>(m) * K + kch[j];
-                nl = norm8<true>(xl, wl, load16(g), r[m]);
-                nh = norm8<true>(xh, wh, load16(g + 8), r[m]);
-            } else {
-                nl = norm8<false>(xl, wl, zero, r[m]);
-                nh = norm8<false>(xh, wh, zero, r[m]);
-            }
+            float ss = 0.0f;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                a[m][j][t] = nl[t];
-                a[m][j][4 + t] = nh[t];
+            for (int j = 0; j < J; ++j) {
+                ss += sumsq8(u32x4_t{a[m][j][0], a[m][j][1], a[m][j][2], a[m][j][3]});
+                ss += sumsq8(u32x4_t{a[m][j][4], a[m][j][5], a[m][j][6], a[m][j][7]});
+            }
+            r[m] = wave_sum(ss);
+        }
+        if (lane == 0)
+#pragma unroll
+            for (int m = 0; m < MR; ++m) ssq[wave][m] = r[m];
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            float t = 0.0f;
+            for (int w = 0; w < nwaves; ++w) t += ssq[w][m];
+            r[m] = rms_factor(t, K, fu.eps);
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            if (!kvalid[j]) continue;
+            if constexpr (!kEarlyWeight) load_weight(fu, kch, kvalid, j);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const u32x4_t xl = {a[m][j][0], a[m][j][1], a[m][j][2], a[m][j][3]};
+                const u32x4_t xh = {a[m][j][4], a[m][j][5], a[m][j][6], a[m][j][7]};
+                u32x4_t nl, nh;
+                if constexpr (GATED) {
+                    u32x4_t gl, gh;
+                    if constexpr (kEarlyGate) {
+                        gl = gv[m][j][0];
+                        gh = gv[m][j][1];
+                    } else {
+                        const uint16_t* g = fu.gate + static_cast<int64_t>(m) * K + kch[j];
+                        gl = load16(g);
+                        gh = load16(g + 8);
+                    }
+                    nl = norm8<true>(xl, wv[j][0], gl, r[m]);
+                    nh = norm8<true>(xh, wv[j][1], gh, r[m]);
+                } else {
+                    const u32x4_t zero = {0u, 0u, 0u, 0u};
+                    nl = norm8<false>(xl, wv[j][0], zero, r[m]);
+                    nh = norm8<false>(xh, wv[j][1], zero, r[m]);
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    a[m][j][t] = nl[t];
+                    a[m][j][4 + t] = nh[t];
+                }
             }
         }
     }
-}
+};
 
-template <int MR, int J, int RB, int SF, bool FUSED>
+template <int MR, int J, int RB, int SF, int FU>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             const void* __restrict__ S, uint16_t* __restrict__ out,
             int N, int K, int groups_per_block, Fusion fu) {
-    using G = Gemv<MR, J, RB, SF, FUSED>;
+    using G = Gemv<MR, J, RB, SF, FU>;
+    constexpr bool kNorm = FU == kFuseNorm || FU == kFuseGated;
     __shared__ float red[2][kMaxWaves][G::V];
 
     const int lane = threadIdx.x & 63;
@@ -248,8 +294,10 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
         kvalid[j] = kch[j] < K;
     }
 
+    // The first group's weights go first (the activations arrive from L2
+    // meanwhile), except with a norm prologue, which must not wait for them.
     typename G::Regs ra, rb;
-    G::load(ra, W, S, g_begin, N, K, k_blocks, kch, kvalid);
+    if constexpr (!kNorm) G::load(ra, W, S, g_begin, N, K, k_blocks, kch, kvalid);
 
     // Activations of this lane's chunks, as packed BF16 pairs (k, k+1).
     uint32_t a[MR][J][8];
@@ -270,11 +318,13 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             }
         }
 
-    const uint16_t* res = nullptr;
-    if constexpr (FUSED) {
-        if (fu.weight) norm_prologue<MR, J>(a, fu, K, kch, kvalid, lane, wave, nwaves);
-        res = fu.residual;
+    if constexpr (kNorm) {
+        NormOps<MR, J, FU == kFuseGated> no;
+        no.issue(fu, K, kch, kvalid);
+        G::load(ra, W, S, g_begin, N, K, k_blocks, kch, kvalid);
+        no.apply(a, fu, K, kch, kvalid, lane, wave, nwaves);
     }
+    const uint16_t* res = FU != kFuseNone ? fu.residual : nullptr;
 
     int parity = 0;
     for (int g = g_begin; g < g_end; g += 2) {
@@ -302,7 +352,7 @@ constexpr int rows_per_group(int mr, int j) {
     return rb;
 }
 
-template <int MR, int J, int SF, bool FU>
+template <int MR, int J, int SF, int FU>
 gemv_fn pick_j() {
     return &gemv_kernel<MR, J, rows_per_group(MR, J), SF, FU>;
 }
@@ -316,9 +366,9 @@ inline bool fused_fits(int64_t M, int64_t K) {
                                                : M <= kFusedMaxM && K <= kWaveK * kMaxWaves);
 }
 
-template <int MR, int SF, bool FU>
+template <int MR, int SF, int FU>
 gemv_fn pick(int j) {
-    if constexpr (max_chunks(MR) >= 2 && (!FU || MR <= kFusedMaxMTwoChunks))
+    if constexpr (max_chunks(MR) >= 2 && (FU == kFuseNone || MR <= kFusedMaxMTwoChunks))
         if (j == 2) return pick_j<MR, 2, SF, FU>();
     return pick_j<MR, 1, SF, FU>();
 }
@@ -328,7 +378,7 @@ struct Choice {
     int rows_per_group;
 };
 
-template <int MR, int SF, bool FU>
+template <int MR, int SF, int FU>
 Choice choose(int j) {
     return {pick<MR, SF, FU>(j), j == 2 ? rows_per_group(MR, 2) : rows_per_group(MR, 1)};
 }
@@ -336,9 +386,9 @@ Choice choose(int j) {
 template <int SF>
 Choice select_plain(int mr, int j);
 
-template <int SF, bool FU>
+template <int SF, int FU>
 Choice select_kernel(int mr, int j) {
-    if constexpr (FU) {
+    if constexpr (FU != kFuseNone) {
         switch (mr) {
             case 1: return choose<1, SF, FU>(j);
             case 2: return choose<2, SF, FU>(j);
@@ -357,28 +407,28 @@ Choice select_kernel(int mr, int j) {
 template <int SF>
 Choice select_plain(int mr, int j) {
     switch (mr) {
-        case 1: return choose<1, SF, false>(j);
-        case 2: return choose<2, SF, false>(j);
-        case 3: return choose<3, SF, false>(j);
-        case 4: return choose<4, SF, false>(j);
-        case 5: return choose<5, SF, false>(j);
-        case 6: return choose<6, SF, false>(j);
-        case 7: return choose<7, SF, false>(j);
-        case 8: return choose<8, SF, false>(j);
-        case 9: return choose<9, SF, false>(j);
-        case 10: return choose<10, SF, false>(j);
-        case 11: return choose<11, SF, false>(j);
-        case 12: return choose<12, SF, false>(j);
-        case 13: return choose<13, SF, false>(j);
-        case 14: return choose<14, SF, false>(j);
-        case 15: return choose<15, SF, false>(j);
-        default: return choose<16, SF, false>(j);
+        case 1: return choose<1, SF, kFuseNone>(j);
+        case 2: return choose<2, SF, kFuseNone>(j);
+        case 3: return choose<3, SF, kFuseNone>(j);
+        case 4: return choose<4, SF, kFuseNone>(j);
+        case 5: return choose<5, SF, kFuseNone>(j);
+        case 6: return choose<6, SF, kFuseNone>(j);
+        case 7: return choose<7, SF, kFuseNone>(j);
+        case 8: return choose<8, SF, kFuseNone>(j);
+        case 9: return choose<9, SF, kFuseNone>(j);
+        case 10: return choose<10, SF, kFuseNone>(j);
+        case 11: return choose<11, SF, kFuseNone>(j);
+        case 12: return choose<12, SF, kFuseNone>(j);
+        case 13: return choose<13, SF, kFuseNone>(j);
+        case 14: return choose<14, SF, kFuseNone>(j);
+        case 15: return choose<15, SF, kFuseNone>(j);
+        default: return choose<16, SF, kFuseNone>(j);
     }
 }
 
 // The launch of the GEMV for scale format SF, fused or not (arguments
 // checked).
-template <int SF, bool FU>
+template <int SF, int FU>
 int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
              hipStream_t stream, Fusion fu = Fusion{nullptr, nullptr, nullptr, 0.0f}) {
     const int mr = static_cast<int>(M);
@@ -428,9 +478,9 @@ extern "C" int w8a16_gemv_ex(const void* A, const void* Wq, const void* scale, i
     // M = 16).
     if (M >= 4 && skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, scale_format, nullptr, out, M, N, K, s);
     switch (scale_format) {
-        case W8A16_SCALE_BLOCK_F32: return run_gemv<kScaleBlockF32, false>(A, Wq, scale, out, M, N, K, s);
-        case W8A16_SCALE_ROW_F32: return run_gemv<kScaleRowF32, false>(A, Wq, scale, out, M, N, K, s);
-        default: return run_gemv<kScaleBlockBf16, false>(A, Wq, scale, out, M, N, K, s);
+        case W8A16_SCALE_BLOCK_F32: return run_gemv<kScaleBlockF32, kFuseNone>(A, Wq, scale, out, M, N, K, s);
+        case W8A16_SCALE_ROW_F32: return run_gemv<kScaleRowF32, kFuseNone>(A, Wq, scale, out, M, N, K, s);
+        default: return run_gemv<kScaleBlockBf16, kFuseNone>(A, Wq, scale, out, M, N, K, s);
     }
 }
 
@@ -461,5 +511,8 @@ extern "C" int w8a16_gemv_fused(const void* A, const void* gate, const void* nor
         return W8A16_ERR_ALIAS;
     const Fusion fu{static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(norm_weight),
                     static_cast<const uint16_t*>(residual), eps};
-    return run_gemv<kScaleBlockBf16, true>(A, Wq, scale, out, M, N, K, static_cast<hipStream_t>(stream), fu);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gate) return run_gemv<kScaleBlockBf16, kFuseGated>(A, Wq, scale, out, M, N, K, s, fu);
+    if (norm_weight) return run_gemv<kScaleBlockBf16, kFuseNorm>(A, Wq, scale, out, M, N, K, s, fu);
+    return run_gemv<kScaleBlockBf16, kFuseResidual>(A, Wq, scale, out, M, N, K, s, fu);
 }

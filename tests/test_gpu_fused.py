@@ -76,7 +76,10 @@ def check_norm_bits(got, want, what):
 # --- standalone norm ------------------------------------------------------------
 
 @pytest.mark.parametrize("gated", [False, True])
-@pytest.mark.parametrize("M,K", [(1, 4096), (3, 8192), (1024, 4096), (5, 16), (2, 16400), (17, 272)])
+# K picks the kernel: up to 2048 / 4096 / 8192 / 16384 values hold 1 / 2 / 4 / 8
+# chunks per thread in registers; longer rows loop over the row twice.
+@pytest.mark.parametrize("M,K", [(1, 4096), (3, 8192), (1024, 4096), (5, 16), (2, 16400), (17, 272),
+                                 (2, 16384), (4, 12288), (3, 2064)])
 def test_rmsnorm(dev, gated, M, K):
     say(f"rmsnorm gated={gated} M={M} K={K}")
     x = inputs.activations(M, K, 3100 + K)
