@@ -27,6 +27,11 @@ Norm inputs: the layer input, the gate z and the residual are drawn like A
 (N(0, 1) rounded to BF16); a norm weight is ``1 + 0.1 * N(0, 1)`` rounded to
 BF16; epsilon is ``NORM_EPS``.
 
+Mamba-2 decode-step inputs (``MAMBA2_4K`` dimensions): the xBC row and dt_raw
+are drawn like A; conv weights N(0, 0.5) and bias N(0, 0.1) in BF16; conv
+states hold earlier BF16 inputs as float32; SSM states N(0, 0.1) float32;
+``ssm_params`` draws a_log, D and dt_bias (float32) in the usual ranges.
+
 The FP32 scale formats (``weights_fmt``) use the same draws; ``block_f32``
 keeps ``max|w| / 448`` of each block in float32 (no BF16 rounding), and
 ``row_f32`` takes it over each whole weight row instead, as a float32 [N]
@@ -131,6 +136,45 @@ SCALE_FORMATS = ("block_bf16", "block_f32", "row_f32")
 # Norm epsilon of the layer's RMSNorms (the pages do not give it; 1e-5 is the
 # usual value for this model family).
 NORM_EPS = 1e-5
+
+
+# Mamba-2 mixer of the hidden-4096 layer: d_inner = heads * head_dim = 8192,
+# xBC = d_inner + 2 * groups * state = 10240 channels, and the in_proj output
+# row [z | xBC | dt] is 8192 + 10240 + 128 = 18560 wide (IN_4K's N).
+MAMBA2_4K = dict(heads=128, head_dim=64, state=128, groups=8, d_conv=4)
+
+
+def ssm_params(heads: int, seed: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(a_log, d_param, dt_bias), float32 [heads]: a_log = log U(1, 16) (so
+    A = -exp(a_log) lies in [-16, -1]), D = 1 + 0.1 * N(0, 1), and dt_bias ~
+    U(-6.9, -2.25) (softplus of it lies between about 0.001 and 0.1)."""
+    rng = np.random.default_rng(seed)
+    a_log = np.log(rng.uniform(1.0, 16.0, heads)).astype(np.float32)
+    d_param = (1.0 + 0.1 * rng.standard_normal(heads)).astype(np.float32)
+    dt_bias = rng.uniform(-6.9, -2.25, heads).astype(np.float32)
+    return a_log, d_param, dt_bias
+
+
+def conv_params(dim: int, d_conv: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """(weight [dim, d_conv], bias [dim]) as BF16 bits: N(0, 0.5) and N(0, 0.1)."""
+    rng = np.random.default_rng(seed)
+    w = (0.5 * rng.standard_normal((dim, d_conv))).astype(np.float32)
+    b = (0.1 * rng.standard_normal(dim)).astype(np.float32)
+    return _f32_to_bf16_bits(w), _f32_to_bf16_bits(b)
+
+
+def conv_state(B: int, dim: int, d_conv: int, seed: int) -> np.ndarray:
+    """A conv state of earlier inputs, float32 [B, dim, d_conv]: N(0, 1) values
+    rounded to BF16 (the inputs it holds are BF16)."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((B, dim, d_conv), dtype=np.float32)
+    return _bf16_bits_to_f32(_f32_to_bf16_bits(v)).reshape(B, dim, d_conv).copy()
+
+
+def ssm_state(B: int, heads: int, head_dim: int, state: int, seed: int) -> np.ndarray:
+    """An SSM state, float32 [B, heads, head_dim, state] ~ N(0, 0.1)."""
+    rng = np.random.default_rng(seed)
+    return (0.1 * rng.standard_normal((B, heads, head_dim, state), dtype=np.float32)).astype(np.float32)
 
 
 def norm_weight(K: int, seed: int) -> np.ndarray:

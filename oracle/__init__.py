@@ -85,6 +85,13 @@ def _load():
     lib.oracle_rmsnorm.argtypes = [P, P, P, ctypes.c_double, I64, I64, P, P]
     lib.oracle_residual_add.restype = None
     lib.oracle_residual_add.argtypes = [P, P, I64, P]
+    D = ctypes.c_double
+    lib.oracle_conv1d_update.restype = None
+    lib.oracle_conv1d_update.argtypes = [P, P, I64, P, P, I64, I64, I64, P, P]
+    lib.oracle_softplus.restype = D
+    lib.oracle_softplus.argtypes = [D]
+    lib.oracle_ssm_decode.restype = None
+    lib.oracle_ssm_decode.argtypes = [P, P, I64, P, I64, P, P, P, I64, I64, I64, I64, I64, D, D, P, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -242,6 +249,70 @@ def residual_add(residual, ref) -> np.ndarray:
     out = np.empty(r.shape, np.uint16)
     _load().oracle_residual_add(_ptr(r), _ptr(f), r.size, _ptr(out))
     return out
+
+
+def softplus(v: float) -> float:
+    """log(1 + e^v) in fp64."""
+    return float(_load().oracle_softplus(float(v)))
+
+
+def conv1d_update(state, x, weight, bias, ld_x: int | None = None):
+    """One conv1d update step (nemotron_mamba2.rs module docs, forward step 3).
+
+    state: float64 [B, dim, d_conv], updated in place (oldest input first);
+    x: BF16 bits [B, ld_x] (the first dim channels are used); weight: BF16
+    [dim, d_conv]; bias: BF16 [dim]. Returns (exact fp64 [B, dim], BF16 bits)."""
+    if not (isinstance(state, np.ndarray) and state.dtype == np.float64 and state.flags.c_contiguous
+            and state.ndim == 3):
+        raise TypeError("state must be a C-contiguous float64 [B, dim, d_conv] array (updated in place)")
+    Bn, dim, d_conv = state.shape
+    x = _c(x, np.uint16)
+    w = _c(weight, np.uint16)
+    bi = _c(bias, np.uint16)
+    ld = x.shape[1] if ld_x is None else ld_x
+    if x.ndim != 2 or x.shape[0] != Bn or x.shape[1] < dim or ld != x.shape[1]:
+        raise ValueError(f"x must be [B, >= dim] with ld_x its row length, got {x.shape} (ld_x {ld})")
+    if w.shape != (dim, d_conv) or bi.shape != (dim,):
+        raise ValueError(f"weight must be {(dim, d_conv)} and bias {(dim,)}, got {w.shape}, {bi.shape}")
+    exact = np.empty((Bn, dim), np.float64)
+    bits = np.empty((Bn, dim), np.uint16)
+    _load().oracle_conv1d_update(_ptr(state), _ptr(x), ld, _ptr(w), _ptr(bi), Bn, dim, d_conv,
+                                 _ptr(exact), _ptr(bits))
+    return exact, bits
+
+
+def ssm_decode(hstate, xbc, dt_raw, a_log, d_param, dt_bias, groups: int, dt_min: float = 1e-9,
+               dt_max: float = 1e9):
+    """One Mamba-2 SSM decode step (nemotron_mamba2.rs module docs, forward
+    steps 4 and 5; `ssm_decode` argument list).
+
+    hstate: float64 [B, heads, head_dim, state], updated in place; xbc: BF16
+    bits [B, ld] holding x | B | C from column 0; dt_raw: BF16 bits [B, >=
+    heads]; a_log, d_param, dt_bias: float32 [heads]. Returns (y exact fp64
+    [B, heads*head_dim], y BF16 bits, den)."""
+    if not (isinstance(hstate, np.ndarray) and hstate.dtype == np.float64 and hstate.flags.c_contiguous
+            and hstate.ndim == 4):
+        raise TypeError("hstate must be a C-contiguous float64 [B, heads, head_dim, state] array")
+    Bn, heads, hd, st = hstate.shape
+    if groups < 1 or heads % groups:
+        raise ValueError(f"heads ({heads}) must be a multiple of groups ({groups})")
+    xbc = _c(xbc, np.uint16)
+    dt = _c(dt_raw, np.uint16)
+    need = heads * hd + 2 * groups * st
+    if xbc.ndim != 2 or xbc.shape[0] != Bn or xbc.shape[1] < need:
+        raise ValueError(f"xbc must be [B, >= {need}], got {xbc.shape}")
+    if dt.ndim != 2 or dt.shape[0] != Bn or dt.shape[1] < heads:
+        raise ValueError(f"dt_raw must be [B, >= {heads}], got {dt.shape}")
+    al, dp, db = (_c(v, np.float32) for v in (a_log, d_param, dt_bias))
+    if al.shape != (heads,) or dp.shape != (heads,) or db.shape != (heads,):
+        raise ValueError("a_log, d_param and dt_bias must be float32 [heads]")
+    y = np.empty((Bn, heads * hd), np.float64)
+    bits = np.empty((Bn, heads * hd), np.uint16)
+    den = np.empty((Bn, heads * hd), np.float64)
+    _load().oracle_ssm_decode(_ptr(hstate), _ptr(xbc), xbc.shape[1], _ptr(dt), dt.shape[1], _ptr(al), _ptr(dp),
+                              _ptr(db), Bn, heads, hd, st, groups, float(dt_min), float(dt_max),
+                              _ptr(y), _ptr(bits), _ptr(den))
+    return y, bits, den
 
 
 def num_threads() -> int:

@@ -252,6 +252,93 @@ void oracle_residual_add(const uint16_t* residual, const double* ref, int64_t n,
     }
 }
 
+/*
+ * The Mamba-2 decode step between the two projections (nemotron_mamba2.rs
+ * module docs, forward steps 3 to 5: the conv1d update on xBC with bias and
+ * fused SiLU, the split into x, B and C, the SSM state update and output; the
+ * argument lists of `conv1d_update_biased` and `ssm_decode` in that listing).
+ * The pages do not write the formulas out; these are the standard Mamba-2
+ * recurrence for one token (the reading is stated in the design notes).
+ *
+ * Conv1d update, for each sequence b and channel c, with a state of the last
+ * d_conv inputs (oldest first):
+ *   state[c][w] <- state[c][w + 1] (w < d_conv - 1), state[c][d_conv-1] <- x[c]
+ *   out[c] = silu( sum_w state[c][w] * weight[c][w] + bias[c] )
+ */
+void oracle_conv1d_update(double* state, const uint16_t* x, int64_t ld_x, const uint16_t* weight,
+                          const uint16_t* bias, int64_t B, int64_t dim, int64_t d_conv,
+                          double* out_exact, uint16_t* out_bits)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < dim; ++c) {
+            double* s = state + (b * dim + c) * d_conv;
+            for (int64_t w = 0; w + 1 < d_conv; ++w)
+                s[w] = s[w + 1];
+            s[d_conv - 1] = oracle_bf16_value(x[b * ld_x + c]);
+            double acc = oracle_bf16_value(bias[c]);
+            for (int64_t w = 0; w < d_conv; ++w)
+                acc += s[w] * oracle_bf16_value(weight[c * d_conv + w]);
+            double v = oracle_silu(acc);
+            out_exact[b * dim + c] = v;
+            out_bits[b * dim + c] = oracle_bf16_rne(v);
+        }
+}
+
+/* softplus(v) = log(1 + e^v). */
+double oracle_softplus(double v)
+{
+    return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));
+}
+
+/*
+ * SSM decode, for each sequence b and head h (group g = h / (heads / groups)),
+ * with the conv output row xbc = [x (heads * head_dim) | B (groups * state) |
+ * C (groups * state)] and the state h[b][h][p][n]:
+ *   dt   = clamp( softplus(dt_raw[h] + dt_bias[h]), dt_min, dt_max )
+ *   a    = -exp(a_log[h]),  dA = exp(dt * a)
+ *   h[p][n] <- dA * h[p][n] + dt * B[g][n] * x[h][p]
+ *   y[h][p] = sum_n C[g][n] * h[p][n] + D[h] * x[h][p]
+ * y_den receives sum_n |C[g][n] * h[p][n]| + |D[h] * x[h][p]| (for the parity
+ * tolerance).
+ */
+void oracle_ssm_decode(double* hs, const uint16_t* xbc, int64_t ld_xbc, const uint16_t* dt_raw,
+                       int64_t ld_dt, const float* a_log, const float* d_param, const float* dt_bias,
+                       int64_t B, int64_t heads, int64_t head_dim, int64_t st, int64_t groups,
+                       double dt_min, double dt_max, double* y_exact, uint16_t* y_bits, double* y_den)
+{
+    int64_t d_inner = heads * head_dim, per_group = heads / groups;
+    for (int64_t b = 0; b < B; ++b) {
+        const uint16_t* row = xbc + b * ld_xbc;
+        for (int64_t h = 0; h < heads; ++h) {
+            int64_t g = h / per_group;
+            double dt = oracle_softplus(oracle_bf16_value(dt_raw[b * ld_dt + h]) + (double)dt_bias[h]);
+            if (dt < dt_min) dt = dt_min;
+            if (dt > dt_max) dt = dt_max;
+            double dA = exp(dt * -exp((double)a_log[h]));
+            const uint16_t* Bg = row + d_inner + g * st;
+            const uint16_t* Cg = row + d_inner + groups * st + g * st;
+            for (int64_t p = 0; p < head_dim; ++p) {
+                double xv = oracle_bf16_value(row[h * head_dim + p]);
+                double* hp = hs + ((b * heads + h) * head_dim + p) * st;
+                double y = 0.0, den = 0.0;
+                for (int64_t n = 0; n < st; ++n) {
+                    hp[n] = dA * hp[n] + dt * oracle_bf16_value(Bg[n]) * xv;
+                    double t = oracle_bf16_value(Cg[n]) * hp[n];
+                    y += t;
+                    den += fabs(t);
+                }
+                double skip = (double)d_param[h] * xv;
+                y += skip;
+                den += fabs(skip);
+                int64_t o = b * d_inner + h * head_dim + p;
+                y_exact[o] = y;
+                y_bits[o] = oracle_bf16_rne(y);
+                y_den[o] = den;
+            }
+        }
+    }
+}
+
 /* Element-wise array forms of the scalar conversions above. */
 void oracle_e4m3_values(const uint8_t* codes, int64_t n, double* out)
 {
