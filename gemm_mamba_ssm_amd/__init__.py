@@ -10,6 +10,8 @@ kernels in ``libw8a16.so`` (C ABI: ``include/w8a16.h``).
 * ``w8a16_dequant`` - dequantize only (test path for the decode and scale index)
 * ``w8a16_rmsnorm``, ``w8a16_gemv_fused``, ``w8a16_gemm_residual`` - the
   layer's norm prologues and residual epilogue around the projections
+* ``w8a16_conv1d_update``, ``w8a16_ssm_decode`` - the Mamba-2 decode step
+  between the projections
 """
-from .binding import (W8A16Error, w8a16_dequant, w8a16_gemm, w8a16_gemm_residual,  # noqa: F401
-                      w8a16_gemv, w8a16_gemv_fused, w8a16_rmsnorm)
+from .binding import (W8A16Error, w8a16_conv1d_update, w8a16_dequant, w8a16_gemm,  # noqa: F401
+                      w8a16_gemm_residual, w8a16_gemv, w8a16_gemv_fused, w8a16_rmsnorm, w8a16_ssm_decode)

@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_PKG, "libw8a16.so")
 BLOCK = 128
 
 EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_gemv_ex", "w8a16_gemm_ex", "w8a16_rmsnorm", "w8a16_gemv_fused",
-           "w8a16_gemm_residual", "w8a16_dequant", "w8a16_strerror")
+           "w8a16_gemm_residual", "w8a16_conv1d_update", "w8a16_ssm_decode", "w8a16_dequant", "w8a16_strerror")
 
 # enum w8a16_scale_format
 SCALE_BLOCK_BF16, SCALE_BLOCK_F32, SCALE_ROW_F32 = 0, 1, 2
@@ -79,6 +79,10 @@ def load() -> ctypes.CDLL:
     lib.w8a16_gemv_fused.argtypes = [P, P, P, F, P, P, P, P, I64, I64, I64, P]
     lib.w8a16_gemm_residual.restype = ctypes.c_int
     lib.w8a16_gemm_residual.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+    lib.w8a16_conv1d_update.restype = ctypes.c_int
+    lib.w8a16_conv1d_update.argtypes = [P, P, I64, P, P, P, I64, I64, I64, I64, P]
+    lib.w8a16_ssm_decode.restype = ctypes.c_int
+    lib.w8a16_ssm_decode.argtypes = [P, P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, I64, I64, F, F, P]
     lib.w8a16_dequant.restype = ctypes.c_int
     lib.w8a16_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.w8a16_strerror.restype = ctypes.c_char_p
@@ -124,6 +128,18 @@ def gemv_fused_raw(A: int, gate: int, norm_weight: int, eps: float, Wq: int, sca
 def gemm_residual_raw(A: int, Wq: int, scale: int, residual: int, out: int, M: int, N: int, K: int,
                       stream: int = 0) -> int:
     return load().w8a16_gemm_residual(A, Wq, scale, residual, out, M, N, K, stream)
+
+
+def conv1d_update_raw(conv_state: int, x: int, ld_x: int, weight: int, bias: int, out: int, ld_out: int,
+                      batch: int, dim: int, d_conv: int, stream: int = 0) -> int:
+    return load().w8a16_conv1d_update(conv_state, x, ld_x, weight, bias, out, ld_out, batch, dim, d_conv, stream)
+
+
+def ssm_decode_raw(h_state: int, xbc: int, ld_xbc: int, dt_raw: int, ld_dt: int, a_log: int, d_param: int,
+                   dt_bias: int, out: int, ld_out: int, batch: int, heads: int, head_dim: int, state: int,
+                   groups: int, dt_min: float, dt_max: float, stream: int = 0) -> int:
+    return load().w8a16_ssm_decode(h_state, xbc, ld_xbc, dt_raw, ld_dt, a_log, d_param, dt_bias, out, ld_out,
+                                   batch, heads, head_dim, state, groups, dt_min, dt_max, stream)
 
 
 def dequant_raw(Wq: int, scale: int, out: int, N: int, K: int, stream: int = 0) -> int:
@@ -360,4 +376,71 @@ def w8a16_gemm_residual(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor, 
                                         out.data_ptr(), M, N, K, _stream_handle(A.device, stream))
     if st != OK:
         raise W8A16Error("w8a16_gemm_residual", st)
+    return out
+
+
+# --- Mamba-2 decode step (forward steps 3 to 5) ----------------------------------
+
+def _rows(t: torch.Tensor, name: str, dtype, batch: int, width: int) -> int:
+    """Row stride of a [batch, >= width] tensor whose rows are contiguous."""
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.dim() == 2 and t.shape[0] == batch and t.shape[1] >= width and t.stride(1) == 1,
+          f"{name} must be [{batch}, >= {width}] with contiguous rows, got {list(t.shape)} strides {t.stride()}")
+    return t.stride(0) if batch > 1 else t.shape[1]
+
+
+def w8a16_conv1d_update(conv_state: torch.Tensor, x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One conv1d update step: conv_state (float32 [B, dim, d_conv], updated in
+    place) takes x [B, >= dim] (BF16 rows, e.g. a column slice of the in_proj
+    output); returns bf16(silu(bias + sum_w state * weight)) [B, dim]."""
+    _need(conv_state.dtype == torch.float32 and conv_state.dim() == 3 and conv_state.is_contiguous(),
+          "conv_state must be a contiguous float32 [B, dim, d_conv] tensor")
+    B, dim, d_conv = conv_state.shape
+    ld_x = _rows(x, "x", torch.bfloat16, B, dim)
+    _check_bf16(weight, "weight", (dim, d_conv))
+    _check_bf16(bias, "bias", (dim,))
+    if out is None:
+        _check_device(conv_state, x, weight, bias)
+        out = torch.empty((B, dim), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_device(conv_state, x, weight, bias, out)
+    ld_out = _rows(out, "out", torch.bfloat16, B, dim)
+    with torch.cuda.device(x.device):
+        st = load().w8a16_conv1d_update(conv_state.data_ptr(), x.data_ptr(), ld_x, weight.data_ptr(),
+                                        bias.data_ptr(), out.data_ptr(), ld_out, B, dim, d_conv,
+                                        _stream_handle(x.device, stream))
+    if st != OK:
+        raise W8A16Error("w8a16_conv1d_update", st)
+    return out
+
+
+def w8a16_ssm_decode(h_state: torch.Tensor, xbc: torch.Tensor, dt_raw: torch.Tensor, a_log: torch.Tensor,
+                     d_param: torch.Tensor, dt_bias: torch.Tensor, groups: int, dt_min: float = 1e-9,
+                     dt_max: float = 1e9, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One SSM decode step: h_state (float32 [B, heads, head_dim, state],
+    updated in place), xbc = [x | B | C] rows (BF16 [B, >= width]), dt_raw
+    (BF16 [B, >= heads]); returns y [B, heads * head_dim] (BF16)."""
+    _need(h_state.dtype == torch.float32 and h_state.dim() == 4 and h_state.is_contiguous(),
+          "h_state must be a contiguous float32 [B, heads, head_dim, state] tensor")
+    B, heads, hd, st_ = h_state.shape
+    _need(groups >= 1 and heads % groups == 0, f"heads ({heads}) must be a multiple of groups ({groups})")
+    ld_x = _rows(xbc, "xbc", torch.bfloat16, B, heads * hd + 2 * groups * st_)
+    ld_dt = _rows(dt_raw, "dt_raw", torch.bfloat16, B, heads)
+    for t, name in ((a_log, "a_log"), (d_param, "d_param"), (dt_bias, "dt_bias")):
+        _need(t.dtype == torch.float32 and tuple(t.shape) == (heads,) and t.is_contiguous(),
+              f"{name} must be a contiguous float32 [{heads}] tensor")
+    if out is None:
+        _check_device(h_state, xbc, dt_raw, a_log, d_param, dt_bias)
+        out = torch.empty((B, heads * hd), dtype=torch.bfloat16, device=xbc.device)
+    else:
+        _check_device(h_state, xbc, dt_raw, a_log, d_param, dt_bias, out)
+    ld_out = _rows(out, "out", torch.bfloat16, B, heads * hd)
+    with torch.cuda.device(xbc.device):
+        st = load().w8a16_ssm_decode(h_state.data_ptr(), xbc.data_ptr(), ld_x, dt_raw.data_ptr(), ld_dt,
+                                     a_log.data_ptr(), d_param.data_ptr(), dt_bias.data_ptr(), out.data_ptr(),
+                                     ld_out, B, heads, hd, st_, groups, float(dt_min), float(dt_max),
+                                     _stream_handle(xbc.device, stream))
+    if st != OK:
+        raise W8A16Error("w8a16_ssm_decode", st)
     return out

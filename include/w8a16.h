@@ -187,6 +187,45 @@ int w8a16_gemm_residual(const void* A, const void* Wq, const void* scale, const 
                         void* out, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * The Mamba-2 decode step between the two projections (nemotron_mamba2.rs
+ * module docs, forward steps 3 to 5; argument lists and launch shapes of
+ * `conv1d_update_biased` and `ssm_decode` in that listing). The pages name
+ * the steps but do not write the formulas; these are the standard Mamba-2
+ * recurrence for one token. All calls enqueue on `stream`; batch == 0 is a
+ * no-op; arrays must not overlap (W8A16_ERR_ALIAS) except as stated.
+ *
+ * w8a16_conv1d_update: for each sequence b < batch and channel c < dim,
+ *   conv_state[b][c][0..d_conv)   FP32, the last d_conv inputs (oldest first),
+ *                                 updated in place: shifted by one, x appended;
+ *   out[b*ld_out + c] = bf16( silu( bias[c] + sum_w conv_state[b][c][w] * weight[c][w] ) )
+ * x [batch][ld_x] BF16 (the xBC part of the in_proj output row, ld_x >= dim);
+ * weight [dim][d_conv] and bias [dim] BF16; out [batch][ld_out] BF16.
+ * 1 <= d_conv <= 8, batch <= 65535. conv_state 4-byte aligned, the rest 2.
+ */
+int w8a16_conv1d_update(void* conv_state, const void* x, int64_t ld_x, const void* weight, const void* bias,
+                        void* out, int64_t ld_out, int64_t batch, int64_t dim, int64_t d_conv, void* stream);
+
+/*
+ * w8a16_ssm_decode: for each sequence b and head h (group g = h / (heads /
+ * groups)), with the conv output row xbc[b] = [x (heads*head_dim) | B
+ * (groups*state) | C (groups*state)] (BF16, ld_xbc >= its width) and
+ * dt_raw[b][h] (BF16, the dt part of the in_proj output, ld_dt >= heads):
+ *   dt = clamp( softplus(dt_raw + dt_bias[h]), dt_min, dt_max )
+ *   dA = exp( -dt * exp(a_log[h]) )
+ *   h_state[b][h][p][n] <- dA * h_state[b][h][p][n] + dt * B[g][n] * x[h*head_dim + p]
+ *   out[b*ld_out + h*head_dim + p] = bf16( sum_n C[g][n] * h_state[b][h][p][n] + d_param[h] * x[...] )
+ * h_state FP32 [batch][heads][head_dim][state], updated in place, 16-byte
+ * aligned; a_log, d_param, dt_bias FP32 [heads]; out BF16. state % 4 == 0,
+ * 4 <= state <= 256, heads % groups == 0, 0 <= dt_min <= dt_max (finite;
+ * else W8A16_ERR_ARG). Computed in fp32; the sum over n is a fixed
+ * butterfly (deterministic).
+ */
+int w8a16_ssm_decode(void* h_state, const void* xbc, int64_t ld_xbc, const void* dt_raw, int64_t ld_dt,
+                     const float* a_log, const float* d_param, const float* dt_bias, void* out, int64_t ld_out,
+                     int64_t batch, int64_t heads, int64_t head_dim, int64_t state, int64_t groups,
+                     float dt_min, float dt_max, void* stream);
+
+/*
  * Dequantize only (a test path that exposes the device E4M3 decode and the
  * block-scale indexing the two entry points above use). out is FP32 [N][K]:
  *   out[n][k] = float(E4M3(Wq[n][k])) * scale[n/128][k/128]

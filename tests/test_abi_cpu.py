@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "w8a16.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w8a16_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w8a16_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -228,3 +228,53 @@ def test_binding_refuses_bad_norm_arguments():
         binding.w8a16_gemm_residual(A, W, S, torch.zeros((2, 300), dtype=torch.float32))
     with pytest.raises(ValueError, match="HIP device"):
         binding.w8a16_gemm_residual(A, W, S, torch.zeros((2, 300), dtype=torch.bfloat16))
+
+
+def test_mamba2_step_rejections():
+    F = FAKE
+    St, X, Wt, Bi, O = F, F + (1 << 30), F + (2 << 30), F + (3 << 30), F + (4 << 30)
+    conv = binding.conv1d_update_raw
+    # conv1d_update(state, x, ld_x, weight, bias, out, ld_out, batch, dim, d_conv)
+    assert conv(St, X, 64, Wt, Bi, O, 64, 1, 64, 0, 0) == binding.ERR_SHAPE        # d_conv < 1
+    assert conv(St, X, 64, Wt, Bi, O, 64, 1, 64, 9, 0) == binding.ERR_SHAPE        # d_conv > 8
+    assert conv(St, X, 63, Wt, Bi, O, 64, 1, 64, 4, 0) == binding.ERR_SHAPE        # ld_x < dim
+    assert conv(St, X, 64, Wt, Bi, O, 63, 1, 64, 4, 0) == binding.ERR_SHAPE
+    assert conv(St, X, 64, Wt, Bi, O, 64, 65536, 64, 4, 0) == binding.ERR_SHAPE
+    assert conv(St, X, 64, Wt, Bi, O, 64, 0, 64, 4, 0) == binding.OK               # no-op
+    assert conv(0, X, 64, Wt, Bi, O, 64, 1, 64, 4, 0) == binding.ERR_NULL
+    assert conv(St, X, 64, Wt, 0, O, 64, 1, 64, 4, 0) == binding.ERR_NULL
+    assert conv(St + 2, X, 64, Wt, Bi, O, 64, 1, 64, 4, 0) == binding.ERR_ALIGN
+    assert conv(St, X + 1, 64, Wt, Bi, O, 64, 1, 64, 4, 0) == binding.ERR_ALIGN
+    assert conv(St, X, 64, Wt, Bi, X + 64, 64, 1, 64, 4, 0) == binding.ERR_ALIAS   # out over x
+    assert conv(St, X, 64, Wt, Bi, St + 100, 64, 1, 64, 4, 0) == binding.ERR_ALIAS  # out over the state
+    assert conv(St, St + 256, 64, Wt, Bi, O, 64, 1, 64, 4, 0) == binding.ERR_ALIAS  # x inside the state
+    # ssm_decode(h, xbc, ld_xbc, dt, ld_dt, a_log, D, dt_bias, out, ld_out, batch, heads, hd, state, groups, dt_min, dt_max)
+    H, Xb, Dt, Al, Dp, Db = F, F + (1 << 30), F + (2 << 30), F + (3 << 30), F + (3 << 30) + 4096, F + (3 << 30) + 8192
+    ssm = binding.ssm_decode_raw
+    w = 8 * 4 + 2 * 2 * 16                                                      # heads 8, hd 4, groups 2, state 16
+
+    def call(**kw):
+        a = dict(h=H, xbc=Xb, ld_xbc=w, dt=Dt, ld_dt=8, al=Al, dp=Dp, db=Db, out=O, ld_out=32, batch=1, heads=8,
+                 hd=4, state=16, groups=2, dmin=0.0, dmax=1e9)
+        a.update(kw)
+        return ssm(a["h"], a["xbc"], a["ld_xbc"], a["dt"], a["ld_dt"], a["al"], a["dp"], a["db"], a["out"],
+                   a["ld_out"], a["batch"], a["heads"], a["hd"], a["state"], a["groups"], a["dmin"], a["dmax"], 0)
+
+    assert call(groups=3) == binding.ERR_SHAPE                                  # heads % groups
+    assert call(state=18) == binding.ERR_SHAPE                                  # state % 4
+    assert call(state=260) == binding.ERR_SHAPE                                 # state > 256
+    assert call(ld_xbc=w - 1) == binding.ERR_SHAPE
+    assert call(ld_dt=7) == binding.ERR_SHAPE
+    assert call(ld_out=31) == binding.ERR_SHAPE
+    assert call(dmin=-1.0) == binding.ERR_ARG
+    assert call(dmin=2.0, dmax=1.0) == binding.ERR_ARG
+    assert call(dmax=float("nan")) == binding.ERR_ARG
+    assert call(batch=0) == binding.OK
+    assert call(h=0) == binding.ERR_NULL
+    assert call(db=0) == binding.ERR_NULL
+    assert call(h=H + 8) == binding.ERR_ALIGN                                   # state needs 16 bytes
+    assert call(al=Al + 2) == binding.ERR_ALIGN
+    assert call(out=Xb + 16) == binding.ERR_ALIAS
+    assert call(out=H + 64) == binding.ERR_ALIAS
+    assert call(xbc=H + 128) == binding.ERR_ALIAS                                # xbc inside the state
+    assert call(out=Dp) == binding.ERR_ALIAS                                     # out over D
