@@ -24,7 +24,9 @@ reports the same projections at M = 2..16 through the GEMV entry point (the
 multi-sequence decode workloads) and at M = 32..256 through the GEMM.
 `layer_ends` (outside the timed step) times the norm prologues and the
 residual epilogue: fused into the decode GEMV against the unfused chain, and
-the prefill norms and residual GEMM at M = 1024.
+the prefill norms and residual GEMM at M = 1024. `decode_layer` times one
+Mamba-2 layer's whole decode step for one token (fused in_proj, conv1d
+update, SSM decode, fused out_proj) and the conv / SSM kernels alone.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-few-tokens]
                     [--no-layer-ends]
@@ -374,6 +376,91 @@ def layer_ends_report(projs, device, stream, L, check, reps=10):
     return out
 
 
+SSM_STATE_ROTATE_BYTES = 512 << 20      # SSM states rotate over this much, as the weights do
+
+
+def decode_layer_report(projs, device, stream, L, check, reps=10):
+    """Outside the timed step: one Mamba-2 layer's decode step for one token
+    (hidden 4096), every step in this library's kernels: in_proj with its
+    RMSNorm fused, the conv1d update on xBC, the SSM decode, out_proj with the
+    gated norm (gate z read in place from the in_proj output) and the residual
+    fused. Weights and the per-layer conv / SSM states rotate over several
+    copies so they come from HBM. Also the conv and SSM kernels alone, with
+    their algorithmic bytes (states read and written once)."""
+    sh = stream.cuda_stream
+    eps = inputs.NORM_EPS
+    dims = inputs.MAMBA2_4K
+    H, P, S_, G, DC = dims["heads"], dims["head_dim"], dims["state"], dims["groups"], dims["d_conv"]
+    d_inner = H * P
+    d_xbc = d_inner + 2 * G * S_
+    pin, pout = projs
+    N_in, K_in, N_out, K_out = pin.p_dec.N, pin.p_dec.K, pout.p_dec.N, pout.p_dec.K
+    assert N_in == d_inner + d_xbc + H and K_out == d_inner
+    copies = max(2, SSM_STATE_ROTATE_BYTES // (d_inner * S_ * 4))
+    h_states = [torch.from_numpy(inputs.ssm_state(1, H, P, S_, 9000)).to(device)]
+    h_states += [h_states[0].clone() for _ in range(copies - 1)]
+    c_states = [torch.from_numpy(inputs.conv_state(1, d_xbc, DC, 9001)).to(device) for _ in range(copies)]
+    cw, cb = (to_dev(a, torch.bfloat16, device) for a in inputs.conv_params(d_xbc, DC, 9002))
+    a_log, d_param, dt_bias = (torch.from_numpy(a).to(device) for a in inputs.ssm_params(H, 9003))
+    x = to_dev(inputs.activations(1, K_in, 9004), torch.bfloat16, device)
+    w_in = to_dev(inputs.norm_weight(K_in, 9005), torch.bfloat16, device)
+    w_out = to_dev(inputs.norm_weight(K_out, 9006), torch.bfloat16, device)
+    proj = torch.empty((1, N_in), dtype=torch.bfloat16, device=device)      # [z | xBC | dt]
+    xbc = torch.empty((1, d_xbc), dtype=torch.bfloat16, device=device)
+    y = torch.empty((1, d_inner), dtype=torch.bfloat16, device=device)
+    out = torch.empty((1, N_out), dtype=torch.bfloat16, device=device)
+    e = 2                                                                    # bytes per BF16 element
+
+    def W(p, i):
+        return p.W[i % p.copies].data_ptr(), p.S[i % p.copies].data_ptr()
+
+    def conv(i):
+        check(binding.conv1d_update_raw(c_states[i % copies].data_ptr(), proj.data_ptr() + e * d_inner, N_in,
+                                        cw.data_ptr(), cb.data_ptr(), xbc.data_ptr(), d_xbc, 1, d_xbc, DC, sh),
+              "conv1d_update")
+
+    def ssm(i):
+        check(binding.ssm_decode_raw(h_states[i % copies].data_ptr(), xbc.data_ptr(), d_xbc,
+                                     proj.data_ptr() + e * (d_inner + d_xbc), N_in, a_log.data_ptr(),
+                                     d_param.data_ptr(), dt_bias.data_ptr(), y.data_ptr(), d_inner, 1, H, P, S_, G,
+                                     1e-9, 1e9, sh), "ssm_decode")
+
+    def layer(i):
+        w, s_ = W(pin, i)
+        check(binding.gemv_fused_raw(x.data_ptr(), 0, w_in.data_ptr(), eps, w, s_, 0, proj.data_ptr(),
+                                     1, N_in, K_in, sh), "gemv_fused")
+        conv(i)
+        ssm(i)
+        w, s_ = W(pout, i)
+        check(binding.gemv_fused_raw(y.data_ptr(), proj.data_ptr(), w_out.data_ptr(), eps, w, s_, x.data_ptr(),
+                                     out.data_ptr(), 1, N_out, K_out, sh, ld_gate=N_in), "gemv_fused")
+
+    def timed(fn):
+        for i in range(L):
+            fn(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for r in range(reps):
+            ev[2 * r].record(stream)
+            for i in range(L):
+                fn(r * L + i)
+            ev[2 * r + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e3 for r in range(reps)]) / L)
+
+    t_layer, t_conv, t_ssm = timed(layer), timed(conv), timed(ssm)
+    b_conv = 2 * d_xbc * DC * 4 + 2 * d_xbc * e + d_xbc * DC * e + d_xbc * e
+    b_ssm = 2 * d_inner * S_ * 4 + d_xbc * e + H * e + d_inner * e + 3 * H * 4
+    return {"unit": "us per launch (or per layer step)",
+            "state_copies_rotated": copies,
+            "layer_step": {"us": round(t_layer, 2),
+                           "kernels": "in_proj fused norm GEMV, conv1d update, SSM decode, "
+                                      "out_proj fused gated norm GEMV + residual"},
+            "conv1d_update": {"us": round(t_conv, 2), "bytes": b_conv, "GB/s": round(b_conv / t_conv / 1e3, 1),
+                              "frac": round(b_conv / t_conv / 1e3 / HBM_PEAK_GBS, 4)},
+            "ssm_decode": {"us": round(t_ssm, 2), "bytes": b_ssm, "GB/s": round(b_ssm / t_ssm / 1e3, 1),
+                           "frac": round(b_ssm / t_ssm / 1e3 / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(budget_s: float):
     """Time the CPU oracle on a bounded sample of the same two workloads."""
     import oracle
@@ -423,7 +510,7 @@ def main():
                     help="skip the few-token report (profiler runs: keeps the dispatch order that "
                          "--summarize-trace / --summarize-counters label)")
     ap.add_argument("--no-layer-ends", action="store_true",
-                    help="skip the norm prologue / residual epilogue timings (profiler runs)")
+                    help="skip the norm prologue / residual epilogue and layer decode-step timings (profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--layers", type=int, default=DEFAULT_LAYERS, help="decode layers (weight copies) per step")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -489,6 +576,7 @@ def main():
 
     few = None if args.no_few_tokens else few_token_report(projs, device, stream, L, check)
     ends = None if args.no_layer_ends else layer_ends_report(projs, device, stream, L, check)
+    layer = None if args.no_layer_ends else decode_layer_report(projs, device, stream, L, check)
 
     if args.copy_calibration:
         src = torch.empty(CALIBRATION_BYTES // 4, dtype=torch.float32, device=device)   # read once, written once
@@ -542,6 +630,7 @@ def main():
         },
         "few_tokens": few,
         "layer_ends": ends,
+        "decode_layer": layer,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget),
     }
     print(json.dumps(rec), flush=True)

@@ -76,7 +76,7 @@ def load() -> ctypes.CDLL:
     lib.w8a16_rmsnorm.restype = ctypes.c_int
     lib.w8a16_rmsnorm.argtypes = [P, P, P, F, P, I64, I64, P]
     lib.w8a16_gemv_fused.restype = ctypes.c_int
-    lib.w8a16_gemv_fused.argtypes = [P, P, P, F, P, P, P, P, I64, I64, I64, P]
+    lib.w8a16_gemv_fused.argtypes = [P, P, I64, P, F, P, P, P, P, I64, I64, I64, P]
     lib.w8a16_gemm_residual.restype = ctypes.c_int
     lib.w8a16_gemm_residual.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.w8a16_conv1d_update.restype = ctypes.c_int
@@ -120,9 +120,9 @@ def rmsnorm_raw(x: int, gate: int, weight: int, eps: float, out: int, M: int, K:
 
 
 def gemv_fused_raw(A: int, gate: int, norm_weight: int, eps: float, Wq: int, scale: int, residual: int,
-                   out: int, M: int, N: int, K: int, stream: int = 0) -> int:
-    return load().w8a16_gemv_fused(A, gate or None, norm_weight or None, eps, Wq, scale, residual or None,
-                                   out, M, N, K, stream)
+                   out: int, M: int, N: int, K: int, stream: int = 0, ld_gate: int | None = None) -> int:
+    return load().w8a16_gemv_fused(A, gate or None, K if ld_gate is None else ld_gate, norm_weight or None, eps,
+                                   Wq, scale, residual or None, out, M, N, K, stream)
 
 
 def gemm_residual_raw(A: int, Wq: int, scale: int, residual: int, out: int, M: int, N: int, K: int,
@@ -325,7 +325,9 @@ def w8a16_gemv_fused(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
                      gate: torch.Tensor | None = None, residual: torch.Tensor | None = None,
                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Decode GEMV with the norm prologue (norm_weight, optional gate) and the
-    residual epilogue fused: out = [residual +] (norm(A) x dequant(Wq)^T), BF16."""
+    residual epilogue fused: out = [residual +] (norm(A) x dequant(Wq)^T), BF16.
+    The gate may be a column slice of a wider row-major tensor (z of the
+    in_proj output), as long as its rows are contiguous and 16-byte aligned."""
     _need(A.dim() == 2, f"A must be [M, K], got shape {tuple(A.shape)}")
     N, K = _check_weights(Wq, scale)
     M = A.shape[0]
@@ -333,8 +335,10 @@ def w8a16_gemv_fused(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
     _need(gate is None or norm_weight is not None, "a gate needs a norm weight")
     if norm_weight is not None:
         _check_bf16(norm_weight, "norm_weight", (K,))
+    ld_gate = K
     if gate is not None:
-        _check_bf16(gate, "gate", (M, K))
+        ld_gate = _rows(gate, "gate", torch.bfloat16, M, K)
+        _need(gate.shape[1] == K, f"gate must have K = {K} columns, got {gate.shape[1]}")
     if residual is not None:
         _check_bf16(residual, "residual", (M, N))
     e = _eps(eps)
@@ -350,8 +354,9 @@ def w8a16_gemv_fused(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
         _check_device(*ins, out)
     ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     with torch.cuda.device(A.device):
-        st = load().w8a16_gemv_fused(A.data_ptr(), ptr(gate), ptr(norm_weight), e, Wq.data_ptr(), scale.data_ptr(),
-                                     ptr(residual), out.data_ptr(), M, N, K, _stream_handle(A.device, stream))
+        st = load().w8a16_gemv_fused(A.data_ptr(), ptr(gate), ld_gate, ptr(norm_weight), e, Wq.data_ptr(),
+                                     scale.data_ptr(), ptr(residual), out.data_ptr(), M, N, K,
+                                     _stream_handle(A.device, stream))
     if st != OK:
         raise W8A16Error("w8a16_gemv_fused", st)
     return out

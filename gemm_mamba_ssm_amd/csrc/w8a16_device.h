@@ -119,9 +119,10 @@ __device__ __forceinline__ u32x4_t load16(const void* p) {
 // norm prologue on the activations when `weight` is set (gated by silu(gate)
 // when `gate` is set too), and a residual epilogue when `residual` is set.
 struct Fusion {
-    const uint16_t* gate;       // [M][K] BF16, or nullptr
+    const uint16_t* gate;       // [M] rows of K BF16, ld_gate apart, or nullptr
     const uint16_t* weight;     // [K] BF16 norm weight, or nullptr (no norm)
     const uint16_t* residual;   // [M][N] BF16, or nullptr
+    int64_t ld_gate;
     float eps;
 };
 

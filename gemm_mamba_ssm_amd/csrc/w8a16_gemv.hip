@@ -200,7 +200,7 @@ struct NormOps {
             if constexpr (kEarlyGate)
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
-                    const uint16_t* g = fu.gate + static_cast<int64_t>(m) * K + kch[j];
+                    const uint16_t* g = fu.gate + static_cast<int64_t>(m) * fu.ld_gate + kch[j];
                     gv[m][j][0] = kvalid[j] ? load16(g) : zero;
                     gv[m][j][1] = kvalid[j] ? load16(g + 8) : zero;
                 }
@@ -246,7 +246,7 @@ struct NormOps {
                         gl = gv[m][j][0];
                         gh = gv[m][j][1];
                     } else {
-                        const uint16_t* g = fu.gate + static_cast<int64_t>(m) * K + kch[j];
+                        const uint16_t* g = fu.gate + static_cast<int64_t>(m) * fu.ld_gate + kch[j];
                         gl = load16(g);
                         gh = load16(g + 8);
                     }
@@ -430,7 +430,7 @@ Choice select_plain(int mr, int j) {
 // checked).
 template <int SF, int FU>
 int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
-             hipStream_t stream, Fusion fu = Fusion{nullptr, nullptr, nullptr, 0.0f}) {
+             hipStream_t stream, Fusion fu = Fusion{nullptr, nullptr, nullptr, 0, 0.0f}) {
     const int mr = static_cast<int>(M);
     const int j = K > static_cast<int64_t>(kWaveK) * kMaxWaves ? 2 : 1;
     const int nwaves = static_cast<int>(ceil_div(K, static_cast<int64_t>(kWaveK) * j));
@@ -489,7 +489,7 @@ extern "C" int w8a16_gemv(const void* A, const void* Wq, const void* scale, void
     return w8a16_gemv_ex(A, Wq, scale, W8A16_SCALE_BLOCK_BF16, out, M, N, K, stream);
 }
 
-extern "C" int w8a16_gemv_fused(const void* A, const void* gate, const void* norm_weight, float eps,
+extern "C" int w8a16_gemv_fused(const void* A, const void* gate, int64_t ld_gate, const void* norm_weight, float eps,
                                 const void* Wq, const void* scale, const void* residual, void* out,
                                 int64_t M, int64_t N, int64_t K, void* stream) {
     using namespace w8a16;
@@ -497,6 +497,7 @@ extern "C" int w8a16_gemv_fused(const void* A, const void* gate, const void* nor
     int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
     if (st != W8A16_OK) return st;
     if (gate && !norm_weight) return W8A16_ERR_ARG;            // a gate belongs to the norm
+    if (gate && (ld_gate < K || ld_gate % 8 != 0 || ld_gate > INT32_MAX)) return W8A16_ERR_SHAPE;
     if (norm_weight && (!(eps >= 0.0f) || eps > 3.0e38f)) return W8A16_ERR_ARG;   // also NaN
     if (noop) return W8A16_OK;
     if (!fused_fits(M, K)) return W8A16_ERR_SHAPE;
@@ -507,10 +508,10 @@ extern "C" int w8a16_gemv_fused(const void* A, const void* gate, const void* nor
         if (overlaps(out, out_bytes, residual, out_bytes)) return W8A16_ERR_ALIAS;
     }
     if ((norm_weight && overlaps(out, out_bytes, norm_weight, K * 2)) ||
-        (gate && overlaps(out, out_bytes, gate, M * K * 2)))
+        (gate && overlaps(out, out_bytes, gate, ((M - 1) * ld_gate + K) * 2)))
         return W8A16_ERR_ALIAS;
     const Fusion fu{static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(norm_weight),
-                    static_cast<const uint16_t*>(residual), eps};
+                    static_cast<const uint16_t*>(residual), gate ? ld_gate : K, eps};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gate) return run_gemv<kScaleBlockBf16, kFuseGated>(A, Wq, scale, out, M, N, K, s, fu);
     if (norm_weight) return run_gemv<kScaleBlockBf16, kFuseNorm>(A, Wq, scale, out, M, N, K, s, fu);

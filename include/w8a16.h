@@ -166,7 +166,10 @@ int w8a16_rmsnorm(const void* x, const void* gate, const void* weight, float eps
  * Decode GEMV with the prologue and epilogue fused (one launch per
  * projection): A is the layer input x (in_proj, norm_weight set, gate NULL)
  * or the SSM output y (out_proj, gate = z); norm_weight NULL means no norm
- * (then gate must be NULL too, else W8A16_ERR_ARG). residual ([M][N] BF16,
+ * (then gate must be NULL too, else W8A16_ERR_ARG). The gate's rows (K BF16
+ * each) lie ld_gate elements apart, so z can be read in place from the
+ * in_proj output row [z | xBC | dt] (ld_gate >= K, ld_gate % 8 == 0, gate
+ * 16-byte aligned; ignored without a gate). residual ([M][N] BF16,
  * 2-byte aligned, or NULL) adds the epilogue; it must not overlap out.
  * The scale is the BF16 block grid; errors as for w8a16_gemv. Shapes: 1 <= M
  * <= 4 with K <= 16384, or 5 <= M <= 8 with K <= 8192 (the norm's operands
@@ -174,7 +177,7 @@ int w8a16_rmsnorm(const void* x, const void* gate, const void* weight, float eps
  * and the two-step form w8a16_rmsnorm + w8a16_gemm_residual applies. Every
  * M runs the GEMV kernel (the skinny path of w8a16_gemv is not fused).
  */
-int w8a16_gemv_fused(const void* A, const void* gate, const void* norm_weight, float eps,
+int w8a16_gemv_fused(const void* A, const void* gate, int64_t ld_gate, const void* norm_weight, float eps,
                      const void* Wq, const void* scale, const void* residual, void* out,
                      int64_t M, int64_t N, int64_t K, void* stream);
 

@@ -193,6 +193,8 @@ def test_norm_and_fused_rejections():
     assert fused(A, 0, Wn, 1e-5, Wq, S, R, O, 5, 256, 8192 + 16, 0) == binding.ERR_SHAPE
     assert fused(A, 0, Wn, 1e-5, Wq, S, R, O, 4, 256, 16384 + 16, 0) == binding.ERR_SHAPE
     assert fused(A, 0, Wn, 1e-5, Wq, S, R, O, 0, 256, 256, 0) == binding.OK           # no-op
+    assert fused(A, G, Wn, 1e-5, Wq, S, R, O, 1, 256, 256, 0, ld_gate=255) == binding.ERR_SHAPE   # ld_gate < K
+    assert fused(A, G, Wn, 1e-5, Wq, S, R, O, 1, 256, 256, 0, ld_gate=260) == binding.ERR_SHAPE   # ld_gate % 8
     assert fused(A, 0, Wn + 8, 1e-5, Wq, S, R, O, 1, 256, 256, 0) == binding.ERR_ALIGN
     assert fused(A, G + 8, Wn, 1e-5, Wq, S, R, O, 1, 256, 256, 0) == binding.ERR_ALIGN
     assert fused(A, 0, Wn, 1e-5, Wq, S, R + 1, O, 1, 256, 256, 0) == binding.ERR_ALIGN

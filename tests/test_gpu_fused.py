@@ -141,6 +141,28 @@ def test_gemv_fused_gated_norm_and_residual(dev, M, N, K):
     check_close(bits(got), want, den, f"fused gated+res M={M} N={N} K={K}", extra_rel=2.0 ** -8)
 
 
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_gemv_fused_gate_read_in_place(dev, M):
+    """The gate as a column slice of a wider row (z of the in_proj output row
+    [z | xBC | dt]): the same bits as with a contiguous copy of it."""
+    N, K = 4096, 8192
+    y = inputs.activations(M, K, 4310 + M)
+    zrow = inputs.activations(M, K + 2208, 4320 + M)                  # z in columns 8 .. 8 + K
+    w = inputs.norm_weight(K, 4330)
+    res = inputs.activations(M, N, 4340 + M)
+    Wq, S = inputs.weights(N, K, 0.02, 4350)
+    dy, dW, dS, dw, dr = bf(y, dev), u8(Wq, dev), bf(S, dev), bf(w, dev), bf(res, dev)
+    zdev = bf(zrow, dev)
+    z_slice = zdev[:, 8:8 + K]
+    z_copy = z_slice.contiguous()
+    a = bits(binding.w8a16_gemv_fused(dy, dW, dS, norm_weight=dw, eps=EPS, gate=z_slice, residual=dr))
+    b = bits(binding.w8a16_gemv_fused(dy, dW, dS, norm_weight=dw, eps=EPS, gate=z_copy, residual=dr))
+    assert np.array_equal(a, b)
+    _, act = oracle.rmsnorm(y, w, EPS, gate=np.ascontiguousarray(zrow[:, 8:8 + K]))
+    ref, den = oracle.w8a16(act, Wq, S)
+    check_close(a, oracle.bf16_value(res) + ref, den, f"gate slice M={M}", extra_rel=2.0 ** -8)
+
+
 @pytest.mark.parametrize("M", [1, 2, 3])
 def test_gemv_fused_without_prologue_matches_plain_bits(dev, M):
     """With neither norm nor residual the fused kernel computes the plain GEMV's
