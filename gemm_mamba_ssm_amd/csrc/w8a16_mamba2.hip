@@ -79,32 +79,51 @@ ssm_decode_kernel(float* __restrict__ hstate, const uint16_t* __restrict__ xbc, 
     const int g = h / (heads / groups);
     const int64_t d_inner = static_cast<int64_t>(heads) * head_dim;
     const uint16_t* row = xbc + b * ld_xbc;
-
-    float dt = softplus(bf16v(dt_raw + b * ld_dt + h) + dt_bias[h]);
-    dt = fminf(fmaxf(dt, dt_min), dt_max);
-    const float dA = expf(-dt * expf(a_log[h]));
-    const float xv = bf16v(row + static_cast<int64_t>(h) * head_dim + p);
-    const float dtx = dt * xv;
     const uint16_t* Bg = row + d_inner + static_cast<int64_t>(g) * st;
     const uint16_t* Cg = row + d_inner + static_cast<int64_t>(groups) * st + static_cast<int64_t>(g) * st;
     float* hp = hstate + ((b * heads + h) * head_dim + p) * st;
 
+    // Every load first, the state's (from HBM) at the head, so that the
+    // memory round trips overlap instead of following one another.
+    f32x4_t hv[NCH];
+    float bv[NCH][4], cv[NCH][4];
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+        const int n0 = 4 * (lane + q * kLanesPerRow);
+        if (n0 < st) hv[q] = *reinterpret_cast<const f32x4_t*>(hp + n0);
+    }
+    const float raw = bf16v(dt_raw + b * ld_dt + h) + dt_bias[h];
+    const float a_h = a_log[h], d_h = d_param[h];
+    const float xv = bf16v(row + static_cast<int64_t>(h) * head_dim + p);
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+        const int n0 = 4 * (lane + q * kLanesPerRow);
+        if (n0 < st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bv[q][i] = bf16v(Bg + n0 + i);
+                cv[q][i] = bf16v(Cg + n0 + i);
+            }
+    }
+
+    const float dt = fminf(fmaxf(softplus(raw), dt_min), dt_max);
+    const float dA = expf(-dt * expf(a_h));
+    const float dtx = dt * xv;
     float y = 0.0f;
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
         const int n0 = 4 * (lane + q * kLanesPerRow);
         if (n0 >= st) break;
-        f32x4_t hv = *reinterpret_cast<const f32x4_t*>(hp + n0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            hv[i] = dA * hv[i] + bf16v(Bg + n0 + i) * dtx;
-            y = fmaf(bf16v(Cg + n0 + i), hv[i], y);
+            hv[q][i] = dA * hv[q][i] + bv[q][i] * dtx;
+            y = fmaf(cv[q][i], hv[q][i], y);
         }
-        *reinterpret_cast<f32x4_t*>(hp + n0) = hv;
+        *reinterpret_cast<f32x4_t*>(hp + n0) = hv[q];
     }
 #pragma unroll
     for (int d = kLanesPerRow / 2; d >= 1; d /= 2) y += __shfl_xor(y, d, kLanesPerRow);
-    if (lane == 0) out[b * ld_out + static_cast<int64_t>(h) * head_dim + p] = f32_to_bf16_bits(y + d_param[h] * xv);
+    if (lane == 0) out[b * ld_out + static_cast<int64_t>(h) * head_dim + p] = f32_to_bf16_bits(y + d_h * xv);
 }
 
 // [p, p + bytes) for a [rows][ld] array of which each row uses `used` elements.
