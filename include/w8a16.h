@@ -25,7 +25,9 @@
  *
  * Ownership: the caller owns every buffer it passes; the library keeps no
  * pointer to them after a call returns. The only memory the library allocates
- * is the GEMM workspace described at w8a16_gemm.
+ * is the GEMM workspace described at w8a16_gemm. The decode-step entry points
+ * (w8a16_conv1d_update, w8a16_ssm_decode) update the caller's state buffers in
+ * place; every other entry point only writes `out`.
  * Streams: `stream` is a hipStream_t (NULL = the legacy default stream). Every
  * call only enqueues work on it and returns without synchronizing; the result
  * is ready once the stream reaches that point.
@@ -55,8 +57,8 @@ enum w8a16_status {
 };
 
 /*
- * Scale formats of the _ex entry points. The two entry points above take the
- * first; the others are the variants the pages name besides it:
+ * Scale formats of the _ex entry points. w8a16_gemv and w8a16_gemm (below)
+ * take the first; the others are the variants the pages name besides it:
  *  - W8A16_SCALE_BLOCK_BF16: BF16 [ceil(N/128)][ceil(K/128)] (the grid above);
  *  - W8A16_SCALE_BLOCK_F32: FP32, same grid and index (nemotron_mamba2.rs
  *    source listing, `set_fp8_weights`: its format check names FP32 block
