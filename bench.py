@@ -525,7 +525,49 @@ def cpu_baseline(budget_s: float):
         "sample": f"{reps} whole M=1 decode passes (in_proj + out_proj) in {t_dec:.1f} s",
         "prefill": {"value": round(flops / t_pre / 1e12, 5), "unit": "TFLOP/s",
                     "sample": f"{rows} whole output rows of the M=1024 in_proj in {t_pre:.1f} s"},
+        "layer_steps": cpu_baseline_layer_steps(),
     }
+
+
+def cpu_baseline_layer_steps(budget_s: float = 1.0):
+    """The oracle's norms and decode-step updates on the same shapes as
+    `layer_ends` / `decode_layer` (one token, hidden 4096; the prefill norm on
+    whole rows), each repeated for about budget_s, as us per call (per row
+    for the prefill norm)."""
+    import oracle
+
+    dims = inputs.MAMBA2_4K
+    H, P, S_, G, DC = dims["heads"], dims["head_dim"], dims["state"], dims["groups"], dims["d_conv"]
+    d_inner = H * P
+    d_xbc = d_inner + 2 * G * S_
+    x = inputs.activations(1, 4096, 9301)
+    w = inputs.norm_weight(4096, 9302)
+    y = inputs.activations(1, d_inner, 9303)
+    z = inputs.activations(1, d_inner, 9304)
+    w2 = inputs.norm_weight(d_inner, 9305)
+    row = inputs.activations(1, d_xbc + H, 9306)
+    cw, cb = inputs.conv_params(d_xbc, DC, 9307)
+    cstate = inputs.conv_state(1, d_xbc, DC, 9308).astype(np.float64)
+    hstate = inputs.ssm_state(1, H, P, S_, 9309).astype(np.float64)
+    a_log, d_param, dt_bias = inputs.ssm_params(H, 9310)
+    xbc = inputs.activations(1, d_xbc, 9311)
+
+    def per_call(fn):
+        n, t0 = 0, time.perf_counter()
+        while n == 0 or time.perf_counter() - t0 < budget_s:
+            fn()
+            n += 1
+        return round((time.perf_counter() - t0) / n * 1e6, 1), n
+
+    out = {"unit": "us per call on the host cores (the fp64 oracle as it stands)"}
+    for name, fn in (("rmsnorm_1x4096", lambda: oracle.rmsnorm(x, w, inputs.NORM_EPS)),
+                     ("gated_rmsnorm_1x8192", lambda: oracle.rmsnorm(y, w2, inputs.NORM_EPS, gate=z)),
+                     ("conv1d_update_10240ch", lambda: oracle.conv1d_update(cstate, row, cw, cb)),
+                     ("ssm_decode_128x64x128", lambda: oracle.ssm_decode(hstate, xbc, row[:, d_xbc:], a_log,
+                                                                         d_param, dt_bias, G))):
+        us, n = per_call(fn)
+        out[name] = {"us": us, "calls": n}
+    return out
 
 
 def main():
