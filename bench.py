@@ -435,6 +435,22 @@ def decode_layer_report(projs, device, stream, L, check, reps=10):
         check(binding.gemv_fused_raw(y.data_ptr(), proj.data_ptr(), w_out.data_ptr(), eps, w, s_, x.data_ptr(),
                                      out.data_ptr(), 1, N_out, K_out, h, ld_gate=N_in), "gemv_fused")
 
+    def layer_in_proj_conv(i, h=sh):
+        """The same step with the conv fused into in_proj (3 launches); the conv
+        outputs overwrite the xBC columns of the in_proj output, where the SSM
+        then reads them."""
+        w, s_ = W(pin, i)
+        check(binding.gemv_in_proj_raw(x.data_ptr(), w_in.data_ptr(), eps, w, s_, c_states[i % copies].data_ptr(),
+                                       cw.data_ptr(), cb.data_ptr(), d_inner, d_xbc, DC, proj.data_ptr(), 1, N_in,
+                                       K_in, h), "gemv_in_proj")
+        check(binding.ssm_decode_raw(h_states[i % copies].data_ptr(), proj.data_ptr() + e * d_inner, N_in,
+                                     proj.data_ptr() + e * (d_inner + d_xbc), N_in, a_log.data_ptr(),
+                                     d_param.data_ptr(), dt_bias.data_ptr(), y.data_ptr(), d_inner, 1, H, P, S_, G,
+                                     1e-9, 1e9, h), "ssm_decode")
+        w, s_ = W(pout, i)
+        check(binding.gemv_fused_raw(y.data_ptr(), proj.data_ptr(), w_out.data_ptr(), eps, w, s_, x.data_ptr(),
+                                     out.data_ptr(), 1, N_out, K_out, h, ld_gate=N_in), "gemv_fused")
+
     def graph_of_layers():
         """L layer steps (each with its own weight copies and states) captured
         in one HIP graph; returns us per layer step over `reps` replays."""
@@ -442,14 +458,14 @@ def decode_layer_report(projs, device, stream, L, check, reps=10):
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             for i in range(L):
-                layer(i, side.cuda_stream)
+                layer_in_proj_conv(i, side.cuda_stream)
         stream.wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             h = torch.cuda.current_stream(device).cuda_stream
             for i in range(L):
-                layer(i, h)
+                layer_in_proj_conv(i, h)
         g.replay()
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
@@ -473,6 +489,7 @@ def decode_layer_report(projs, device, stream, L, check, reps=10):
         return float(np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e3 for r in range(reps)]) / L)
 
     t_layer, t_conv, t_ssm = timed(layer), timed(conv), timed(ssm)
+    t_layer3 = timed(layer_in_proj_conv)
     t_graph = graph_of_layers()
     b_conv = 2 * d_xbc * DC * 4 + 2 * d_xbc * e + d_xbc * DC * e + d_xbc * e
     b_ssm = 2 * d_inner * S_ * 4 + d_xbc * e + H * e + d_inner * e + 3 * H * 4
@@ -481,8 +498,11 @@ def decode_layer_report(projs, device, stream, L, check, reps=10):
             "layer_step": {"us": round(t_layer, 2),
                            "kernels": "in_proj fused norm GEMV, conv1d update, SSM decode, "
                                       "out_proj fused gated norm GEMV + residual"},
+            "layer_step_conv_in_in_proj": {"us": round(t_layer3, 2),
+                                           "kernels": "in_proj GEMV with its norm and the conv1d update fused, "
+                                                      "SSM decode, out_proj fused"},
             "layer_step_hip_graph": {"us": round(t_graph, 2),
-                                     "how": f"{L} layer steps captured in one HIP graph, replayed"},
+                                     "how": f"{L} layer steps (conv in in_proj) captured in one HIP graph, replayed"},
             "conv1d_update": {"us": round(t_conv, 2), "bytes": b_conv, "GB/s": round(b_conv / t_conv / 1e3, 1),
                               "frac": round(b_conv / t_conv / 1e3 / HBM_PEAK_GBS, 4)},
             "ssm_decode": {"us": round(t_ssm, 2), "bytes": b_ssm, "GB/s": round(b_ssm / t_ssm / 1e3, 1),

@@ -11,7 +11,9 @@ kernels in ``libw8a16.so`` (C ABI: ``include/w8a16.h``).
 * ``w8a16_rmsnorm``, ``w8a16_gemv_fused``, ``w8a16_gemm_residual`` - the
   layer's norm prologues and residual epilogue around the projections
 * ``w8a16_conv1d_update``, ``w8a16_ssm_decode`` - the Mamba-2 decode step
-  between the projections
+  between the projections; ``w8a16_gemv_in_proj`` - in_proj with its norm and
+  the conv1d update fused
 """
 from .binding import (W8A16Error, w8a16_conv1d_update, w8a16_dequant, w8a16_gemm,  # noqa: F401
-                      w8a16_gemm_residual, w8a16_gemv, w8a16_gemv_fused, w8a16_rmsnorm, w8a16_ssm_decode)
+                      w8a16_gemm_residual, w8a16_gemv, w8a16_gemv_fused, w8a16_gemv_in_proj, w8a16_rmsnorm,
+                      w8a16_ssm_decode)

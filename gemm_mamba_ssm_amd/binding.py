@@ -31,7 +31,8 @@ LIB_PATH = os.path.join(_PKG, "libw8a16.so")
 BLOCK = 128
 
 EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_gemv_ex", "w8a16_gemm_ex", "w8a16_rmsnorm", "w8a16_gemv_fused",
-           "w8a16_gemm_residual", "w8a16_conv1d_update", "w8a16_ssm_decode", "w8a16_dequant", "w8a16_strerror")
+           "w8a16_gemm_residual", "w8a16_conv1d_update", "w8a16_gemv_in_proj", "w8a16_ssm_decode", "w8a16_dequant",
+           "w8a16_strerror")
 
 # enum w8a16_scale_format
 SCALE_BLOCK_BF16, SCALE_BLOCK_F32, SCALE_ROW_F32 = 0, 1, 2
@@ -81,6 +82,8 @@ def load() -> ctypes.CDLL:
     lib.w8a16_gemm_residual.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.w8a16_conv1d_update.restype = ctypes.c_int
     lib.w8a16_conv1d_update.argtypes = [P, P, I64, P, P, P, I64, I64, I64, I64, P]
+    lib.w8a16_gemv_in_proj.restype = ctypes.c_int
+    lib.w8a16_gemv_in_proj.argtypes = [P, P, F, P, P, P, P, P, I64, I64, I64, P, I64, I64, I64, P]
     lib.w8a16_ssm_decode.restype = ctypes.c_int
     lib.w8a16_ssm_decode.argtypes = [P, P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, I64, I64, F, F, P]
     lib.w8a16_dequant.restype = ctypes.c_int
@@ -133,6 +136,13 @@ def gemm_residual_raw(A: int, Wq: int, scale: int, residual: int, out: int, M: i
 def conv1d_update_raw(conv_state: int, x: int, ld_x: int, weight: int, bias: int, out: int, ld_out: int,
                       batch: int, dim: int, d_conv: int, stream: int = 0) -> int:
     return load().w8a16_conv1d_update(conv_state, x, ld_x, weight, bias, out, ld_out, batch, dim, d_conv, stream)
+
+
+def gemv_in_proj_raw(A: int, norm_weight: int, eps: float, Wq: int, scale: int, conv_state: int, conv_weight: int,
+                     conv_bias: int, conv_begin: int, conv_dim: int, d_conv: int, out: int, M: int, N: int, K: int,
+                     stream: int = 0) -> int:
+    return load().w8a16_gemv_in_proj(A, norm_weight, eps, Wq, scale, conv_state, conv_weight, conv_bias,
+                                     conv_begin, conv_dim, d_conv, out, M, N, K, stream)
 
 
 def ssm_decode_raw(h_state: int, xbc: int, ld_xbc: int, dt_raw: int, ld_dt: int, a_log: int, d_param: int,
@@ -448,4 +458,42 @@ def w8a16_ssm_decode(h_state: torch.Tensor, xbc: torch.Tensor, dt_raw: torch.Ten
                                      _stream_handle(xbc.device, stream))
     if st != OK:
         raise W8A16Error("w8a16_ssm_decode", st)
+    return out
+
+
+def w8a16_gemv_in_proj(x: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor, norm_weight: torch.Tensor,
+                       eps: float, conv_state: torch.Tensor, conv_weight: torch.Tensor, conv_bias: torch.Tensor,
+                       conv_begin: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The decode step's in_proj in one launch: RMSNorm of x, the projection,
+    and the conv1d update applied in place to the output columns
+    [conv_begin, conv_begin + dim) (conv_state float32 [M, dim, d_conv],
+    updated). Returns out [M, N] (BF16)."""
+    _need(x.dim() == 2, f"x must be [M, K], got shape {tuple(x.shape)}")
+    N, K = _check_weights(Wq, scale)
+    M = x.shape[0]
+    _check_bf16(x, "x", (M, K))
+    _check_bf16(norm_weight, "norm_weight", (K,))
+    _need(conv_state.dtype == torch.float32 and conv_state.dim() == 3 and conv_state.is_contiguous()
+          and conv_state.shape[0] == M, f"conv_state must be a contiguous float32 [{M}, dim, d_conv] tensor")
+    dim, d_conv = conv_state.shape[1], conv_state.shape[2]
+    _check_bf16(conv_weight, "conv_weight", (dim, d_conv))
+    _check_bf16(conv_bias, "conv_bias", (dim,))
+    _need(0 <= conv_begin and conv_begin + dim <= N, f"conv columns [{conv_begin}, {conv_begin + dim}) exceed N = {N}")
+    e = _eps(eps)
+    _need(M <= FUSED_MAX_M and (K <= GEMV_MAX_K if M > FUSED_MAX_M_LONG_K else K <= GEMV_MAX_K_SMALL_M),
+          f"w8a16_gemv_in_proj takes M <= 4 with K <= {GEMV_MAX_K_SMALL_M} or M <= 8 with K <= {GEMV_MAX_K}")
+    ins = [x, Wq, scale, norm_weight, conv_state, conv_weight, conv_bias]
+    if out is None:
+        _check_device(*ins)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_bf16(out, "out", (M, N))
+        _check_device(*ins, out)
+    with torch.cuda.device(x.device):
+        st = load().w8a16_gemv_in_proj(x.data_ptr(), norm_weight.data_ptr(), e, Wq.data_ptr(), scale.data_ptr(),
+                                       conv_state.data_ptr(), conv_weight.data_ptr(), conv_bias.data_ptr(),
+                                       conv_begin, dim, d_conv, out.data_ptr(), M, N, K,
+                                       _stream_handle(x.device, stream))
+    if st != OK:
+        raise W8A16Error("w8a16_gemv_in_proj", st)
     return out

@@ -124,6 +124,13 @@ struct Fusion {
     const uint16_t* residual;   // [M][N] BF16, or nullptr
     int64_t ld_gate;
     float eps;
+    // conv1d update on output columns [conv_begin, conv_begin + conv_dim)
+    // (the in_proj form): FP32 state [M][conv_dim][d_conv], BF16 taps
+    // [conv_dim][d_conv] and bias [conv_dim].
+    float* conv_state;
+    const uint16_t* conv_weight;
+    const uint16_t* conv_bias;
+    int conv_begin, conv_dim, d_conv;
 };
 
 // SiLU in fp32: z / (1 + e^-z).
@@ -174,6 +181,24 @@ __device__ __forceinline__ uint16_t residual_add_bits(uint16_t y, uint16_t resid
 
 __device__ __forceinline__ uint16_t residual_out(float sum, uint16_t residual) {
     return residual_add_bits(f32_to_bf16_bits(sum), residual);
+}
+
+// conv1d update of one channel (nemotron_mamba2.rs module docs, forward step
+// 3): the FP32 state s[0..d_conv) of the last inputs, oldest first, is
+// shifted and takes the new BF16 input x; returns bf16(silu(bias + sum_t
+// s[t] * w[t])), summed in tap order.
+__device__ __forceinline__ uint16_t conv_update_channel(float* s, const uint16_t* w, uint16_t bias, uint16_t x,
+                                                        int d_conv) {
+    float acc = bf16_bits_to_f32(bias);
+    for (int t = 0; t + 1 < d_conv; ++t) {
+        const float v = s[t + 1];
+        s[t] = v;
+        acc = fmaf(v, bf16_bits_to_f32(w[t]), acc);
+    }
+    const float xv = bf16_bits_to_f32(x);
+    s[d_conv - 1] = xv;
+    acc = fmaf(xv, bf16_bits_to_f32(w[d_conv - 1]), acc);
+    return f32_to_bf16_bits(silu(acc));
 }
 
 }  // namespace w8a16

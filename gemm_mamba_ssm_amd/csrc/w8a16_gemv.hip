@@ -73,8 +73,10 @@ __device__ __forceinline__ void butterfly(float (&v)[P], int lane) {
 
 // What a kernel fuses around the product (w8a16_gemv_fused): nothing (the
 // plain GEMV), the residual epilogue only, or the RMSNorm / gated RMSNorm
-// prologue (each with the residual epilogue when one is passed).
-constexpr int kFuseNone = 0, kFuseResidual = 1, kFuseNorm = 2, kFuseGated = 3;
+// prologue (each with the residual epilogue when one is passed); and the
+// in_proj form (w8a16_gemv_in_proj): the RMSNorm prologue with the conv1d
+// update applied to the xBC columns as they are stored.
+constexpr int kFuseNone = 0, kFuseResidual = 1, kFuseNorm = 2, kFuseGated = 3, kFuseNormConv = 4;
 
 template <int MR, int J, int RB, int SF, int FU>
 struct Gemv {
@@ -108,9 +110,21 @@ struct Gemv {
             r.s[j] = kvalid[j] ? block_scale<SF>(S, scale_index(n0, kch[j], k_blocks)) : 0.0f;
     }
 
-    // The output element o: BF16 of the sum, or the residual epilogue.
+    // Output (m, n): BF16 of the sum, the residual epilogue, or on the conv
+    // columns the conv1d update of the channel with this BF16 output as its
+    // new input (each channel's output is stored by exactly one lane).
     __device__ static __forceinline__ void store(uint16_t* __restrict__ out, const uint16_t* __restrict__ res,
-                                                 int64_t o, float val) {
+                                                 const Fusion& fu, int m, int n, int N, float val) {
+        const int64_t o = static_cast<int64_t>(m) * N + n;
+        if constexpr (FU == kFuseNormConv) {
+            const int c = n - fu.conv_begin;
+            if (c >= 0 && c < fu.conv_dim) {
+                out[o] = conv_update_channel(fu.conv_state + (static_cast<int64_t>(m) * fu.conv_dim + c) * fu.d_conv,
+                                             fu.conv_weight + static_cast<int64_t>(c) * fu.d_conv, fu.conv_bias[c],
+                                             f32_to_bf16_bits(val), fu.d_conv);
+                return;
+            }
+        }
         if constexpr (FU != kFuseNone)
             if (res) {
                 out[o] = residual_out(val, res[o]);
@@ -122,7 +136,7 @@ struct Gemv {
     __device__ static __forceinline__ void process(const Regs& r, const uint32_t (&a)[MR][J][8],
                                                    float (*red)[kMaxWaves][V], int parity,
                                                    uint16_t* __restrict__ out, const uint16_t* __restrict__ res,
-                                                   const void* __restrict__ S,
+                                                   const Fusion& fu, const void* __restrict__ S,
                                                    int g, int N, int lane, int wave, int nwaves) {
         float v[P];
 #pragma unroll
@@ -152,7 +166,7 @@ struct Gemv {
             if (holder) {
                 const int i = idx / MR, m = idx % MR;
                 if (n0 + i < N)
-                    store(out, res, static_cast<int64_t>(m) * N + n0 + i, v[0] * row_scale<SF>(S, n0 + i));
+                    store(out, res, fu, m, n0 + i, N, v[0] * row_scale<SF>(S, n0 + i));
             }
         } else {
             if (holder) red[parity][wave][idx] = v[0];
@@ -162,7 +176,7 @@ struct Gemv {
                 for (int w = 0; w < nwaves; ++w) tot += red[parity][w][lane];
                 const int i = lane / MR, m = lane % MR;
                 if (n0 + i < N)
-                    store(out, res, static_cast<int64_t>(m) * N + n0 + i, tot * row_scale<SF>(S, n0 + i));
+                    store(out, res, fu, m, n0 + i, N, tot * row_scale<SF>(S, n0 + i));
             }
             // The next group writes red[parity ^ 1]; red[parity] is written
             // again only after the next barrier, which wave 0 reaches after
@@ -273,7 +287,7 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             const void* __restrict__ S, uint16_t* __restrict__ out,
             int N, int K, int groups_per_block, Fusion fu) {
     using G = Gemv<MR, J, RB, SF, FU>;
-    constexpr bool kNorm = FU == kFuseNorm || FU == kFuseGated;
+    constexpr bool kNorm = FU == kFuseNorm || FU == kFuseGated || FU == kFuseNormConv;
     __shared__ float red[2][kMaxWaves][G::V];
 
     const int lane = threadIdx.x & 63;
@@ -329,11 +343,11 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     int parity = 0;
     for (int g = g_begin; g < g_end; g += 2) {
         if (g + 1 < g_end) G::load(rb, W, S, g + 1, N, K, k_blocks, kch, kvalid);
-        G::process(ra, a, red, parity, out, res, S, g, N, lane, wave, nwaves);
+        G::process(ra, a, red, parity, out, res, fu, S, g, N, lane, wave, nwaves);
         parity ^= 1;
         if (g + 1 >= g_end) break;
         if (g + 2 < g_end) G::load(ra, W, S, g + 2, N, K, k_blocks, kch, kvalid);
-        G::process(rb, a, red, parity, out, res, S, g + 1, N, lane, wave, nwaves);
+        G::process(rb, a, red, parity, out, res, fu, S, g + 1, N, lane, wave, nwaves);
         parity ^= 1;
     }
 }
@@ -352,9 +366,16 @@ constexpr int rows_per_group(int mr, int j) {
     return rb;
 }
 
+// The in_proj form's conv epilogue needs a few more registers: a group of
+// 64 partial sums per lane (4 rows x 16) is halved so that it does not spill.
+constexpr int rows_for(int mr, int j, int fu) {
+    const int rb = rows_per_group(mr, j);
+    return fu == kFuseNormConv && mr * rb >= 64 ? rb / 2 : rb;
+}
+
 template <int MR, int J, int SF, int FU>
 gemv_fn pick_j() {
-    return &gemv_kernel<MR, J, rows_per_group(MR, J), SF, FU>;
+    return &gemv_kernel<MR, J, rows_for(MR, J, FU), SF, FU>;
 }
 
 // The fused kernels hold the norm's operands beside the activations; they
@@ -380,7 +401,7 @@ struct Choice {
 
 template <int MR, int SF, int FU>
 Choice choose(int j) {
-    return {pick<MR, SF, FU>(j), j == 2 ? rows_per_group(MR, 2) : rows_per_group(MR, 1)};
+    return {pick<MR, SF, FU>(j), j == 2 ? rows_for(MR, 2, FU) : rows_for(MR, 1, FU)};
 }
 
 template <int SF>
@@ -430,7 +451,7 @@ Choice select_plain(int mr, int j) {
 // checked).
 template <int SF, int FU>
 int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
-             hipStream_t stream, Fusion fu = Fusion{nullptr, nullptr, nullptr, 0, 0.0f}) {
+             hipStream_t stream, Fusion fu = Fusion{}) {
     const int mr = static_cast<int>(M);
     const int j = K > static_cast<int64_t>(kWaveK) * kMaxWaves ? 2 : 1;
     const int nwaves = static_cast<int>(ceil_div(K, static_cast<int64_t>(kWaveK) * j));
@@ -510,10 +531,51 @@ extern "C" int w8a16_gemv_fused(const void* A, const void* gate, int64_t ld_gate
     if ((norm_weight && overlaps(out, out_bytes, norm_weight, K * 2)) ||
         (gate && overlaps(out, out_bytes, gate, ((M - 1) * ld_gate + K) * 2)))
         return W8A16_ERR_ALIAS;
-    const Fusion fu{static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(norm_weight),
-                    static_cast<const uint16_t*>(residual), gate ? ld_gate : K, eps};
+    Fusion fu{};
+    fu.gate = static_cast<const uint16_t*>(gate);
+    fu.weight = static_cast<const uint16_t*>(norm_weight);
+    fu.residual = static_cast<const uint16_t*>(residual);
+    fu.ld_gate = gate ? ld_gate : K;
+    fu.eps = eps;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gate) return run_gemv<kScaleBlockBf16, kFuseGated>(A, Wq, scale, out, M, N, K, s, fu);
     if (norm_weight) return run_gemv<kScaleBlockBf16, kFuseNorm>(A, Wq, scale, out, M, N, K, s, fu);
     return run_gemv<kScaleBlockBf16, kFuseResidual>(A, Wq, scale, out, M, N, K, s, fu);
+}
+
+extern "C" int w8a16_gemv_in_proj(const void* A, const void* norm_weight, float eps, const void* Wq, const void* scale,
+                                  void* conv_state, const void* conv_weight, const void* conv_bias,
+                                  int64_t conv_begin, int64_t conv_dim, int64_t d_conv, void* out,
+                                  int64_t M, int64_t N, int64_t K, void* stream) {
+    using namespace w8a16;
+    bool noop = false;
+    int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
+    if (st != W8A16_OK) return st;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return W8A16_ERR_ARG;   // also NaN
+    if (conv_begin < 0 || conv_dim < 1 || conv_begin + conv_dim > N || d_conv < 1 || d_conv > 8)
+        return W8A16_ERR_SHAPE;
+    if (noop) return W8A16_OK;
+    if (!fused_fits(M, K)) return W8A16_ERR_SHAPE;
+    if (!norm_weight || !conv_state || !conv_weight || !conv_bias) return W8A16_ERR_NULL;
+    if (!aligned(norm_weight, 16) || !aligned(conv_state, 4) || !aligned(conv_weight, 2) || !aligned(conv_bias, 2))
+        return W8A16_ERR_ALIGN;
+    const int64_t out_bytes = M * N * 2, sb = M * conv_dim * d_conv * 4, wb = conv_dim * d_conv * 2;
+    const void* reads[] = {A, Wq, scale, norm_weight, conv_weight, conv_bias};
+    const int64_t read_bytes[] = {M * K * 2, N * K, scale_bytes(W8A16_SCALE_BLOCK_BF16, N, K), K * 2, wb, conv_dim * 2};
+    if (overlaps(out, out_bytes, norm_weight, K * 2) || overlaps(out, out_bytes, conv_state, sb) ||
+        overlaps(out, out_bytes, conv_weight, wb) || overlaps(out, out_bytes, conv_bias, conv_dim * 2))
+        return W8A16_ERR_ALIAS;
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(conv_state, sb, reads[i], read_bytes[i])) return W8A16_ERR_ALIAS;
+    Fusion fu{};
+    fu.weight = static_cast<const uint16_t*>(norm_weight);
+    fu.ld_gate = K;
+    fu.eps = eps;
+    fu.conv_state = static_cast<float*>(conv_state);
+    fu.conv_weight = static_cast<const uint16_t*>(conv_weight);
+    fu.conv_bias = static_cast<const uint16_t*>(conv_bias);
+    fu.conv_begin = static_cast<int>(conv_begin);
+    fu.conv_dim = static_cast<int>(conv_dim);
+    fu.d_conv = static_cast<int>(d_conv);
+    return run_gemv<kScaleBlockBf16, kFuseNormConv>(A, Wq, scale, out, M, N, K, static_cast<hipStream_t>(stream), fu);
 }

@@ -43,18 +43,8 @@ conv1d_update_kernel(float* __restrict__ state, const uint16_t* __restrict__ x, 
     const int c = blockIdx.x * kConvThreads + threadIdx.x;
     const int64_t b = blockIdx.y;
     if (c >= dim) return;
-    float* s = state + (b * dim + c) * d_conv;
-    const uint16_t* w = weight + static_cast<int64_t>(c) * d_conv;
-    float acc = bf16v(bias + c);
-    for (int t = 0; t + 1 < d_conv; ++t) {       // shift: the oldest input leaves
-        const float v = s[t + 1];
-        s[t] = v;
-        acc = fmaf(v, bf16v(w + t), acc);
-    }
-    const float xv = bf16v(x + b * ld_x + c);
-    s[d_conv - 1] = xv;
-    acc = fmaf(xv, bf16v(w + d_conv - 1), acc);
-    out[b * ld_out + c] = f32_to_bf16_bits(silu(acc));
+    out[b * ld_out + c] = conv_update_channel(state + (b * dim + c) * d_conv, weight + static_cast<int64_t>(c) * d_conv,
+                                              bias[c], x[b * ld_x + c], d_conv);
 }
 
 // softplus(v) = log(1 + e^v), in the form that neither overflows nor cancels.

@@ -211,6 +211,24 @@ int w8a16_conv1d_update(void* conv_state, const void* x, int64_t ld_x, const voi
                         void* out, int64_t ld_out, int64_t batch, int64_t dim, int64_t d_conv, void* stream);
 
 /*
+ * w8a16_gemv_in_proj: the in_proj of the decode step in one launch. The
+ * RMSNorm prologue of w8a16_gemv_fused (norm_weight required, no gate, no
+ * residual), the projection, and the conv1d update above applied to the
+ * output columns [conv_begin, conv_begin + conv_dim) as they are stored: for
+ * column n = conv_begin + c of row m, the channel c takes the projection's
+ * BF16 output as its new input, conv_state[m][c] is updated in place and
+ * out[m][n] receives the conv output. The other columns hold the projection
+ * (z and dt of the row [z | xBC | dt]). The result is bit-identical to
+ * w8a16_gemv_fused followed by w8a16_conv1d_update on those columns, one
+ * launch fewer. Shapes as for w8a16_gemv_fused; conv_begin + conv_dim <= N,
+ * 1 <= d_conv <= 8; conv_state 4-byte aligned, taps [conv_dim][d_conv] and
+ * bias [conv_dim] BF16, 2-byte aligned; no buffer may overlap another.
+ */
+int w8a16_gemv_in_proj(const void* A, const void* norm_weight, float eps, const void* Wq, const void* scale,
+                       void* conv_state, const void* conv_weight, const void* conv_bias, int64_t conv_begin,
+                       int64_t conv_dim, int64_t d_conv, void* out, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * w8a16_ssm_decode: for each sequence b and head h (group g = h / (heads /
  * groups)), with the conv output row xbc[b] = [x (heads*head_dim) | B
  * (groups*state) | C (groups*state)] (BF16, ld_xbc >= its width) and

@@ -280,3 +280,23 @@ def test_mamba2_step_rejections():
     assert call(out=H + 64) == binding.ERR_ALIAS
     assert call(xbc=H + 128) == binding.ERR_ALIAS                                # xbc inside the state
     assert call(out=Dp) == binding.ERR_ALIAS                                     # out over D
+
+
+def test_in_proj_rejections():
+    F = FAKE
+    A, Wn, Wq, S, St, Cw, Cb, O = (F + (i << 30) for i in range(8))
+    ip = binding.gemv_in_proj_raw
+    # gemv_in_proj(A, norm_weight, eps, Wq, scale, conv_state, conv_weight, conv_bias, begin, dim, d_conv, out, M, N, K)
+    assert ip(A, Wn, 1e-5, Wq, S, St, Cw, Cb, 100, 200, 4, O, 1, 256, 256, 0) == binding.ERR_SHAPE   # past N
+    assert ip(A, Wn, 1e-5, Wq, S, St, Cw, Cb, 0, 0, 4, O, 1, 256, 256, 0) == binding.ERR_SHAPE      # no columns
+    assert ip(A, Wn, 1e-5, Wq, S, St, Cw, Cb, 0, 64, 9, O, 1, 256, 256, 0) == binding.ERR_SHAPE     # d_conv > 8
+    assert ip(A, Wn, float("nan"), Wq, S, St, Cw, Cb, 0, 64, 4, O, 1, 256, 256, 0) == binding.ERR_ARG
+    assert ip(A, Wn, 1e-5, Wq, S, St, Cw, Cb, 0, 64, 4, O, 9, 256, 256, 0) == binding.ERR_SHAPE     # M > 8
+    assert ip(A, Wn, 1e-5, Wq, S, St, Cw, Cb, 0, 64, 4, O, 0, 256, 256, 0) == binding.OK            # no-op
+    assert ip(A, 0, 1e-5, Wq, S, St, Cw, Cb, 0, 64, 4, O, 1, 256, 256, 0) == binding.ERR_NULL
+    assert ip(A, Wn, 1e-5, Wq, S, 0, Cw, Cb, 0, 64, 4, O, 1, 256, 256, 0) == binding.ERR_NULL
+    assert ip(A, Wn, 1e-5, Wq, S, St + 2, Cw, Cb, 0, 64, 4, O, 1, 256, 256, 0) == binding.ERR_ALIGN
+    assert ip(A, Wn + 8, 1e-5, Wq, S, St, Cw, Cb, 0, 64, 4, O, 1, 256, 256, 0) == binding.ERR_ALIGN
+    assert ip(A, Wn, 1e-5, Wq, S, O + 64, Cw, Cb, 0, 64, 4, O, 1, 256, 256, 0) == binding.ERR_ALIAS  # state in out
+    assert ip(A, Wn, 1e-5, Wq, S, St, Cw, Cb, 0, 64, 4, Cw - 64, 1, 256, 256, 0) == binding.ERR_ALIAS
+    assert ip(A, Wn, 1e-5, Wq, S, A + 16, Cw, Cb, 0, 64, 4, O, 1, 256, 256, 0) == binding.ERR_ALIAS   # state over A

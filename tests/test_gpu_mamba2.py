@@ -12,6 +12,12 @@ oracle, over several tokens so that the carried states are checked too.
   exp / softplus are within a few ulp); each output within one BF16 step of
   its value plus 1e-4 of sum_n |C h| + |D x|.
 * An SSM step with dt = 0 leaves the state bit-identical.
+* in_proj with the conv epilogue (w8a16_gemv_in_proj): the conv state comes
+  out shifted bit for bit with the projection's output as its newest entry
+  (within the product tolerance of the oracle), the other columns within that
+  tolerance too, the conv outputs within one BF16 step of the oracle's conv
+  of those inputs; and, where it groups rows like w8a16_gemv_fused, bit for
+  bit the result of the two launches it replaces.
 """
 import numpy as np
 import pytest
@@ -146,3 +152,63 @@ def test_mamba2_rejections_on_device(dev):
     with pytest.raises(ValueError):
         binding.w8a16_ssm_decode(h, xbc, dt, p, p, p, groups=3)
     torch.cuda.synchronize()
+
+
+# --- in_proj with the RMSNorm prologue and the conv1d epilogue (one launch) --------------------
+
+def _in_proj_case(M, hidden, d_inner, d_xbc, heads, d_conv, seed):
+    n_in = d_inner + d_xbc + heads
+    x = inputs.activations(M, hidden, seed)
+    nw = inputs.norm_weight(hidden, seed + 1)
+    W, S = inputs.weights(n_in, hidden, 0.02, seed + 2)
+    cw, cb = inputs.conv_params(d_xbc, d_conv, seed + 3)
+    st = inputs.conv_state(M, d_xbc, d_conv, seed + 4)
+    return n_in, x, nw, W, S, cw, cb, st
+
+
+IN_PROJ_SHAPES = [  # (M, hidden, d_inner, d_xbc, heads, d_conv)
+    (1, 4096, 8192, 10240, 128, 4),     # the hidden-4096 layer
+    (2, 4096, 8192, 10240, 128, 4),
+    (3, 1024, 1024, 1536, 16, 3),
+    (4, 16384, 512, 768, 8, 4),         # two chunks per lane
+    (4, 1024, 1024, 1536, 16, 4),       # halved row groups for the conv epilogue
+    (8, 2048, 512, 640, 8, 2),
+]
+
+
+@pytest.mark.parametrize("M,hidden,d_inner,d_xbc,heads,d_conv", IN_PROJ_SHAPES)
+def test_gemv_in_proj_conv_epilogue(dev, M, hidden, d_inner, d_xbc, heads, d_conv):
+    say(f"gemv_in_proj M={M} hidden={hidden} xBC={d_xbc} d_conv={d_conv}")
+    eps = inputs.NORM_EPS
+    n_in, x, nw, W, S, cw, cb, st0 = _in_proj_case(M, hidden, d_inner, d_xbc, heads, d_conv, 9500 + M)
+    dx, dnw, dW, dS, dcw, dcb = bf(x, dev), bf(nw, dev), torch.from_numpy(W).to(dev), bf(S, dev), bf(cw, dev), bf(cb, dev)
+    d_state = f32(st0, dev)
+    got = bits(binding.w8a16_gemv_in_proj(dx, dW, dS, dnw, eps, d_state, dcw, dcb, d_inner))
+    new_state = d_state.cpu().numpy()
+    torch.cuda.synchronize()
+    conv_cols = slice(d_inner, d_inner + d_xbc)
+    # the state: shifted bit for bit, and its newest entry is the projection's output
+    assert np.array_equal(new_state[:, :, :-1].view(np.uint32), st0[:, :, 1:].view(np.uint32))
+    _, a = oracle.rmsnorm(x, nw, eps)
+    ref, den = oracle.w8a16(a, W, S)
+    new_in = new_state[:, :, -1].astype(np.float64)
+    err = np.abs(new_in - ref[:, conv_cols])
+    assert np.all(err <= 4e-3 * den[:, conv_cols] + 1e-6), "conv input (the projection) outside tolerance"
+    g = oracle.bf16_value(got)
+    other = np.ones(n_in, bool)
+    other[conv_cols] = False
+    assert np.all(np.abs(g[:, other] - ref[:, other]) <= 4e-3 * den[:, other] + 1e-6), "z / dt outside tolerance"
+    # the conv outputs: the oracle's conv of the old state with the kernel's own new inputs
+    new_bits = torch.from_numpy(new_state[:, :, -1].copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    _, want = oracle.conv1d_update(st0.astype(np.float64), new_bits, cw, cb)
+    check_step_bits(got[:, conv_cols], want, f"in_proj conv M={M}")
+    # same row groups as the fused GEMV (M <= 3, or two chunks per lane): bit-identical to the two launches
+    if M <= 3 or hidden > 8192:
+        proj = binding.w8a16_gemv_fused(dx, dW, dS, norm_weight=dnw, eps=eps)
+        d2 = f32(st0, dev)
+        conv = binding.w8a16_conv1d_update(d2, proj[:, conv_cols], dcw, dcb)
+        torch.cuda.synchronize()
+        chain = bits(proj)
+        chain[:, conv_cols] = bits(conv)
+        assert np.array_equal(got, chain)
+        assert np.array_equal(d2.cpu().numpy().view(np.uint32), new_state.view(np.uint32))
