@@ -15,9 +15,10 @@ oracle, over several tokens so that the carried states are checked too.
 * in_proj with the conv epilogue (w8a16_gemv_in_proj): the conv state comes
   out shifted bit for bit with the projection's output as its newest entry
   (within the product tolerance of the oracle), the other columns within that
-  tolerance too, the conv outputs within one BF16 step of the oracle's conv
-  of those inputs; and, where it groups rows like w8a16_gemv_fused, bit for
-  bit the result of the two launches it replaces.
+  tolerance too, the conv outputs within the oracle's chain's value plus one
+  output rounding and the effect of a one-step difference in the conv input;
+  and, where it groups rows like w8a16_gemv_fused, bit for bit the result of
+  the two launches it replaces.
 """
 import numpy as np
 import pytest
@@ -198,10 +199,18 @@ def test_gemv_in_proj_conv_epilogue(dev, M, hidden, d_inner, d_xbc, heads, d_con
     other = np.ones(n_in, bool)
     other[conv_cols] = False
     assert np.all(np.abs(g[:, other] - ref[:, other]) <= 4e-3 * den[:, other] + 1e-6), "z / dt outside tolerance"
-    # the conv outputs: the oracle's conv of the old state with the kernel's own new inputs
-    new_bits = torch.from_numpy(new_state[:, :, -1].copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    _, want = oracle.conv1d_update(st0.astype(np.float64), new_bits, cw, cb)
-    check_step_bits(got[:, conv_cols], want, f"in_proj conv M={M}")
+    # the conv outputs against the oracle's own chain (its projection, rounded to BF16, as the conv input).
+    # The kernel's input may be one BF16 step (2^-7 relative at most) from the oracle's where the product
+    # lies near a rounding midpoint; silu' < 1.1, so that moves the output by at most 1.1 |w_last| 2^-7 |x|,
+    # on top of the output's own rounding (2^-8 relative).
+    ex, want = oracle.conv1d_update(st0.astype(np.float64), oracle.bf16_rne(ref[:, conv_cols]), cw, cb)
+    x_ref = oracle.bf16_value(oracle.bf16_rne(ref[:, conv_cols]))
+    w_last = np.abs(oracle.bf16_value(cw[:, -1]))[None, :]
+    tol = 2.0 ** -8 * np.abs(ex) + 1.1 * w_last * 2.0 ** -7 * np.abs(x_ref) + 1e-30
+    cerr = np.abs(oracle.bf16_value(got[:, conv_cols]) - ex)
+    say(f"  in_proj conv M={M}: max err/tol {float(np.max(cerr / tol)):.4f}, "
+        f"{float(np.mean(got[:, conv_cols] != want)) * 100:.3f} % of outputs differ from the oracle's rounding")
+    assert np.all(cerr <= tol), "conv outputs outside tolerance"
     # same row groups as the fused GEMV (M <= 3, or two chunks per lane): bit-identical to the two launches
     if M <= 3 or hidden > 8192:
         proj = binding.w8a16_gemv_fused(dx, dW, dS, norm_weight=dnw, eps=eps)
