@@ -94,6 +94,26 @@ __device__ __forceinline__ float block_scale(const void* S, int64_t idx) {
         return 1.0f;
 }
 
+// The same scale as raw bits (BF16 bits, or FP32 bits), for callers that
+// load it early and decode it where it is used.
+template <int SF>
+__device__ __forceinline__ uint32_t block_scale_bits(const void* S, int64_t idx) {
+    if constexpr (SF == kScaleBlockBf16)
+        return static_cast<const uint16_t*>(S)[idx];
+    else if constexpr (SF == kScaleBlockF32)
+        return __float_as_uint(static_cast<const float*>(S)[idx]);
+    else
+        return __float_as_uint(1.0f);
+}
+
+template <int SF>
+__device__ __forceinline__ float scale_from_bits(uint32_t bits) {
+    if constexpr (SF == kScaleBlockBf16)
+        return bf16_bits_to_f32(bits);
+    else
+        return __uint_as_float(bits);
+}
+
 // Scale of weight row n in format SF: the FP32 [N] entry, 1 for the block formats.
 template <int SF>
 __device__ __forceinline__ float row_scale(const void* S, int64_t n) {
@@ -183,21 +203,46 @@ __device__ __forceinline__ uint16_t residual_out(float sum, uint16_t residual) {
     return residual_add_bits(f32_to_bf16_bits(sum), residual);
 }
 
+constexpr int kMaxConvTaps = 8;        // d_conv at most (checked by the entry points)
+
 // conv1d update of one channel (nemotron_mamba2.rs module docs, forward step
 // 3): the FP32 state s[0..d_conv) of the last inputs, oldest first, is
 // shifted and takes the new BF16 input x; returns bf16(silu(bias + sum_t
 // s[t] * w[t])), summed in tap order.
 __device__ __forceinline__ uint16_t conv_update_channel(float* s, const uint16_t* w, uint16_t bias, uint16_t x,
                                                         int d_conv) {
-    float acc = bf16_bits_to_f32(bias);
-    for (int t = 0; t + 1 < d_conv; ++t) {
-        const float v = s[t + 1];
-        s[t] = v;
-        acc = fmaf(v, bf16_bits_to_f32(w[t]), acc);
+    // Every load first, then the sums, then the stores: the state and tap
+    // reads are one memory round trip instead of one per tap. The first 4
+    // taps are read unconditionally (a tap past d_conv re-reads the last
+    // one and is not used), so no branch makes the compiler wait for each
+    // value as it is loaded; taps 4..7 only when d_conv has them.
+    float sv[kMaxConvTaps];
+    uint32_t wb[kMaxConvTaps];
+#pragma unroll
+    for (int t = 0; t < kMaxConvTaps; ++t) {
+        if (t < 4 || t < d_conv) {
+            const int i = min(t, d_conv - 1);
+            sv[t] = s[i];
+            wb[t] = w[i];
+        } else {
+            sv[t] = 0.0f;
+            wb[t] = 0u;
+        }
     }
+    float wv[kMaxConvTaps];
+#pragma unroll
+    for (int t = 0; t < kMaxConvTaps; ++t) wv[t] = bf16_bits_to_f32(wb[t]);
     const float xv = bf16_bits_to_f32(x);
-    s[d_conv - 1] = xv;
-    acc = fmaf(xv, bf16_bits_to_f32(w[d_conv - 1]), acc);
+    float acc = bf16_bits_to_f32(bias);
+#pragma unroll
+    for (int t = 0; t + 1 < kMaxConvTaps; ++t)
+        if (t + 1 < d_conv) acc = fmaf(sv[t + 1], wv[t], acc);
+#pragma unroll
+    for (int t = 0; t < kMaxConvTaps; ++t)
+        if (t + 1 == d_conv) acc = fmaf(xv, wv[t], acc);
+#pragma unroll
+    for (int t = 0; t < kMaxConvTaps; ++t)
+        if (t < d_conv) s[t] = t + 1 < d_conv ? sv[t + 1] : xv;
     return f32_to_bf16_bits(silu(acc));
 }
 

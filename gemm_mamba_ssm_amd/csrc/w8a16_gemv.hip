@@ -40,6 +40,9 @@ namespace w8a16 {
 namespace {
 
 constexpr int kChunk = 16;             // K values (bytes of W) per lane per load
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as zero
+constexpr int kBufferFlags = 0x00020000;        // raw buffer, 32-bit data format
+constexpr int kNonTemporal = 2;                 // cache policy of the weight stream: read once
 constexpr int kWaveK = 64 * kChunk;    // K values covered by one wave-wide load
 constexpr int kMaxWaves = 8;           // 512 threads: up to 256 VGPRs per lane
 constexpr int kWavesPerCu = 8;         // resident waves per CU the grid aims for
@@ -88,26 +91,34 @@ struct Gemv {
 
     struct Regs {
         u32x4_t w[RB][J];
-        float s[J];
+        uint32_t s_bits[J];        // the block scales' bits, decoded where they are used
     };
 
     __device__ static __forceinline__ void load(Regs& r, const uint8_t* __restrict__ W,
                                                 const void* __restrict__ S, int g, int N, int K,
                                                 int k_blocks, const int (&kch)[J], const bool (&kvalid)[J]) {
         const int n0 = g * RB;
+        // The scales first: all RB rows sit in scale row-block n0/128, and
+        // every row's sum needs them, so waiting for them must not wait for
+        // the weight rows issued after them. The load is unconditional (a
+        // lane past K reads block 0 of the row-block and its scale is
+        // replaced by 0 where it is used), so that no branch makes the
+        // compiler wait for the value right after the load.
+#pragma unroll
+        for (int j = 0; j < J; ++j) r.s_bits[j] = block_scale_bits<SF>(S, scale_index(n0, kvalid[j] ? kch[j] : 0, k_blocks));
+        __builtin_amdgcn_sched_barrier(0);
+        // Buffer loads over the group's rows: a row past N or a chunk past K
+        // lies beyond num_records and reads as zero, so there is no branch
+        // around the loads and the compiler can wait for each row alone.
+        const int rows = min(RB, N - n0);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, rows * K, kBufferFlags);
 #pragma unroll
         for (int i = 0; i < RB; ++i)
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                if (n0 + i < N && kvalid[j])
-                    r.w[i][j] = load_stream16(W + static_cast<int64_t>(n0 + i) * K + kch[j]);
-                else
-                    r.w[i][j] = u32x4_t{0u, 0u, 0u, 0u};
-            }
-        // All RB rows sit in scale row-block n0/128.
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-            r.s[j] = kvalid[j] ? block_scale<SF>(S, scale_index(n0, kch[j], k_blocks)) : 0.0f;
+            for (int j = 0; j < J; ++j)
+                r.w[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                rw, kvalid[j] ? static_cast<uint32_t>(i * K + kch[j]) : kOutOfRange, 0, kNonTemporal));
     }
 
     // Output (m, n): BF16 of the sum, the residual epilogue, or on the conv
@@ -133,7 +144,7 @@ struct Gemv {
         out[o] = f32_to_bf16_bits(val);
     }
 
-    __device__ static __forceinline__ void process(const Regs& r, const uint32_t (&a)[MR][J][8],
+    __device__ static __forceinline__ void process(const Regs& r, const uint32_t (&a)[MR][J][8], const bool (&kvalid)[J],
                                                    float (*red)[kMaxWaves][V], int parity,
                                                    uint16_t* __restrict__ out, const uint16_t* __restrict__ res,
                                                    const Fusion& fu, const void* __restrict__ S,
@@ -142,7 +153,8 @@ struct Gemv {
 #pragma unroll
         for (int i = 0; i < P; ++i) v[i] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < J; ++j)
+        for (int j = 0; j < J; ++j) {
+            const float sj = kvalid[j] ? scale_from_bits<SF>(r.s_bits[j]) : 0.0f;
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 bf16x2_t wv[8];
@@ -154,9 +166,10 @@ struct Gemv {
                     for (int t = 0; t < 8; ++t)
                         p = __builtin_amdgcn_fdot2_f32_bf16(
                             wv[t], __builtin_bit_cast(bf16x2_t, a[m][j][t]), p, false);
-                    v[i * MR + m] = fmaf(p, r.s[j], v[i * MR + m]);
+                    v[i * MR + m] = fmaf(p, sj, v[i * MR + m]);
                 }
             }
+        }
         butterfly<P, P, 32>(v, lane);
 
         const int idx = lane >> kLaneShift;                       // value this lane now holds
@@ -308,23 +321,25 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
         kvalid[j] = kch[j] < K;
     }
 
-    // The first group's weights go first (the activations arrive from L2
-    // meanwhile), except with a norm prologue, which must not wait for them.
+    // Activations of this lane's chunks, as packed BF16 pairs (k, k+1). They
+    // are loaded before the first group's weights: a wave's memory loads
+    // complete in issue order, so this way the first row's products wait
+    // for the activations and that row only, and each later row is reduced
+    // as it arrives while the rest of the group is still streaming in.
+    // Chunks past K read as zero (beyond num_records).
     typename G::Regs ra, rb;
-    if constexpr (!kNorm) G::load(ra, W, S, g_begin, N, K, k_blocks, kch, kvalid);
-
-    // Activations of this lane's chunks, as packed BF16 pairs (k, k+1).
     uint32_t a[MR][J][8];
+    const __amdgpu_buffer_rsrc_t rsrc_a =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, MR * K * 2, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-            u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-            if (kvalid[j]) {
-                const uint16_t* p = A + static_cast<int64_t>(m) * K + kch[j];
-                lo = load16(p);
-                hi = load16(p + 8);
-            }
+            const uint32_t off = static_cast<uint32_t>((m * K + kch[j]) * 2);
+            const u32x4_t lo = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, kvalid[j] ? off : kOutOfRange, 0, 0));
+            const u32x4_t hi = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, kvalid[j] ? off + 16 : kOutOfRange, 0, 0));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 a[m][j][t] = lo[t];
@@ -337,17 +352,19 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
         no.issue(fu, K, kch, kvalid);
         G::load(ra, W, S, g_begin, N, K, k_blocks, kch, kvalid);
         no.apply(a, fu, K, kch, kvalid, lane, wave, nwaves);
+    } else {
+        G::load(ra, W, S, g_begin, N, K, k_blocks, kch, kvalid);
     }
     const uint16_t* res = FU != kFuseNone ? fu.residual : nullptr;
 
     int parity = 0;
     for (int g = g_begin; g < g_end; g += 2) {
         if (g + 1 < g_end) G::load(rb, W, S, g + 1, N, K, k_blocks, kch, kvalid);
-        G::process(ra, a, red, parity, out, res, fu, S, g, N, lane, wave, nwaves);
+        G::process(ra, a, kvalid, red, parity, out, res, fu, S, g, N, lane, wave, nwaves);
         parity ^= 1;
         if (g + 1 >= g_end) break;
         if (g + 2 < g_end) G::load(ra, W, S, g + 2, N, K, k_blocks, kch, kvalid);
-        G::process(rb, a, red, parity, out, res, fu, S, g + 1, N, lane, wave, nwaves);
+        G::process(rb, a, kvalid, red, parity, out, res, fu, S, g + 1, N, lane, wave, nwaves);
         parity ^= 1;
     }
 }
@@ -552,7 +569,7 @@ extern "C" int w8a16_gemv_in_proj(const void* A, const void* norm_weight, float 
     int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
     if (st != W8A16_OK) return st;
     if (!(eps >= 0.0f) || eps > 3.0e38f) return W8A16_ERR_ARG;   // also NaN
-    if (conv_begin < 0 || conv_dim < 1 || conv_begin + conv_dim > N || d_conv < 1 || d_conv > 8)
+    if (conv_begin < 0 || conv_dim < 1 || conv_begin + conv_dim > N || d_conv < 1 || d_conv > kMaxConvTaps)
         return W8A16_ERR_SHAPE;
     if (noop) return W8A16_OK;
     if (!fused_fits(M, K)) return W8A16_ERR_SHAPE;

@@ -29,7 +29,7 @@ namespace w8a16 {
 namespace {
 
 constexpr int kConvThreads = 256;
-constexpr int kMaxConv = 8;            // d_conv at most
+constexpr int kMaxConv = kMaxConvTaps;   // d_conv at most
 constexpr int kRowsPerWg = 8;          // SSM state rows (h, p) per workgroup
 constexpr int kLanesPerRow = 32;
 constexpr int kMaxState = 256;         // 2 chunks of 4 states per lane
