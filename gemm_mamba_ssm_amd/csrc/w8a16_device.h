@@ -204,45 +204,49 @@ __device__ __forceinline__ uint16_t residual_out(float sum, uint16_t residual) {
 }
 
 constexpr int kMaxConvTaps = 8;        // d_conv at most (checked by the entry points)
+constexpr int kConvFastTaps = 4;       // d_conv up to this reads its operands in one round trip
 
 // conv1d update of one channel (nemotron_mamba2.rs module docs, forward step
 // 3): the FP32 state s[0..d_conv) of the last inputs, oldest first, is
 // shifted and takes the new BF16 input x; returns bf16(silu(bias + sum_t
 // s[t] * w[t])), summed in tap order.
-__device__ __forceinline__ uint16_t conv_update_channel(float* s, const uint16_t* w, uint16_t bias, uint16_t x,
+// For d_conv <= 4 (the Mamba-2 layers) every operand is loaded before the
+// sums and stores, one memory round trip: the 4 state values and taps are
+// read unconditionally (a tap past d_conv re-reads the last one and is not
+// used), so no branch makes the compiler wait for each value as it arrives.
+// Longer convolutions take the taps one by one, in the same order.
+__device__ __forceinline__ uint16_t conv_update_channel(float* s, const uint16_t* w, const uint16_t* bias_p, uint16_t x,
                                                         int d_conv) {
-    // Every load first, then the sums, then the stores: the state and tap
-    // reads are one memory round trip instead of one per tap. The first 4
-    // taps are read unconditionally (a tap past d_conv re-reads the last
-    // one and is not used), so no branch makes the compiler wait for each
-    // value as it is loaded; taps 4..7 only when d_conv has them.
-    float sv[kMaxConvTaps];
-    uint32_t wb[kMaxConvTaps];
+    const float xv = bf16_bits_to_f32(x);
+    if (d_conv <= kConvFastTaps) {
+        float sv[kConvFastTaps];
+        uint32_t wb[kConvFastTaps];
 #pragma unroll
-    for (int t = 0; t < kMaxConvTaps; ++t) {
-        if (t < 4 || t < d_conv) {
+        for (int t = 0; t < kConvFastTaps; ++t) {
             const int i = min(t, d_conv - 1);
             sv[t] = s[i];
             wb[t] = w[i];
-        } else {
-            sv[t] = 0.0f;
-            wb[t] = 0u;
         }
+        float acc = bf16_bits_to_f32(*bias_p);
+#pragma unroll
+        for (int t = 0; t + 1 < kConvFastTaps; ++t)
+            if (t + 1 < d_conv) acc = fmaf(sv[t + 1], bf16_bits_to_f32(wb[t]), acc);
+#pragma unroll
+        for (int t = 0; t < kConvFastTaps; ++t)
+            if (t + 1 == d_conv) acc = fmaf(xv, bf16_bits_to_f32(wb[t]), acc);
+#pragma unroll
+        for (int t = 0; t < kConvFastTaps; ++t)
+            if (t < d_conv) s[t] = t + 1 < d_conv ? sv[t + 1] : xv;
+        return f32_to_bf16_bits(silu(acc));
     }
-    float wv[kMaxConvTaps];
-#pragma unroll
-    for (int t = 0; t < kMaxConvTaps; ++t) wv[t] = bf16_bits_to_f32(wb[t]);
-    const float xv = bf16_bits_to_f32(x);
-    float acc = bf16_bits_to_f32(bias);
-#pragma unroll
-    for (int t = 0; t + 1 < kMaxConvTaps; ++t)
-        if (t + 1 < d_conv) acc = fmaf(sv[t + 1], wv[t], acc);
-#pragma unroll
-    for (int t = 0; t < kMaxConvTaps; ++t)
-        if (t + 1 == d_conv) acc = fmaf(xv, wv[t], acc);
-#pragma unroll
-    for (int t = 0; t < kMaxConvTaps; ++t)
-        if (t < d_conv) s[t] = t + 1 < d_conv ? sv[t + 1] : xv;
+    float acc = bf16_bits_to_f32(*bias_p);
+    for (int t = 0; t + 1 < d_conv; ++t) {
+        const float v = s[t + 1];
+        s[t] = v;
+        acc = fmaf(v, bf16_bits_to_f32(w[t]), acc);
+    }
+    s[d_conv - 1] = xv;
+    acc = fmaf(xv, bf16_bits_to_f32(w[d_conv - 1]), acc);
     return f32_to_bf16_bits(silu(acc));
 }
 

@@ -107,18 +107,23 @@ struct Gemv {
 #pragma unroll
         for (int j = 0; j < J; ++j) r.s_bits[j] = block_scale_bits<SF>(S, scale_index(n0, kvalid[j] ? kch[j] : 0, k_blocks));
         __builtin_amdgcn_sched_barrier(0);
-        // Buffer loads over the group's rows: a row past N or a chunk past K
-        // lies beyond num_records and reads as zero, so there is no branch
-        // around the loads and the compiler can wait for each row alone.
+        // Buffer loads over the group's rows, so there is no branch around
+        // them and the compiler can wait for each row alone: a chunk past K
+        // gets an offset past num_records and reads as zero; a row past N
+        // re-reads the group's last row (the scalar offset), and its sum is
+        // never stored. The lane offset is the same for every row.
         const int rows = min(RB, N - n0);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, rows * K, kBufferFlags);
+        uint32_t voff[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) voff[j] = kvalid[j] ? static_cast<uint32_t>(kch[j]) : kOutOfRange;
 #pragma unroll
         for (int i = 0; i < RB; ++i)
 #pragma unroll
             for (int j = 0; j < J; ++j)
                 r.w[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                rw, kvalid[j] ? static_cast<uint32_t>(i * K + kch[j]) : kOutOfRange, 0, kNonTemporal));
+                                rw, voff[j], min(i, rows - 1) * K, kNonTemporal));
     }
 
     // Output (m, n): BF16 of the sum, the residual epilogue, or on the conv
@@ -131,7 +136,7 @@ struct Gemv {
             const int c = n - fu.conv_begin;
             if (c >= 0 && c < fu.conv_dim) {
                 out[o] = conv_update_channel(fu.conv_state + (static_cast<int64_t>(m) * fu.conv_dim + c) * fu.d_conv,
-                                             fu.conv_weight + static_cast<int64_t>(c) * fu.d_conv, fu.conv_bias[c],
+                                             fu.conv_weight + static_cast<int64_t>(c) * fu.d_conv, fu.conv_bias + c,
                                              f32_to_bf16_bits(val), fu.d_conv);
                 return;
             }

@@ -44,7 +44,7 @@ conv1d_update_kernel(float* __restrict__ state, const uint16_t* __restrict__ x, 
     const int64_t b = blockIdx.y;
     if (c >= dim) return;
     out[b * ld_out + c] = conv_update_channel(state + (b * dim + c) * d_conv, weight + static_cast<int64_t>(c) * d_conv,
-                                              bias[c], x[b * ld_x + c], d_conv);
+                                              bias + c, x[b * ld_x + c], d_conv);
 }
 
 // softplus(v) = log(1 + e^v), in the form that neither overflows nor cancels.

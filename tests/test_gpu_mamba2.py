@@ -174,6 +174,7 @@ IN_PROJ_SHAPES = [  # (M, hidden, d_inner, d_xbc, heads, d_conv)
     (4, 16384, 512, 768, 8, 4),         # two chunks per lane
     (4, 1024, 1024, 1536, 16, 4),       # halved row groups for the conv epilogue
     (8, 2048, 512, 640, 8, 2),
+    (2, 1024, 1024, 1536, 16, 6),       # d_conv > 4: the taps one by one
 ]
 
 
