@@ -123,11 +123,6 @@ __device__ __forceinline__ float row_scale(const void* S, int64_t n) {
         return 1.0f;
 }
 
-// 16-byte global load that bypasses cache retention (weights are streamed once).
-__device__ __forceinline__ u32x4_t load_stream16(const uint8_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
-
 __device__ __forceinline__ u32x4_t load16(const void* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
 }

@@ -29,7 +29,6 @@ namespace w8a16 {
 namespace {
 
 constexpr int kConvThreads = 256;
-constexpr int kMaxConv = kMaxConvTaps;   // d_conv at most
 constexpr int kRowsPerWg = 8;          // SSM state rows (h, p) per workgroup
 constexpr int kLanesPerRow = 32;
 constexpr int kMaxState = 256;         // 2 chunks of 4 states per lane
@@ -128,7 +127,7 @@ extern "C" int w8a16_conv1d_update(void* conv_state, const void* x, int64_t ld_x
                                    const void* bias, void* out, int64_t ld_out, int64_t batch, int64_t dim,
                                    int64_t d_conv, void* stream) {
     using namespace w8a16;
-    if (batch < 0 || dim < 1 || d_conv < 1 || d_conv > kMaxConv || ld_x < dim || ld_out < dim ||
+    if (batch < 0 || dim < 1 || d_conv < 1 || d_conv > kMaxConvTaps || ld_x < dim || ld_out < dim ||
         batch > 65535 || dim > INT32_MAX || ld_x > INT32_MAX || ld_out > INT32_MAX)
         return W8A16_ERR_SHAPE;
     if (batch == 0) return W8A16_OK;
