@@ -330,24 +330,24 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
         auto issue = [&](int kt, int slot) {
             const int k0 = (ks0 + kt) * TK;
             uint8_t* base = smem + slot * kStageBytes;
-            const bool full = k0 + TK <= K;
+            auto dst_a = [&](int i) { return (lds_void*)(base + i * (kThreads * 16) + wave * 1024); };
+            auto dst_w = [&](int i) { return (lds_void*)(base + kATileBytes + i * (kThreads * 16) + wave * 1024); };
+            if (k0 + TK <= K) {                        // one branch per step, not one per load
 #pragma unroll
-            for (int i = 0; i < kAChunksPerThread; ++i) {
-                lds_void* dst = (lds_void*)(base + i * (kThreads * 16) + wave * 1024);
-                if (full)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst, 16, a_off[i], k0 * 2, 0, 0);
-                else
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rsrc_a, dst, 16, (k0 + a_k[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange, 0, 0, 0);
-            }
+                for (int i = 0; i < kAChunksPerThread; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst_a(i), 16, a_off[i], k0 * 2, 0, 0);
 #pragma unroll
-            for (int i = 0; i < kWChunksPerThread; ++i) {
-                lds_void* dst = (lds_void*)(base + kATileBytes + i * (kThreads * 16) + wave * 1024);
-                if (full)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, dst, 16, w_off[i], k0, 0, 0);
-                else
+                for (int i = 0; i < kWChunksPerThread; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, dst_w(i), 16, w_off[i], k0, 0, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kAChunksPerThread; ++i)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rsrc_w, dst, 16, (k0 + w_k[i] < K) ? w_off[i] + k0 : kOutOfRange, 0, 0, 0);
+                        rsrc_a, dst_a(i), 16, (k0 + a_k[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < kWChunksPerThread; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rsrc_w, dst_w(i), 16, (k0 + w_k[i] < K) ? w_off[i] + k0 : kOutOfRange, 0, 0, 0);
             }
         };
 
