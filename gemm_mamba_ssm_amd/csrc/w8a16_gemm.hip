@@ -186,7 +186,7 @@ __device__ __forceinline__ void wait_steps(int younger) {
             return;
         }
     }
-    if (younger >= 1)
+    if (__builtin_expect(younger >= 1, 1))
         wait_vmem<C::kChunks>();
     else
         wait_vmem<0>();
@@ -332,7 +332,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
             uint8_t* base = smem + slot * kStageBytes;
             auto dst_a = [&](int i) { return (lds_void*)(base + i * (kThreads * 16) + wave * 1024); };
             auto dst_w = [&](int i) { return (lds_void*)(base + kATileBytes + i * (kThreads * 16) + wave * 1024); };
-            if (k0 + TK <= K) {                        // one branch per step, not one per load
+            if (__builtin_expect(k0 + TK <= K, 1)) {   // one branch per step, not one per load
 #pragma unroll
                 for (int i = 0; i < kAChunksPerThread; ++i)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, dst_a(i), 16, a_off[i], k0 * 2, 0, 0);
@@ -403,7 +403,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
         float s_lane = load_scales(s_base);
 
         auto fold = [&](int kb) {
-            if (kb - s_base >= 64) {
+            if (__builtin_expect(kb - s_base >= 64, 0)) {
                 s_base += 64;
                 s_lane = load_scales(s_base);
             }
@@ -434,9 +434,9 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
             constexpr bool kFirst = decltype(first_c)::value;
             wait_steps<C>(min(len - 1, kt + kStages - 2) - kt);
             lds_barrier();
-            if (kt + kStages - 1 < len) issue(kt + kStages - 1, (kSlot + kStages - 1) % kStages);
+            if (__builtin_expect(kt + kStages - 1 < len, 1)) issue(kt + kStages - 1, (kSlot + kStages - 1) % kStages);
             compute(slot_c, first_c);
-            if (!kFirst || kt + 1 == len) fold(kb0 + (kt >> 1));
+            if (!kFirst || __builtin_expect(kt + 1 == len, 0)) fold(kb0 + (kt >> 1));
         };
 
         // Every wave is done reading the stages of the previous piece.
@@ -447,14 +447,14 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
         constexpr int kUnroll = 2 * kStages;
         for (int kt = 0; kt < len; kt += kUnroll) {    // stages 0 .. kStages-1, twice
             step(std::integral_constant<int, 0>{}, std::true_type{}, kt);
-            if (kt + 1 < len) step(std::integral_constant<int, 1 % kStages>{}, std::false_type{}, kt + 1);
-            if (kt + 2 < len) step(std::integral_constant<int, 2 % kStages>{}, std::true_type{}, kt + 2);
-            if (kt + 3 < len) step(std::integral_constant<int, 3 % kStages>{}, std::false_type{}, kt + 3);
-            if (kt + 4 < len) step(std::integral_constant<int, 4 % kStages>{}, std::true_type{}, kt + 4);
-            if (kt + 5 < len) step(std::integral_constant<int, 5 % kStages>{}, std::false_type{}, kt + 5);
+            if (__builtin_expect(kt + 1 < len, 1)) step(std::integral_constant<int, 1 % kStages>{}, std::false_type{}, kt + 1);
+            if (__builtin_expect(kt + 2 < len, 1)) step(std::integral_constant<int, 2 % kStages>{}, std::true_type{}, kt + 2);
+            if (__builtin_expect(kt + 3 < len, 1)) step(std::integral_constant<int, 3 % kStages>{}, std::false_type{}, kt + 3);
+            if (__builtin_expect(kt + 4 < len, 1)) step(std::integral_constant<int, 4 % kStages>{}, std::true_type{}, kt + 4);
+            if (__builtin_expect(kt + 5 < len, 1)) step(std::integral_constant<int, 5 % kStages>{}, std::false_type{}, kt + 5);
             if constexpr (kUnroll > 6) {
-                if (kt + 6 < len) step(std::integral_constant<int, 6 % kStages>{}, std::true_type{}, kt + 6);
-                if (kt + 7 < len) step(std::integral_constant<int, 7 % kStages>{}, std::false_type{}, kt + 7);
+                if (__builtin_expect(kt + 6 < len, 1)) step(std::integral_constant<int, 6 % kStages>{}, std::true_type{}, kt + 6);
+                if (__builtin_expect(kt + 7 < len, 1)) step(std::integral_constant<int, 7 % kStages>{}, std::false_type{}, kt + 7);
             }
         }
 
