@@ -444,18 +444,23 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
 #pragma unroll
         for (int i = 0; i + 1 < kStages; ++i)
             if (i < len) issue(i, i);
-        constexpr int kUnroll = 2 * kStages;
-        for (int kt = 0; kt < len; kt += kUnroll) {    // stages 0 .. kStages-1, twice
+        constexpr int kUnroll = 2 * kStages;             // stages 0 .. kStages-1, twice
+        static_assert(kUnroll == 6, "the unrolled steps below");
+        int kt = 0;
+        for (; kt + kUnroll <= len; kt += kUnroll) {      // whole chunks: no per-step length checks
             step(std::integral_constant<int, 0>{}, std::true_type{}, kt);
-            if (__builtin_expect(kt + 1 < len, 1)) step(std::integral_constant<int, 1 % kStages>{}, std::false_type{}, kt + 1);
-            if (__builtin_expect(kt + 2 < len, 1)) step(std::integral_constant<int, 2 % kStages>{}, std::true_type{}, kt + 2);
-            if (__builtin_expect(kt + 3 < len, 1)) step(std::integral_constant<int, 3 % kStages>{}, std::false_type{}, kt + 3);
-            if (__builtin_expect(kt + 4 < len, 1)) step(std::integral_constant<int, 4 % kStages>{}, std::true_type{}, kt + 4);
-            if (__builtin_expect(kt + 5 < len, 1)) step(std::integral_constant<int, 5 % kStages>{}, std::false_type{}, kt + 5);
-            if constexpr (kUnroll > 6) {
-                if (__builtin_expect(kt + 6 < len, 1)) step(std::integral_constant<int, 6 % kStages>{}, std::true_type{}, kt + 6);
-                if (__builtin_expect(kt + 7 < len, 1)) step(std::integral_constant<int, 7 % kStages>{}, std::false_type{}, kt + 7);
-            }
+            step(std::integral_constant<int, 1 % kStages>{}, std::false_type{}, kt + 1);
+            step(std::integral_constant<int, 2 % kStages>{}, std::true_type{}, kt + 2);
+            step(std::integral_constant<int, 3 % kStages>{}, std::false_type{}, kt + 3);
+            step(std::integral_constant<int, 4 % kStages>{}, std::true_type{}, kt + 4);
+            step(std::integral_constant<int, 5 % kStages>{}, std::false_type{}, kt + 5);
+        }
+        if (kt < len) {                                     // the last, partial chunk
+            step(std::integral_constant<int, 0>{}, std::true_type{}, kt);
+            if (kt + 1 < len) step(std::integral_constant<int, 1 % kStages>{}, std::false_type{}, kt + 1);
+            if (kt + 2 < len) step(std::integral_constant<int, 2 % kStages>{}, std::true_type{}, kt + 2);
+            if (kt + 3 < len) step(std::integral_constant<int, 3 % kStages>{}, std::false_type{}, kt + 3);
+            if (kt + 4 < len) step(std::integral_constant<int, 4 % kStages>{}, std::true_type{}, kt + 4);
         }
 
         if (kb0 == 0 && kb1 == k_blocks) {        // the whole tile: write it
