@@ -327,6 +327,19 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
         // DMA of k-step ks0 + kt into stage `slot`. A full k-step passes k0
         // as the scalar offset; the K-tail step checks each lane's k and sends
         // lanes past K out of range (they load zeros).
+        // DMA of a k-step known to lie inside K (not the last k-step).
+        auto issue_full = [&](int kt, int slot) {
+            const int k0 = (ks0 + kt) * TK;
+            uint8_t* base = smem + slot * kStageBytes;
+#pragma unroll
+            for (int i = 0; i < kAChunksPerThread; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc_a, (lds_void*)(base + i * (kThreads * 16) + wave * 1024), 16, a_off[i], k0 * 2, 0, 0);
+#pragma unroll
+            for (int i = 0; i < kWChunksPerThread; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc_w, (lds_void*)(base + kATileBytes + i * (kThreads * 16) + wave * 1024), 16, w_off[i], k0, 0, 0);
+        };
         auto issue = [&](int kt, int slot) {
             const int k0 = (ks0 + kt) * TK;
             uint8_t* base = smem + slot * kStageBytes;
@@ -429,6 +442,22 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
         // (ks0 is even, so this is the first k-step of a scale block); the
         // unrolled loop below starts at multiples of 2 * kStages, so the
         // stage and the parity are static.
+        // A step of a steady chunk (one that ends at least kStages steps
+        // before the piece): the wait count is fixed, the step it issues is a
+        // full one, and it is not the last step.
+        auto steady_step = [&](auto slot_c, auto first_c, int kt) {
+            constexpr int kSlot = decltype(slot_c)::value;
+            constexpr bool kFirst = decltype(first_c)::value;
+            wait_vmem<(kStages - 2) * C::kChunks>();
+            lds_barrier();
+            issue_full(kt + kStages - 1, (kSlot + kStages - 1) % kStages);
+            compute(slot_c, first_c);
+            // kt + 1 < len here, so this folds after the odd steps only; the
+            // run-time form keeps each step its own block for the compiler
+            // (with a compile-time condition it schedules two steps as one
+            // and spills).
+            if (!kFirst || kt + 1 == len) fold(kb0 + (kt >> 1));
+        };
         auto step = [&](auto slot_c, auto first_c, int kt) {
             constexpr int kSlot = decltype(slot_c)::value;
             constexpr bool kFirst = decltype(first_c)::value;
@@ -447,6 +476,14 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
         constexpr int kUnroll = 2 * kStages;             // stages 0 .. kStages-1, twice
         static_assert(kUnroll == 6, "the unrolled steps below");
         int kt = 0;
+        for (; kt + kUnroll + kStages - 1 < len; kt += kUnroll) {   // steady chunks
+            steady_step(std::integral_constant<int, 0>{}, std::true_type{}, kt);
+            steady_step(std::integral_constant<int, 1 % kStages>{}, std::false_type{}, kt + 1);
+            steady_step(std::integral_constant<int, 2 % kStages>{}, std::true_type{}, kt + 2);
+            steady_step(std::integral_constant<int, 3 % kStages>{}, std::false_type{}, kt + 3);
+            steady_step(std::integral_constant<int, 4 % kStages>{}, std::true_type{}, kt + 4);
+            steady_step(std::integral_constant<int, 5 % kStages>{}, std::false_type{}, kt + 5);
+        }
         for (; kt + kUnroll <= len; kt += kUnroll) {      // whole chunks: no per-step length checks
             step(std::integral_constant<int, 0>{}, std::true_type{}, kt);
             step(std::integral_constant<int, 1 % kStages>{}, std::false_type{}, kt + 1);
