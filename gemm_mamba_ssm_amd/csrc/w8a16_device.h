@@ -148,9 +148,13 @@ struct Fusion {
     int conv_begin, conv_dim, d_conv;
 };
 
-// SiLU in fp32: z / (1 + e^-z).
+// SiLU in fp32: z / (1 + e^-z), with the hardware exponential and reciprocal
+// (a few ulp of fp32; every use rounds the result, or a product with it, to
+// BF16). The IEEE-exact expf and division take about five times the VALU
+// work, which showed in the gated norm prologue of the decode GEMV. Large
+// |z| is exact in the limit: e^-z -> 0 gives z, e^-z -> inf gives -0.
 __device__ __forceinline__ float silu(float z) {
-    return z / (1.0f + expf(-z));
+    return __fdividef(z, 1.0f + __expf(-z));
 }
 
 // Sum of squares of 8 BF16 values (4 packed pairs).

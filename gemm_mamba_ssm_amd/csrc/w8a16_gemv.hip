@@ -489,6 +489,16 @@ int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_
         const int rb = ceil_div(N, 4) >= 8 * cus ? 4 : 8;
         c = {rb == 4 ? &gemv_kernel<1, 1, 4, SF, FU> : &gemv_kernel<1, 1, 8, SF, FU>, rb};
         per_block = std::max<int64_t>(1, ceil_div(N, rb) / (18 * cus));
+        if constexpr (FU == kFuseNorm || FU == kFuseGated || FU == kFuseNormConv) {
+            // Every workgroup normalizes the whole activation row before its
+            // products, so the norm forms take more rows per workgroup:
+            // 8-row groups, and two of them per workgroup behind the gated
+            // norm (whose prologue also computes silu of the gate). Measured
+            // on the Mamba-2 projections: in_proj 15.2 -> 14.3 us, out_proj
+            // 10.0 -> 9.1 us.
+            c = {&gemv_kernel<1, 1, 8, SF, FU>, 8};
+            per_block = FU == kFuseGated ? 2 : 1;
+        }
     } else {
         const int64_t resident = cus * (kWavesPerCu / nwaves > 0 ? kWavesPerCu / nwaves : 1);
         per_block = ceil_div(ceil_div(N, c.rows_per_group), resident);
