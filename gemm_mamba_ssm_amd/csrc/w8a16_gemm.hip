@@ -76,9 +76,11 @@ static_assert(kScaleBlock == TN && kScaleBlock == 2 * TK, "one scale block per t
 // The skinny tiles do not pad M to 128 rows (at M = 16 that would be 8x the
 // MFMA work) and keep more workgroups and more stages in flight per CU, since
 // there the weights stream from HBM with little work per byte.
-template <int WAVES_M, int BI_, int BJ_, int WG_PER_CU, int STAGES, int MIN_SHARE>
+template <int WAVES_M, int BI_, int BJ_, int WG_PER_CU, int STAGES, int MIN_SHARE, int KSPLIT = 1>
 struct TileShape {
     static constexpr int WM = WAVES_M, WN = 4 / WAVES_M, BI = BI_, BJ = BJ_;
+    static constexpr int kSplit = KSPLIT;                      // k-groups of 4 waves per workgroup
+    static constexpr int kThreadsWg = kThreads * KSPLIT;
     static constexpr int TM = WM * BI * 32;
     static constexpr int kWgPerCu = WG_PER_CU;                 // resident workgroups per CU
     static constexpr int kStages = STAGES;                     // LDS ring (kStages - 1 steps in flight)
@@ -92,10 +94,16 @@ struct TileShape {
     static constexpr int kMinShareBlocks = MIN_SHARE;          // fewest k-blocks a shared tile hands one workgroup
     static_assert(WN * BJ * 32 == TN, "4 waves cover the 128 columns");
     static_assert(kAChunksPerThread >= 1 && kATileBytes % (16 * kThreads) == 0, "whole DMA chunks per thread");
-    static_assert(kStages * kStageBytes * kWgPerCu <= 160 * 1024, "LDS of the resident workgroups");
+    static_assert(kStages * kStageBytes * kWgPerCu * KSPLIT <= 160 * 1024, "LDS of the resident workgroups");
+    static_assert(KSPLIT == 1 || (KSPLIT == 2 && TM * TN * 4 <= 2 * kStages * kStageBytes), "combine buffer in LDS");
     static_assert((kStages - 2) * kChunks < 64, "vmcnt field");
 };
 using BigTile = TileShape<2, 2, 2, 2, 3, 4>;
+// The 128 x 128 tile with the k-range of every tile split between two groups
+// of 4 waves in one workgroup (one workgroup per CU), added through LDS at the
+// end: for as many tiles as CUs, no partial tiles go through memory and no
+// combine kernel runs. Whole tiles only, with a multiple of 4 k-steps.
+using BigSplit = TileShape<2, 2, 2, 1, 3, 4, 2>;
 using Skinny64 = TileShape<1, 2, 1, 3, 3, 4>;
 using Skinny32 = TileShape<1, 1, 1, 4, 3, 4>;
 
@@ -209,11 +217,16 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
     // attach alias scopes to LDS accesses, after which it waits for every
     // in-flight DMA before each LDS read (the explicit waits below already
     // order them).
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+    constexpr int KS = C::kSplit;
+    __shared__ __attribute__((aligned(16))) uint8_t smem_all[KS * kStages * kStageBytes];
 
     const int G = gridDim.x;
     const int w = xcd_remap(blockIdx.x, G);
-    const int tid = threadIdx.x, lane = tid & 63;
+    // k-group g of the workgroup (KS = 2) has its own LDS stages and its own
+    // half of every tile's k-steps; wave and tid are local to the group.
+    const int kgroup = KS == 2 ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kThreads) : 0;
+    uint8_t* const smem = smem_all + kgroup * (kStages * kStageBytes);
+    const int tid = threadIdx.x % kThreads, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int li = lane & 31, lg = lane >> 5;
@@ -313,8 +326,12 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
         }
         const int tm = t % sc.tiles_m, tn = t / sc.tiles_m;
         const int m0 = tm * TM, n0 = tn * TN;
-        const int ks0 = 2 * kb0;                       // first k-step (even)
-        const int len = min(2 * kb1, nk) - ks0;        // k-steps in this piece (>= 1)
+        // k-steps [ks0, ks0 + len) of this piece (ks0 even, len >= 1); with
+        // two k-groups (whole tiles, a multiple of 4 k-steps) group g takes
+        // the g-th half, which starts a scale block.
+        const int len = (min(2 * kb1, nk) - 2 * kb0) / KS;
+        const int ks0 = 2 * kb0 + kgroup * len;
+        kb0 += kgroup * (len / 2);
 
         // Buffer resources over this tile's rows of A and W: rows past M or
         // N lie beyond num_records and read as zero.
@@ -500,7 +517,33 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
             if (kt + 4 < len) step(std::integral_constant<int, 4 % kStages>{}, std::true_type{}, kt + 4);
         }
 
-        if (kb0 == 0 && kb1 == k_blocks) {        // the whole tile: write it
+        if constexpr (KS == 2) {
+            // Group 1's sums go through LDS (lane-major, no bank conflicts)
+            // and group 0 adds them to its own, k order kept, and writes.
+            lds_barrier();                          // every wave is done with the stages
+            float* xs = reinterpret_cast<float*>(smem_all);
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        float* x = xs + ((wave * BI * BJ + bi * BJ + bj) * 16 + v) * 64 + lane;
+                        if (kgroup == 1) *x = acc[bi][bj][v];
+                    }
+            lds_barrier();
+            if (kgroup == 0) {
+#pragma unroll
+                for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            acc[bi][bj][v] += xs[((wave * BI * BJ + bi * BJ + bj) * 16 + v) * 64 + lane];
+                store_tile(acc, m0, n0);
+            }
+            continue;
+        } else if (kb0 == 0 && kb1 == k_blocks) {        // the whole tile: write it
             store_tile(acc, m0, n0);
             continue;
         }
@@ -529,7 +572,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
 // One kernel per (tile shape, scale format, residual); suffixes: s1 = FP32
 // block scales, r = FP32 row scales, res = residual epilogue.
 #define W8A16_GEMM_KERNEL(NAME, C, SF, RES)                                                          \
-    __global__ void __launch_bounds__(kThreads, C::kWgPerCu)                                         \
+    __global__ void __launch_bounds__(C::kThreadsWg, C::kWgPerCu)                                    \
     NAME(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,   \
          const uint16_t* __restrict__ res, uint16_t* __restrict__ out, float* __restrict__ partials,  \
          int M, int N, int K, Schedule sc) {                                                         \
@@ -552,6 +595,10 @@ W8A16_GEMM_KERNEL(gemm_kernel_32_r, Skinny32, kScaleRowF32, false)
 W8A16_GEMM_KERNEL(gemm_kernel_128_res, BigTile, kScaleBlockBf16, true)
 W8A16_GEMM_KERNEL(gemm_kernel_64_res, Skinny64, kScaleBlockBf16, true)
 W8A16_GEMM_KERNEL(gemm_kernel_32_res, Skinny32, kScaleBlockBf16, true)
+W8A16_GEMM_KERNEL(gemm_kernel_128k2, BigSplit, kScaleBlockBf16, false)
+W8A16_GEMM_KERNEL(gemm_kernel_128k2_s1, BigSplit, kScaleBlockF32, false)
+W8A16_GEMM_KERNEL(gemm_kernel_128k2_r, BigSplit, kScaleRowF32, false)
+W8A16_GEMM_KERNEL(gemm_kernel_128k2_res, BigSplit, kScaleBlockBf16, true)
 #undef W8A16_GEMM_KERNEL
 
 // Combine of the split tiles. The host lists, for every split tile, the
@@ -718,13 +765,22 @@ int run_gemm(const void* A, const void* Wq, const void* scale, const void* resid
     const int k_blocks = static_cast<int>(ceil_div(K, kScaleBlockHost));
     const int slots = std::min(C::kWgPerCu * device_cu_count(), kMaxSplits);
     Schedule sc;
-    const int grid = plan(tiles, tiles_m, k_blocks, slots, C::kMinShareBlocks, &sc);
+    int grid;
+    if constexpr (C::kSplit == 2) {
+        sc = Schedule{};                             // whole tiles, one per workgroup (tiles <= slots)
+        sc.tiles_m = static_cast<int>(tiles_m);
+        sc.k_blocks = k_blocks;
+        sc.full_rounds = 1;
+        grid = static_cast<int>(tiles);
+    } else {
+        grid = plan(tiles, tiles_m, k_blocks, slots, C::kMinShareBlocks, &sc);
+    }
     Workspace ws;
     if (sc.shared_groups > 0) {
         const int st = workspace_for(s, static_cast<size_t>(2) * slots * C::kTileFloats * sizeof(float), &ws);
         if (st != W8A16_OK) return st;
     }
-    int st = launch(GemmKernel<C, SF, RES>::fn, dim3(static_cast<unsigned>(grid)), dim3(kThreads), s,
+    int st = launch(GemmKernel<C, SF, RES>::fn, dim3(static_cast<unsigned>(grid)), dim3(C::kThreadsWg), s,
                     static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
                     static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out), ws.partials,
                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), sc);
@@ -743,6 +799,12 @@ int gemm_by_shape(const void* A, const void* Wq, const void* scale, const void* 
     if (skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
     if (M <= Skinny32::TM) return run_gemm<Skinny32, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
     if (M <= Skinny64::TM) return run_gemm<Skinny64, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
+    // About as many 128 x 128 tiles as CUs (at least three quarters of them,
+    // so no more than a quarter idles) and whole k-steps in two equal halves
+    // of whole scale blocks: one workgroup per tile, k split inside it.
+    const int64_t tiles = ceil_div(M, BigTile::TM) * ceil_div(N, TN), cus = device_cu_count();
+    if (tiles <= cus && 4 * tiles >= 3 * cus && K % (4 * TK) == 0)
+        return run_gemm<BigSplit, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
     return run_gemm<BigTile, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
 }
 

@@ -152,14 +152,18 @@ def test_gemv_k_edges(dev, M, N, K):
 #    (whole tiles only, the last wave over a quarter full);
 #  * 32 x 128: N = 140000 gives 1094 tiles (a round of 1024 plus a split
 #    remainder), N = 166400 gives 1300 (whole tiles only);
-#  * 64 x 128: N = 98400 gives 769 tiles (a round of 768 plus one split tile).
+#  * 64 x 128: N = 98400 gives 769 tiles (a round of 768 plus one split tile);
+#  * 128 x 128 with the k-steps split between two wave groups of one
+#    workgroup (192..256 tiles on 256 CUs, K a multiple of 256): M = 200,
+#    N = 12200, K = 1280 (ragged M and N; 10 k-steps per group: a steady
+#    chunk and a partial one) and M = 256, N = 12288, K = 512 (4 per group).
 @pytest.mark.parametrize("M,N,K", [(1, 384, 256), (17, 130, 144), (127, 300, 272), (129, 1000, 1040),
                                    (300, 257, 4096), (256, 256, 128), (1, 1, 16), (64, 4096, 512),
                                    (513, 640, 1024), (130, 18560, 128), (66, 65704, 1040),
                                    (72, 78339, 1040), (65, 89603, 1040), (32, 18560, 4096), (20, 4096, 8192),
                                    (3, 140000, 1040), (5, 166400, 528), (33, 1000, 1040), (48, 18560, 2048),
                                    (40, 98400, 528), (31, 300, 4112), (16, 18560, 4096), (9, 1000, 4096),
-                                   (7, 1000, 8208), (2, 4100, 1936)])
+                                   (7, 1000, 8208), (2, 4100, 1936), (200, 12200, 1280), (256, 12288, 512)])
 def test_gemm_every_element(dev, M, N, K):
     say(f"gemm M={M} N={N} K={K}")
     A = inputs.activations(M, K, 900 + M)

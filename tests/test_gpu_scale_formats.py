@@ -70,7 +70,7 @@ GEMV_SHAPES = [(1, 1000, 1040), (1, 18560, 4096), (1, 4096, 8192), (3, 300, 1638
                (4, 1000, 1040), (8, 259, 272), (16, 18560, 4096), (9, 300, 8192), (13, 130, 3072)]
 GEMM_SHAPES = [(1, 384, 256), (16, 1000, 4096), (3, 140000, 1040), (20, 4096, 8192), (31, 300, 4112),
                (33, 1000, 1040), (40, 98400, 528), (129, 1000, 1040), (300, 257, 4096), (66, 65704, 1040),
-               (65, 89603, 1040), (513, 640, 1024)]
+               (65, 89603, 1040), (513, 640, 1024), (200, 12200, 1280)]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -113,7 +113,7 @@ def test_prefill_1k_in_proj_sampled(dev, fmt):
 
 ALL_PATHS = [("gemv", 1, 1000, 1040), ("gemv", 3, 300, 8192), ("gemv", 8, 1000, 1040), ("gemm", 16, 1000, 2048),
              ("gemm", 24, 4096, 8192), ("gemm", 50, 1000, 1040), ("gemm", 200, 1000, 1040),
-             ("gemm", 72, 78339, 1040)]
+             ("gemm", 72, 78339, 1040), ("gemm", 256, 12288, 512)]
 ENTRY = {"gemv": binding.w8a16_gemv, "gemm": binding.w8a16_gemm}
 
 
