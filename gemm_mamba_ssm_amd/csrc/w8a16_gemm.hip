@@ -274,12 +274,14 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
     // 32x32 MFMA result layout: lane l holds column l % 32; value v is row
     // 8*(v/4) + 4*(l/32) + v%4 of the block.
     // A per-row scale multiplies the finished sum (1 for the block formats).
-    auto store_tile = [&](const f32x16_t (&r)[BI][BJ], int m0, int n0) {
+    // ONLY_BI >= 0 writes that 32-row block of the wave's rows only.
+    auto store_tile = [&](const f32x16_t (&r)[BI][BJ], int m0, int n0, int only_bi = -1) {
         const int l = opaque(lane), li = l & 31, lg = l >> 5;
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
             for (int bj = 0; bj < BJ; ++bj) {
+                if (only_bi >= 0 && bi != only_bi) continue;
                 const int n = n0 + wn * kWaveCols + bj * 32 + li;
                 float rs = 1.0f;
                 if constexpr (SF == kScaleRowF32) rs = n < N ? row_scale<SF>(S, n) : 0.0f;
@@ -518,30 +520,30 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
         }
 
         if constexpr (KS == 2) {
-            // Group 1's sums go through LDS (lane-major, no bank conflicts)
-            // and group 0 adds them to its own, k order kept, and writes.
+            // The two groups' sums meet in LDS (lane-major, no bank
+            // conflicts): group g hands over its 32-row blocks bi != g, adds
+            // the other group's block bi == g to its own (a + b, the same
+            // bits either way round) and writes those rows.
+            static_assert(BI == 2, "one 32-row block per group");
             lds_barrier();                          // every wave is done with the stages
             float* xs = reinterpret_cast<float*>(smem_all);
+            auto slot = [&](int bi, int bj, int v) { return ((wave * BI * BJ + bi * BJ + bj) * 16 + v) * 64 + lane; };
 #pragma unroll
             for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        float* x = xs + ((wave * BI * BJ + bi * BJ + bj) * 16 + v) * 64 + lane;
-                        if (kgroup == 1) *x = acc[bi][bj][v];
-                    }
+                    for (int v = 0; v < 16; ++v)
+                        if (bi != kgroup) xs[slot(bi, bj, v)] = acc[bi][bj][v];
             lds_barrier();
-            if (kgroup == 0) {
 #pragma unroll
-                for (int bi = 0; bi < BI; ++bi)
+            for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-                    for (int bj = 0; bj < BJ; ++bj)
+                for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            acc[bi][bj][v] += xs[((wave * BI * BJ + bi * BJ + bj) * 16 + v) * 64 + lane];
-                store_tile(acc, m0, n0);
-            }
+                    for (int v = 0; v < 16; ++v)
+                        if (bi == kgroup) acc[bi][bj][v] += xs[slot(bi, bj, v)];
+            store_tile(acc, m0, n0, kgroup);
             continue;
         } else if (kb0 == 0 && kb1 == k_blocks) {        // the whole tile: write it
             store_tile(acc, m0, n0);
