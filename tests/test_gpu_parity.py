@@ -156,14 +156,17 @@ def test_gemv_k_edges(dev, M, N, K):
 #  * 128 x 128 with the k-steps split between two wave groups of one
 #    workgroup (192..256 tiles on 256 CUs, K a multiple of 256): M = 200,
 #    N = 12200, K = 1280 (ragged M and N; 10 k-steps per group: a steady
-#    chunk and a partial one) and M = 256, N = 12288, K = 512 (4 per group).
+#    chunk and a partial one) and M = 256, N = 12288, K = 512 (4 per group);
+#  * a round of 512 128 x 128 tiles and a split remainder of 88 with ragged M
+#    and N: M = 130, N = 38300, K = 512.
 @pytest.mark.parametrize("M,N,K", [(1, 384, 256), (17, 130, 144), (127, 300, 272), (129, 1000, 1040),
                                    (300, 257, 4096), (256, 256, 128), (1, 1, 16), (64, 4096, 512),
                                    (513, 640, 1024), (130, 18560, 128), (66, 65704, 1040),
                                    (72, 78339, 1040), (65, 89603, 1040), (32, 18560, 4096), (20, 4096, 8192),
                                    (3, 140000, 1040), (5, 166400, 528), (33, 1000, 1040), (48, 18560, 2048),
                                    (40, 98400, 528), (31, 300, 4112), (16, 18560, 4096), (9, 1000, 4096),
-                                   (7, 1000, 8208), (2, 4100, 1936), (200, 12200, 1280), (256, 12288, 512)])
+                                   (7, 1000, 8208), (2, 4100, 1936), (200, 12200, 1280), (256, 12288, 512),
+                                   (130, 38300, 512)])
 def test_gemm_every_element(dev, M, N, K):
     say(f"gemm M={M} N={N} K={K}")
     A = inputs.activations(M, K, 900 + M)
