@@ -786,13 +786,17 @@ int run_gemm(const void* A, const void* Wq, const void* scale, const void* resid
                     static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
                     static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out), ws.partials,
                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), sc);
-    if (st != W8A16_OK || sc.shared_groups == 0) return st;
-    SplitList list;
-    const int splits = list_splits(sc, &list);
-    if (splits == 0) return W8A16_OK;
-    return launch(&combine_kernel<C, SF, RES>, dim3(static_cast<unsigned>(splits), C::TM / kCombineRows),
-                  dim3(kThreads), s, static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), scale,
-                  static_cast<const uint16_t*>(residual), static_cast<int>(M), static_cast<int>(N), sc, list);
+    if constexpr (C::kSplit == 2) {
+        return st;                                   // whole tiles: nothing to combine
+    } else {
+        if (st != W8A16_OK || sc.shared_groups == 0) return st;
+        SplitList list;
+        const int splits = list_splits(sc, &list);
+        if (splits == 0) return W8A16_OK;
+        return launch(&combine_kernel<C, SF, RES>, dim3(static_cast<unsigned>(splits), C::TM / kCombineRows),
+                      dim3(kThreads), s, static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), scale,
+                      static_cast<const uint16_t*>(residual), static_cast<int>(M), static_cast<int>(N), sc, list);
+    }
 }
 
 template <int SF, bool RES>
