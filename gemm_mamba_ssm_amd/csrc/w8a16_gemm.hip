@@ -50,6 +50,12 @@
 //    ever waits for another and no atomics or flags are needed.
 // The shared part runs first so that the partial stores drain while the
 // workgroups go on with their whole tiles.
+//
+// When the 128 x 128 tiles about match the CUs (the out_proj's 256), one
+// workgroup of two 4-wave groups takes each tile instead: each group runs half
+// of the tile's k-steps on its own LDS stages, and the two fp32 halves are
+// added in LDS at the end, so nothing goes through memory twice and no second
+// kernel runs (BigSplit below).
 #include <map>
 #include <mutex>
 #include <type_traits>
