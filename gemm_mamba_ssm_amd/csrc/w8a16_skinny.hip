@@ -1,5 +1,5 @@
 // Skinny GEMM for the w8a16 block-scaled FP8 projection, M <= 16 rows and
-// K <= 4096:
+// K <= 8192:
 //
 //   out[m][n] = sum_k A[m][k] * E4M3(W[n][k]) * scale[n/128][k/128]
 // (Qwen3SsmLayer docs, `set_fp8_decode_weights`; NemotronMamba2Layer docs,
@@ -11,7 +11,9 @@
 // the activations in registers) with the matrix cores doing the products:
 //  * K is split across the S waves of a workgroup: wave w owns a contiguous
 //    range of at most KB 128-wide k-blocks, and holds the activations of that
-//    range (all M rows, as MFMA A operands) in registers for the whole kernel;
+//    range (all M rows, as MFMA A operands) in registers for the whole pass;
+//    K above 4096 takes two passes, each over half the k-blocks, and the
+//    second pass adds its sums to the first's (kept in LDS, fp32);
 //  * a workgroup walks a contiguous range of 16-row weight blocks; for each,
 //    every wave streams its 16 x (KB * 128)-byte slice straight from HBM into
 //    registers, D - 1 blocks ahead (a ring of D blocks; D = 2 measured
@@ -58,8 +60,9 @@ __device__ __forceinline__ void wait_vmem() {
 // MB = 16-row blocks of A (1 for M <= 16, 2 for M <= 32); KB = k-blocks per
 // wave at most (the activations of KB k-blocks take 16 * MB * KB VGPRs); D =
 // weight blocks in flight per wave; MAXW = waves per workgroup at most; SF =
-// scale format.
-template <int MB, int KB, int D, int MAXW, int SF>
+// scale format; NPASS = passes over K (1 or 2): in pass p, wave w owns the
+// k-blocks from (p * waves + w) * KB, so 16 waves cover K <= NPASS * 4096.
+template <int MB, int KB, int D, int MAXW, int SF, int NPASS>
 __global__ void __launch_bounds__(64 * MAXW)
 skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,
               const uint16_t* __restrict__ res, uint16_t* __restrict__ out, int M, int N, int K,
@@ -73,156 +76,179 @@ skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, con
     __shared__ uint16_t outs[kMaxBlocksPerWg * 256 * MB];
     // Per-row scales of the workgroup's weight rows (row format only).
     __shared__ float row_s[kRowScale ? kMaxBlocksPerWg * kRows : 1];
+    // Sums of the earlier passes, per output (two passes only).
+    static_assert(NPASS == 1 || NPASS == 2, "one or two passes over K");
+    __shared__ float part[NPASS > 1 ? kMaxBlocksPerWg * 256 * MB : 1];
 
     const int waves = blockDim.x / 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int lane = threadIdx.x % 64;
     const int r = lane % 16, g = lane / 16;
     const int k_blocks = (K + kScaleBlock - 1) / kScaleBlock;
-    const int kb0 = wave * KB;                       // this wave's k-blocks: [kb0, kb0 + KB) within k_blocks
     const int nblk = (N + kRows - 1) / kRows;
     const int blk0 = blockIdx.x * blocks_per_wg, blk1 = min(nblk, blk0 + blocks_per_wg);
     if (blk0 >= blk1) return;                        // uniform over the workgroup
 
-    // Lane's k of chunk c of the wave's j-th k-block (K % 16 == 0, so a
-    // lane's 16 bytes are all inside K or all outside).
-    auto kof = [&](int j, int c) { return (kb0 + j) * kScaleBlock + 64 * c + 16 * g; };
-    uint32_t w_off[KB][2];
-#pragma unroll
-    for (int j = 0; j < KB; ++j)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) w_off[j][c] = kof(j, c) < K ? static_cast<uint32_t>(r * K + kof(j, c)) : kOutOfRange;
-
-    // Activations of the wave's k-range, [mb][j][c][h]: 8 BF16 each.
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, M * K * 2, kBufferFlags);
-    u32x4_t a[MB][KB][2][2];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int k = kof(j, c) + 8 * h;
-                    a[mb][j][c][h] =
-                        __builtin_amdgcn_raw_buffer_load_b128(ra, k < K ? ((mb * 16 + r) * K + k) * 2 : kOutOfRange, 0, 0);
-                }
-
-    // Block scales of the workgroup's rows and the wave's k-blocks: lane l
-    // holds scale row srow0 + l / KB, k-block kb0 + l % KB (a workgroup's rows
-    // span at most kMaxBlocksPerWg * 16 / 128 + 2 scale rows). With per-row
-    // scales, the workgroup's rows' scales go to LDS instead (read after the
-    // first barrier of the loop).
+    // Per-row scales of the workgroup's rows to LDS (read after the first
+    // barrier of the loop).
     constexpr int kScaleBytes = SF == kScaleBlockBf16 ? 2 : 4;
     const int scale_elems = kRowScale ? N : ((N + kScaleBlock - 1) / kScaleBlock) * k_blocks;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(S), 0, scale_elems * kScaleBytes, kBufferFlags);
-    constexpr int kScaleRows = 64 / KB;
-    static_assert(kMaxBlocksPerWg * kRows / kScaleBlock + 2 <= kScaleRows, "one scale load per workgroup");
-    const int srow0 = blk0 * kRows / kScaleBlock;
-    float s_lane = 1.0f;
-    if constexpr (SF == kScaleBlockBf16 || SF == kScaleBlockF32) {
-        const int srow = srow0 + lane / KB, kb = kb0 + lane % KB;
-        const bool ok = srow * kScaleBlock < N && kb < k_blocks;
-        const uint32_t off = ok ? static_cast<uint32_t>(srow * k_blocks + kb) * kScaleBytes : kOutOfRange;
-        if constexpr (SF == kScaleBlockBf16)
-            s_lane = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
-        else
-            s_lane = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
-    } else {
+    if constexpr (kRowScale) {
         for (int i = threadIdx.x; i < (blk1 - blk0) * kRows; i += blockDim.x) {
             const int n = blk0 * kRows + i;
             row_s[i] = __uint_as_float(
                 __builtin_amdgcn_raw_buffer_load_b32(rs, n < N ? static_cast<uint32_t>(n) * 4 : kOutOfRange, 0, 0));
         }
     }
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, M * K * 2, kBufferFlags);
+    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    int parity = 0;
 
-    // Weights of row block b into a ring slot: [j][c], 16 bytes each; rows
-    // past N read zeros (beyond the buffer's range). Blocks past the
-    // workgroup's range get an empty range and load zeros: the loads are the
-    // same in every step (so the waits are too, also the compiler's own).
-    u32x4_t wr[D][KB][2];
-    auto issue = [&](int b, u32x4_t (&dst)[KB][2]) {
-        const bool live = b < blk1;
-        const int n0 = (live ? b : blk0) * kRows;
-        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, live ? min(kRows, N - n0) * K : 0,
-            kBufferFlags);
+    // Each pass loads its activations and scales, then streams every weight
+    // block of the workgroup through the ring; the ring drains at the end of
+    // a pass, so the waits are the same in every pass.
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int kb0 = (pass * waves + wave) * KB;      // this wave's k-blocks: [kb0, kb0 + KB) within k_blocks
+
+        // Lane's k of chunk c of the wave's j-th k-block (K % 16 == 0, so a
+        // lane's 16 bytes are all inside K or all outside).
+        auto kof = [&](int j, int c) { return (kb0 + j) * kScaleBlock + 64 * c + 16 * g; };
+        uint32_t w_off[KB][2];
 #pragma unroll
         for (int j = 0; j < KB; ++j)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) dst[j][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[j][c], 0, 0);
-    };
-#pragma unroll
-    for (int d = 0; d < D; ++d) issue(blk0 + d, wr[d]);
+            for (int c = 0; c < 2; ++c) w_off[j][c] = kof(j, c) < K ? static_cast<uint32_t>(r * K + kof(j, c)) : kOutOfRange;
 
-    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    int parity = 0;
-    // Block bb in ring slot d: wait for its loads (the later blocks' stay in
-    // flight), multiply, refill the slot with block bb + D, then reduce.
-    auto block = [&](int bb, u32x4_t (&w)[KB][2]) {
-        // Loads in flight, oldest first: this block, then the D - 1 later ones.
-        wait_vmem<(D - 1) * 2 * KB>();
-        __builtin_amdgcn_sched_barrier(0);
-        const int srow = bb * kRows / kScaleBlock;   // srow - srow0 < kScaleRows
-        f32x4_t acc[MB];
+        // Activations of the wave's k-range, [mb][j][c][h]: 8 BF16 each.
+        u32x4_t a[MB][KB][2][2];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = zero;
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            const float s =
-                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), (srow - srow0) * KB + j));
-            f32x4_t blk[MB];
+            for (int j = 0; j < KB; ++j)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const bf16x8_t bw0 = e4m3x8(w[j][c][0], w[j][c][1]), bw1 = e4m3x8(w[j][c][2], w[j][c][3]);
+                for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < 2; ++h) {
+                        const int k = kof(j, c) + 8 * h;
+                        a[mb][j][c][h] =
+                            __builtin_amdgcn_raw_buffer_load_b128(ra, k < K ? ((mb * 16 + r) * K + k) * 2 : kOutOfRange, 0, 0);
+                    }
+
+        // Block scales of the workgroup's rows and the wave's k-blocks: lane l
+        // holds scale row srow0 + l / KB, k-block kb0 + l % KB (a workgroup's rows
+        // span at most kMaxBlocksPerWg * 16 / 128 + 2 scale rows). Per-row
+        // scales are in LDS instead.
+        constexpr int kScaleRows = 64 / KB;
+        static_assert(kMaxBlocksPerWg * kRows / kScaleBlock + 2 <= kScaleRows, "one scale load per workgroup");
+        const int srow0 = blk0 * kRows / kScaleBlock;
+        float s_lane = 1.0f;
+        if constexpr (SF == kScaleBlockBf16 || SF == kScaleBlockF32) {
+            const int srow = srow0 + lane / KB, kb = kb0 + lane % KB;
+            const bool ok = srow * kScaleBlock < N && kb < k_blocks;
+            const uint32_t off = ok ? static_cast<uint32_t>(srow * k_blocks + kb) * kScaleBytes : kOutOfRange;
+            if constexpr (SF == kScaleBlockBf16)
+                s_lane = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+            else
+                s_lane = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+        }
+
+        // Weights of row block b into a ring slot: [j][c], 16 bytes each; rows
+        // past N read zeros (beyond the buffer's range). Blocks past the
+        // workgroup's range get an empty range and load zeros: the loads are the
+        // same in every step (so the waits are too, also the compiler's own).
+        u32x4_t wr[D][KB][2];
+        auto issue = [&](int b, u32x4_t (&dst)[KB][2]) {
+            const bool live = b < blk1;
+            const int n0 = (live ? b : blk0) * kRows;
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, live ? min(kRows, N - n0) * K : 0,
+                kBufferFlags);
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        blk[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, a[mb][j][c][h]), h ? bw1 : bw0,
-                            (c == 0 && h == 0) ? zero : blk[mb], 0, 0, 0);
+            for (int j = 0; j < KB; ++j)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) dst[j][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[j][c], 0, 0);
+        };
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(blk0 + d, wr[d]);
+
+        // Block bb in ring slot d: wait for its loads (the later blocks' stay in
+        // flight), multiply, refill the slot with block bb + D, then reduce.
+        auto block = [&](int bb, u32x4_t (&w)[KB][2]) {
+            // Loads in flight, oldest first: this block, then the D - 1 later ones.
+            wait_vmem<(D - 1) * 2 * KB>();
+            __builtin_amdgcn_sched_barrier(0);
+            const int srow = bb * kRows / kScaleBlock;   // srow - srow0 < kScaleRows
+            f32x4_t acc[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = zero;
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                const float s =
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), (srow - srow0) * KB + j));
+                f32x4_t blk[MB];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const bf16x8_t bw0 = e4m3x8(w[j][c][0], w[j][c][1]), bw1 = e4m3x8(w[j][c][2], w[j][c][3]);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            blk[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, a[mb][j][c][h]), h ? bw1 : bw0,
+                                (c == 0 && h == 0) ? zero : blk[mb], 0, 0, 0);
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[mb][v] = fmaf(blk[mb][v], s, acc[mb][v]);
             }
+            issue(bb + D, w);
+            // 16x16 MFMA result layout: lane l holds column l % 16, rows
+            // 4(l/16) + v. Thread t < 256 * MB then writes output (row, column) =
+            // (t / 16, t % 16): the sum over the waves in k order.
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[mb][v] = fmaf(blk[mb][v], s, acc[mb][v]);
+            for (int mb = 0; mb < MB; ++mb) red[parity][(wave * MB + mb) * 64 + lane] = acc[mb];
+            __syncthreads();
+            if (threadIdx.x < 256 * MB) {                // blockDim.x >= 256 * MB
+                const int t = threadIdx.x;
+                const int row = t / 16, col = t % 16;
+                const int mb = row / 16, rr = row % 16;
+                const int l = col + 16 * (rr / 4), v = rr % 4;
+                float sum = red[parity][mb * 64 + l][v];
+                for (int w2 = 1; w2 < waves; ++w2) sum += red[parity][(w2 * MB + mb) * 64 + l][v];
+                if (bb < blk1) {
+                    // Two passes: the first pass's sum, then the second's added to
+                    // it (the same thread writes and reads an output's slot).
+                    const int o = (bb - blk0) * 256 * MB + t;
+                    if constexpr (NPASS > 1) {
+                        if (pass == 0) part[o] = sum;
+                        else sum = part[o] + sum;
+                    }
+                    if (pass == NPASS - 1) {
+                        if constexpr (kRowScale) sum *= row_s[(bb - blk0) * kRows + col];
+                        outs[o] = f32_to_bf16_bits(sum);
+                    }
+                }
+            }
+            // red[parity] is written again two blocks later, after the next
+            // barrier, which every thread reaches only once done reading it.
+            parity ^= 1;
+        };
+        // D blocks per iteration, the last iteration padded with blocks past the
+        // range (their weights load as zeros and their outputs are dropped): the
+        // loads and waits are the same in every iteration.
+        static_assert(D >= 2 && D <= 4, "ring of 2 to 4 blocks");
+        for (int b = blk0; b < blk1; b += D) {
+            block(b, wr[0]);
+            block(b + 1, wr[1]);
+            if constexpr (D >= 3) block(b + 2, wr[2]);
+            if constexpr (D >= 4) block(b + 3, wr[3]);
         }
-        issue(bb + D, w);
-        // 16x16 MFMA result layout: lane l holds column l % 16, rows
-        // 4(l/16) + v. Thread t < 256 * MB then writes output (row, column) =
-        // (t / 16, t % 16): the sum over the waves in k order.
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) red[parity][(wave * MB + mb) * 64 + lane] = acc[mb];
-        __syncthreads();
-        if (threadIdx.x < 256 * MB) {                // blockDim.x >= 256 * MB
-            const int t = threadIdx.x;
-            const int row = t / 16, col = t % 16;
-            const int mb = row / 16, rr = row % 16;
-            const int l = col + 16 * (rr / 4), v = rr % 4;
-            float sum = red[parity][mb * 64 + l][v];
-            for (int w2 = 1; w2 < waves; ++w2) sum += red[parity][(w2 * MB + mb) * 64 + l][v];
-            if constexpr (kRowScale) sum *= row_s[((bb - blk0) * kRows + col) % (kMaxBlocksPerWg * kRows)];
-            if (bb < blk1) outs[(bb - blk0) * 256 * MB + t] = f32_to_bf16_bits(sum);
-        }
-        // red[parity] is written again two blocks later, after the next
-        // barrier, which every thread reaches only once done reading it.
-        parity ^= 1;
-    };
-    // D blocks per iteration, the last iteration padded with blocks past the
-    // range (their weights load as zeros and their outputs are dropped): the
-    // loads and waits are the same in every iteration.
-    static_assert(D >= 2 && D <= 4, "ring of 2 to 4 blocks");
-    for (int b = blk0; b < blk1; b += D) {
-        block(b, wr[0]);
-        block(b + 1, wr[1]);
-        if constexpr (D >= 3) block(b + 2, wr[2]);
-        if constexpr (D >= 4) block(b + 3, wr[3]);
+        wait_vmem<0>();                                  // the zero loads past the range
     }
-    wait_vmem<0>();                                  // the zero loads past the range
     __syncthreads();
     // Output (row, column n0 + col) of block b sits at outs[(b - blk0) * 256 *
     // MB + row * 16 + col]; threads take 16-column runs of one row.
@@ -241,10 +267,10 @@ skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, con
 
 }  // namespace
 
-// M <= 16, K <= 4096. Waves per workgroup: enough that each holds at most
-// two k-blocks of activations, at least 4. The grid aims at about 16 resident
-// waves per CU, each workgroup taking a contiguous range of 16-row weight
-// blocks.
+// M <= 16, K <= 8192 (one pass over K up to 4096, two above). Waves per
+// workgroup: enough that each holds at most two k-blocks of activations per
+// pass, at least 4. The grid aims at about 16 resident waves per CU, each
+// workgroup taking a contiguous range of 16-row weight blocks.
 int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
                 int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     if (M < 1 || M > kSkinnyMaxM) return W8A16_ERR_SHAPE;
@@ -255,7 +281,8 @@ int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const
     if (static_cast<int64_t>(kRows) * K >= static_cast<int64_t>(kOutOfRange) ||
         scale_bytes(fmt, N, K) >= static_cast<int64_t>(kOutOfRange))
         return W8A16_ERR_SHAPE;
-    int waves = static_cast<int>(ceil_div(k_blocks, kb_max));
+    const int passes = k_blocks > kMaxWaves * kb_max ? 2 : 1;
+    int waves = static_cast<int>(ceil_div(k_blocks, kb_max * passes));
     waves = std::max(waves, 4);
     const int64_t nblk = ceil_div(N, kRows);
     if (nblk > INT32_MAX) return W8A16_ERR_SHAPE;
@@ -269,11 +296,17 @@ int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const
     auto r = static_cast<const uint16_t*>(residual);
     switch (fmt) {
         case W8A16_SCALE_BLOCK_BF16:
-            return launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockBf16>, grid, block, stream, a, w, scale, r, o, m, n, k, p);
+            return passes == 1
+                       ? launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockBf16, 1>, grid, block, stream, a, w, scale, r, o, m, n, k, p)
+                       : launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockBf16, 2>, grid, block, stream, a, w, scale, r, o, m, n, k, p);
         case W8A16_SCALE_BLOCK_F32:
-            return launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockF32>, grid, block, stream, a, w, scale, r, o, m, n, k, p);
+            return passes == 1
+                       ? launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockF32, 1>, grid, block, stream, a, w, scale, r, o, m, n, k, p)
+                       : launch(&skinny_kernel<1, 2, 2, 16, kScaleBlockF32, 2>, grid, block, stream, a, w, scale, r, o, m, n, k, p);
         case W8A16_SCALE_ROW_F32:
-            return launch(&skinny_kernel<1, 2, 2, 16, kScaleRowF32>, grid, block, stream, a, w, scale, r, o, m, n, k, p);
+            return passes == 1
+                       ? launch(&skinny_kernel<1, 2, 2, 16, kScaleRowF32, 1>, grid, block, stream, a, w, scale, r, o, m, n, k, p)
+                       : launch(&skinny_kernel<1, 2, 2, 16, kScaleRowF32, 2>, grid, block, stream, a, w, scale, r, o, m, n, k, p);
         default:
             return W8A16_ERR_ARG;
     }

@@ -91,7 +91,8 @@ enum w8a16_scale_format {
  * 16 <= K <= 16384 for M <= 8 and 16 <= K <= 8192 for M >= 9.
  * M == 0 or N == 0 is a no-op returning W8A16_OK.
  * Each weight byte is read from HBM once per call for all M rows. From
- * M = 4 on, with K <= 4096, the call runs the skinny path of w8a16_gemm
+ * M = 4 on with K <= 4096, and from M = 12 on with K <= 8192, the call runs
+ * the skinny path of w8a16_gemm
  * (products on the matrix cores; same result contract).
  */
 int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
@@ -104,7 +105,8 @@ int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
  * M >= 0 (any), N >= 0, 16 <= K < 2^23, K % 16 == 0; M == 0 or N == 0 is a
  * no-op. The block scale is applied in fp32 per 128-wide k-block, as in the
  * GEMV. Paths, chosen by M and K only:
- *  - M <= 16 and K <= 4096: the weights stream from HBM straight into the
+ *  - M <= 16 and K <= 4096, or 12 <= M <= 16 and K <= 8192 (two passes over
+ *    K): the weights stream from HBM straight into the
  *    matrix-core operands (one kernel, no workspace);
  *  - otherwise output tiles of 32 (M <= 32), 64 (M <= 64) or 128 rows by 128
  *    columns: the E4M3 weight bytes of a tile are staged once per workgroup

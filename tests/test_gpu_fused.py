@@ -190,7 +190,8 @@ def test_gemv_fused_without_prologue_matches_plain_bits(dev, M):
 # --- residual epilogue of the GEMM (every path) ------------------------------------
 
 GEMM_RES_SHAPES = [(1, 384, 256), (16, 1000, 4096), (20, 4096, 8192), (40, 98400, 528), (129, 1000, 1040),
-                   (300, 257, 4096), (66, 65704, 1040), (513, 640, 1024), (200, 12200, 1280)]
+                   (300, 257, 4096), (66, 65704, 1040), (513, 640, 1024), (200, 12200, 1280),
+                   (12, 300, 6160)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_RES_SHAPES)

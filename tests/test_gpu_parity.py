@@ -139,9 +139,12 @@ def test_gemv_k_edges(dev, M, N, K):
 
 # --- GEMM ------------------------------------------------------------------------
 
-# M <= 16 with K <= 4096 streams the weights through the skinny kernel (16-row
-# weight blocks, K split over 4 to 16 waves, ring of 2 blocks per wave; ragged
-# N, idle waves when K is short, several blocks per workgroup). Otherwise the
+# M <= 16 with K <= 4096 (M >= 12: K <= 8192) streams the weights through the
+# skinny kernel (16-row weight blocks, K split over 4 to 16 waves, ring of 2
+# blocks per wave; ragged N, idle waves when K is short, several blocks per
+# workgroup; K above 4096 in two passes: M = 16, N = 4096, K = 8192 is the
+# Mamba-2 out_proj, K = 4224 and 6160 leave idle waves and a ragged k-block in
+# the second pass). Otherwise the
 # GEMM has three tile shapes: 32 x 128 for M <= 32 (4 workgroups per CU),
 # 64 x 128 for M <= 64 (3 per CU) and 128 x 128 above (2 per CU). For each,
 # the shapes span whole tiles only (few tiles, short K), tiles whose k-blocks
@@ -166,7 +169,7 @@ def test_gemv_k_edges(dev, M, N, K):
                                    (3, 140000, 1040), (5, 166400, 528), (33, 1000, 1040), (48, 18560, 2048),
                                    (40, 98400, 528), (31, 300, 4112), (16, 18560, 4096), (9, 1000, 4096),
                                    (7, 1000, 8208), (2, 4100, 1936), (200, 12200, 1280), (256, 12288, 512),
-                                   (130, 38300, 512)])
+                                   (130, 38300, 512), (16, 4096, 8192), (13, 1000, 4224), (12, 300, 6160)])
 def test_gemm_every_element(dev, M, N, K):
     say(f"gemm M={M} N={N} K={K}")
     A = inputs.activations(M, K, 900 + M)

@@ -4,8 +4,9 @@ block_f32: the BF16 grid's shape and index with FP32 values (nemotron_mamba2.rs
 listing, `set_fp8_weights`); row_f32: one FP32 scale per weight row, applied to
 the finished fp32 row sum (Qwen3SsmLayer docs,
 `set_fp8_rowwise_prefill_weights`). Every path is covered for each format:
-the GEMV kernels (M <= 3, or K > 4096), the skinny kernel (4 <= M <= 16 via
-the GEMV entry, M <= 16 via the GEMM entry, K <= 4096), and the GEMM's
+the GEMV kernels (M <= 3, K > 8192, or K > 4096 below 12 rows), the skinny kernel
+(4 <= M <= 16 via the GEMV entry, M <= 16 via the GEMM entry; K <= 4096, or
+K <= 8192 from 12 rows on), and the GEMM's
 32-, 64- and 128-row tiles with whole and split tiles. Bar as for the BF16
 grid: |gpu - ref| <= 4e-3 * sum_k |A * Wdeq| + 1e-6 on every element, and
 bit-exact where the answer is unique (an FP32 grid holding BF16 values gives
@@ -113,7 +114,8 @@ def test_prefill_1k_in_proj_sampled(dev, fmt):
 
 ALL_PATHS = [("gemv", 1, 1000, 1040), ("gemv", 3, 300, 8192), ("gemv", 8, 1000, 1040), ("gemm", 16, 1000, 2048),
              ("gemm", 24, 4096, 8192), ("gemm", 50, 1000, 1040), ("gemm", 200, 1000, 1040),
-             ("gemm", 72, 78339, 1040), ("gemm", 256, 12288, 512)]
+             ("gemm", 72, 78339, 1040), ("gemm", 256, 12288, 512),
+             ("gemm", 12, 300, 6160)]
 ENTRY = {"gemv": binding.w8a16_gemv, "gemm": binding.w8a16_gemm}
 
 
