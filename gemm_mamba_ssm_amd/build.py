@@ -21,7 +21,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw8a16.so")
 ARCH = "gfx950"
 
-SOURCES = ["w8a16_common.cpp", "w8a16_gemv.hip", "w8a16_gemm.hip", "w8a16_skinny.hip", "w8a16_dequant.hip", "w8a16_norm.hip",
+SOURCES = ["w8a16_common.cpp", "w8a16_gemv.hip", "w8a16_gemm.hip", "w8a16_gemm_wide.hip", "w8a16_skinny.hip", "w8a16_dequant.hip", "w8a16_norm.hip",
            "w8a16_mamba2.hip"]
 
 HIPCC_FLAGS = [

@@ -811,6 +811,7 @@ int gemm_by_shape(const void* A, const void* Wq, const void* scale, const void* 
     if (skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
     if (M <= Skinny32::TM) return run_gemm<Skinny32, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
     if (M <= Skinny64::TM) return run_gemm<Skinny64, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
+    if (wide_gemm_pays(M, N, K, device_cu_count())) return wide_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
     // About as many 128 x 128 tiles as CUs (at least three quarters of them,
     // so no more than a quarter idles) and whole k-steps in two equal halves
     // of whole scale blocks: one workgroup per tile, k split inside it.
