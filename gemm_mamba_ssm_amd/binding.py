@@ -30,15 +30,16 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw8a16.so")
 BLOCK = 128
 
-EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_gemv_ex", "w8a16_gemm_ex", "w8a16_rmsnorm", "w8a16_gemv_fused",
-           "w8a16_gemm_residual", "w8a16_conv1d_update", "w8a16_gemv_in_proj", "w8a16_ssm_decode", "w8a16_dequant",
-           "w8a16_strerror")
+EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_gemv_ex", "w8a16_gemm_ex", "w8a16_gemm_workspace_size",
+           "w8a16_gemm_ws", "w8a16_rmsnorm", "w8a16_gemv_fused", "w8a16_gemm_residual", "w8a16_conv1d_update",
+           "w8a16_gemv_in_proj", "w8a16_ssm_decode", "w8a16_dequant", "w8a16_strerror")
 
 # enum w8a16_scale_format
 SCALE_BLOCK_BF16, SCALE_BLOCK_F32, SCALE_ROW_F32 = 0, 1, 2
 SCALE_FORMATS = {"block_bf16": SCALE_BLOCK_BF16, "block_f32": SCALE_BLOCK_F32, "row_f32": SCALE_ROW_F32}
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ALIAS, ERR_ARG, ERR_MEMORY = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ALIAS, ERR_ARG, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7
+WORKSPACE_ALIGN = 256
 GEMV_MAX_M = 16
 GEMV_MAX_K_SMALL_M = 16384   # M <= 8
 GEMV_MAX_K = 8192            # M >= 9
@@ -73,6 +74,10 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P, P, P, ctypes.c_int, P, I64, I64, I64, P]
+    lib.w8a16_gemm_workspace_size.restype = I64
+    lib.w8a16_gemm_workspace_size.argtypes = [I64, I64, I64]
+    lib.w8a16_gemm_ws.restype = ctypes.c_int
+    lib.w8a16_gemm_ws.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P]
     F = ctypes.c_float
     lib.w8a16_rmsnorm.restype = ctypes.c_int
     lib.w8a16_rmsnorm.argtypes = [P, P, P, F, P, I64, I64, P]
@@ -106,6 +111,16 @@ def gemv_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: int, stre
 
 def gemm_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: int, stream: int = 0) -> int:
     return load().w8a16_gemm(A, Wq, scale, out, M, N, K, stream)
+
+
+def gemm_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace w8a16_gemm_ws needs for (M, N, K) on the current device (0: none)."""
+    return load().w8a16_gemm_workspace_size(M, N, K)
+
+
+def gemm_ws_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: int, workspace: int,
+                workspace_bytes: int, stream: int = 0) -> int:
+    return load().w8a16_gemm_ws(A, Wq, scale, out, M, N, K, workspace or None, workspace_bytes, stream)
 
 
 def gemv_ex_raw(A: int, Wq: int, scale: int, scale_format: int, out: int, M: int, N: int, K: int,
@@ -270,6 +285,51 @@ def w8a16_gemm(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
 
     ``scale`` as for :func:`w8a16_gemv`."""
     return _product("w8a16_gemm", A, Wq, scale, out, stream, scale_format=scale_format)
+
+
+def gemm_workspace(M: int, N: int, K: int, device=None) -> torch.Tensor | None:
+    """A workspace tensor for w8a16_gemm_ws at (M, N, K) (None if the shape needs none).
+
+    Allocated by torch here, once, by the caller's choice: the library itself
+    allocates nothing."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(device):
+        nbytes = gemm_workspace_size(M, N, K)
+    if nbytes < 0:
+        raise W8A16Error("w8a16_gemm_workspace_size", nbytes)
+    if nbytes == 0:
+        return None
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def w8a16_gemm_ws(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor, workspace: torch.Tensor | None,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The GEMM with a caller-supplied workspace (BF16 block grid): shapes whose
+    tiles do not fill the GPU split their k-blocks between workgroups, the
+    partial sums going through ``workspace`` (a uint8 device tensor of at
+    least gemm_workspace_size(M, N, K) bytes; None runs w8a16_gemm)."""
+    _need(A.dtype == torch.bfloat16 and A.dim() == 2 and A.is_contiguous(), "A must be a contiguous bfloat16 [M, K]")
+    N, K, fmt = _check_scaled_weights(Wq, scale, "block_bf16")
+    M = A.shape[0]
+    _need(A.shape[1] == K, f"A is {list(A.shape)} but Wq is {list(Wq.shape)}")
+    if workspace is not None:
+        _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(), "workspace must be a contiguous uint8 tensor")
+        _check_device(A, workspace)
+    if out is None:
+        _check_device(A, Wq, scale)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    else:
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (M, N) and out.is_contiguous(),
+              f"out must be a contiguous bfloat16 [{M}, {N}] tensor")
+        _check_device(A, Wq, scale, out)
+    with torch.cuda.device(A.device):
+        st = gemm_ws_raw(A.data_ptr(), Wq.data_ptr(), scale.data_ptr(), out.data_ptr(), M, N, K,
+                         workspace.data_ptr() if workspace is not None else 0,
+                         workspace.numel() if workspace is not None else 0, _stream_handle(A.device, stream))
+    if st != OK:
+        raise W8A16Error("w8a16_gemm_ws", st)
+    return out
 
 
 def w8a16_dequant(Wq: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None,

@@ -30,7 +30,7 @@ extern "C" const char* w8a16_strerror(int status) {
         case W8A16_ERR_LAUNCH: return "HIP kernel launch failed";
         case W8A16_ERR_ALIAS: return "out overlaps an input buffer";
         case W8A16_ERR_ARG: return "invalid argument";
-        case W8A16_ERR_MEMORY: return "could not allocate the GEMM workspace";
+        case W8A16_ERR_WORKSPACE: return "the GEMM workspace is smaller than w8a16_gemm_workspace_size";
         default: return "unknown w8a16 status";
     }
 }

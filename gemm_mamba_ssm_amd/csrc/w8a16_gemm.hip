@@ -56,8 +56,6 @@
 // of the tile's k-steps on its own LDS stages, and the two fp32 halves are
 // added in LDS at the end, so nothing goes through memory twice and no second
 // kernel runs (BigSplit below).
-#include <map>
-#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -728,43 +726,28 @@ int list_splits(const Schedule& sc, SplitList* list) {
     return n;
 }
 
-// Workspace of one (device, stream): two partial-tile slots per workgroup of
-// the largest grid of any tile shape (at most 64 MB on a 256-CU device).
-// Allocated on first use, grown when a larger one is needed, and kept until
-// the process ends.
-struct Workspace {
-    float* partials = nullptr;
-    size_t bytes = 0;
-};
-
-int workspace_for(hipStream_t stream, size_t bytes, Workspace* ws) {
-    static std::mutex mu;
-    static auto* cache = new std::map<std::pair<int, hipStream_t>, Workspace>();
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return W8A16_ERR_LAUNCH;
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = cache->find({dev, stream});
-    if (it != cache->end() && it->second.bytes >= bytes) {
-        *ws = it->second;
-        return W8A16_OK;
+// Bytes of partial tiles the split schedule of tile shape C needs (0 when
+// it computes whole tiles only): two slots per workgroup of the shared part.
+template <class C>
+int64_t split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if constexpr (C::kSplit == 2) {
+        return 0;
+    } else {
+        const int64_t tiles_m = ceil_div(M, C::TM), tiles = tiles_m * ceil_div(N, TN);
+        if (tiles > INT32_MAX) return 0;
+        Schedule sc;
+        plan(tiles, tiles_m, static_cast<int>(ceil_div(K, kScaleBlockHost)),
+             std::min(C::kWgPerCu * device_cu_count(), kMaxSplits), C::kMinShareBlocks, &sc);
+        return sc.shared_groups > 0 ? 2 * static_cast<int64_t>(sc.shared_groups) * C::kTileFloats * 4 : 0;
     }
-    void* p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) return W8A16_ERR_MEMORY;
-    // A smaller workspace of the same key is only replaced, never freed: work
-    // already enqueued on the stream may still use it.
-    Workspace fresh;
-    fresh.partials = static_cast<float*>(p);
-    fresh.bytes = bytes;
-    (*cache)[{dev, stream}] = fresh;
-    *ws = fresh;
-    return W8A16_OK;
 }
 
 // Plan and launch the GEMM (and, if tiles are split, the combine) with tile
-// shape C and scale format SF.
+// shape C and scale format SF. Without a workspace (partials == nullptr)
+// every tile is computed whole by one workgroup.
 template <class C, int SF, bool RES>
 int run_gemm(const void* A, const void* Wq, const void* scale, const void* residual, void* out, int64_t M,
-             int64_t N, int64_t K, hipStream_t s) {
+             int64_t N, int64_t K, float* partials, size_t workspace_bytes, hipStream_t s) {
     // Buffer offsets are 32-bit: one tile's rows of A must span less than 2 GiB.
     if (static_cast<int64_t>(C::TM) * K * 2 >= static_cast<int64_t>(kOutOfRange)) return W8A16_ERR_SHAPE;
     const int64_t tiles_m = ceil_div(M, C::TM);
@@ -774,23 +757,22 @@ int run_gemm(const void* A, const void* Wq, const void* scale, const void* resid
     const int slots = std::min(C::kWgPerCu * device_cu_count(), kMaxSplits);
     Schedule sc;
     int grid;
-    if constexpr (C::kSplit == 2) {
-        sc = Schedule{};                             // whole tiles, one per workgroup (tiles <= slots)
+    const bool may_split = C::kSplit == 1 && partials != nullptr;
+    if (!may_split) {
+        sc = Schedule{};                             // whole tiles, one per workgroup
         sc.tiles_m = static_cast<int>(tiles_m);
         sc.k_blocks = k_blocks;
         sc.full_rounds = 1;
         grid = static_cast<int>(tiles);
     } else {
         grid = plan(tiles, tiles_m, k_blocks, slots, C::kMinShareBlocks, &sc);
-    }
-    Workspace ws;
-    if (sc.shared_groups > 0) {
-        const int st = workspace_for(s, static_cast<size_t>(2) * slots * C::kTileFloats * sizeof(float), &ws);
-        if (st != W8A16_OK) return st;
+        if (sc.shared_groups > 0 &&
+            workspace_bytes < static_cast<size_t>(2) * sc.shared_groups * C::kTileFloats * sizeof(float))
+            return W8A16_ERR_WORKSPACE;
     }
     int st = launch(GemmKernel<C, SF, RES>::fn, dim3(static_cast<unsigned>(grid)), dim3(C::kThreadsWg), s,
                     static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
-                    static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out), ws.partials,
+                    static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out), partials,
                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), sc);
     if constexpr (C::kSplit == 2) {
         return st;                                   // whole tiles: nothing to combine
@@ -800,25 +782,52 @@ int run_gemm(const void* A, const void* Wq, const void* scale, const void* resid
         const int splits = list_splits(sc, &list);
         if (splits == 0) return W8A16_OK;
         return launch(&combine_kernel<C, SF, RES>, dim3(static_cast<unsigned>(splits), C::TM / kCombineRows),
-                      dim3(kThreads), s, static_cast<const float*>(ws.partials), static_cast<uint16_t*>(out), scale,
+                      dim3(kThreads), s, static_cast<const float*>(partials), static_cast<uint16_t*>(out), scale,
                       static_cast<const uint16_t*>(residual), static_cast<int>(M), static_cast<int>(N), sc, list);
+    }
+}
+
+// The kernel family for (M, N, K) on this device; depends on nothing else.
+enum class Path { kSkinny, kTile32, kTile64, kWide, kBigSplit, kBigTile };
+
+Path choose_path(int64_t M, int64_t N, int64_t K) {
+    if (skinny_fits(M, K)) return Path::kSkinny;
+    if (M <= Skinny32::TM) return Path::kTile32;
+    if (M <= Skinny64::TM) return Path::kTile64;
+    const int cus = device_cu_count();
+    if (wide_gemm_pays(M, N, K, cus)) return Path::kWide;
+    // About as many 128 x 128 tiles as CUs (at least three quarters of them,
+    // so no more than a quarter idles) and whole k-steps in two equal halves
+    // of whole scale blocks: one workgroup per tile, k split inside it.
+    const int64_t tiles = ceil_div(M, BigTile::TM) * ceil_div(N, TN);
+    if (tiles <= cus && 4 * tiles >= 3 * cus && K % (4 * TK) == 0) return Path::kBigSplit;
+    return Path::kBigTile;
+}
+
+int64_t workspace_bytes_for(int64_t M, int64_t N, int64_t K) {
+    switch (choose_path(M, N, K)) {
+        case Path::kTile32: return split_workspace_bytes<Skinny32>(M, N, K);
+        case Path::kTile64: return split_workspace_bytes<Skinny64>(M, N, K);
+        case Path::kBigTile: return split_workspace_bytes<BigTile>(M, N, K);
+        default: return 0;
     }
 }
 
 template <int SF, bool RES>
 int gemm_by_shape(const void* A, const void* Wq, const void* scale, const void* residual, void* out, int64_t M,
-                  int64_t N, int64_t K, hipStream_t s) {
-    if (skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
-    if (M <= Skinny32::TM) return run_gemm<Skinny32, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
-    if (M <= Skinny64::TM) return run_gemm<Skinny64, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
-    if (wide_gemm_pays(M, N, K, device_cu_count())) return wide_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
-    // About as many 128 x 128 tiles as CUs (at least three quarters of them,
-    // so no more than a quarter idles) and whole k-steps in two equal halves
-    // of whole scale blocks: one workgroup per tile, k split inside it.
-    const int64_t tiles = ceil_div(M, BigTile::TM) * ceil_div(N, TN), cus = device_cu_count();
-    if (tiles <= cus && 4 * tiles >= 3 * cus && K % (4 * TK) == 0)
-        return run_gemm<BigSplit, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
-    return run_gemm<BigTile, SF, RES>(A, Wq, scale, residual, out, M, N, K, s);
+                  int64_t N, int64_t K, hipStream_t s, float* partials = nullptr, size_t workspace_bytes = 0) {
+    switch (choose_path(M, N, K)) {
+        case Path::kSkinny: return skinny_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
+        case Path::kTile32:
+            return run_gemm<Skinny32, SF, RES>(A, Wq, scale, residual, out, M, N, K, partials, workspace_bytes, s);
+        case Path::kTile64:
+            return run_gemm<Skinny64, SF, RES>(A, Wq, scale, residual, out, M, N, K, partials, workspace_bytes, s);
+        case Path::kWide: return wide_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
+        case Path::kBigSplit:
+            return run_gemm<BigSplit, SF, RES>(A, Wq, scale, residual, out, M, N, K, nullptr, 0, s);
+        default:
+            return run_gemm<BigTile, SF, RES>(A, Wq, scale, residual, out, M, N, K, partials, workspace_bytes, s);
+    }
 }
 
 }  // namespace
@@ -844,6 +853,34 @@ extern "C" int w8a16_gemm_ex(const void* A, const void* Wq, const void* scale, i
 extern "C" int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
                           int64_t M, int64_t N, int64_t K, void* stream) {
     return w8a16_gemm_ex(A, Wq, scale, W8A16_SCALE_BLOCK_BF16, out, M, N, K, stream);
+}
+
+extern "C" int64_t w8a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    using namespace w8a16;
+    if (M < 0 || N < 0 || K < 16 || (K % 16) != 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return W8A16_ERR_SHAPE;
+    if (M == 0 || N == 0) return 0;
+    return workspace_bytes_for(M, N, K);
+}
+
+extern "C" int w8a16_gemm_ws(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N,
+                             int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+    using namespace w8a16;
+    bool noop = false;
+    const int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
+    if (st != W8A16_OK || noop) return st;
+    if (workspace == nullptr)
+        return gemm_by_shape<kScaleBlockBf16, false>(A, Wq, scale, nullptr, out, M, N, K,
+                                                     static_cast<hipStream_t>(stream));
+    if (workspace_bytes < 0) return W8A16_ERR_ARG;
+    if (!aligned(workspace, 256)) return W8A16_ERR_ALIGN;
+    if (workspace_bytes < workspace_bytes_for(M, N, K)) return W8A16_ERR_WORKSPACE;
+    if (overlaps(workspace, workspace_bytes, out, M * N * 2) || overlaps(workspace, workspace_bytes, A, M * K * 2) ||
+        overlaps(workspace, workspace_bytes, Wq, N * K) ||
+        overlaps(workspace, workspace_bytes, scale, scale_bytes(W8A16_SCALE_BLOCK_BF16, N, K)))
+        return W8A16_ERR_ALIAS;
+    return gemm_by_shape<kScaleBlockBf16, false>(A, Wq, scale, nullptr, out, M, N, K, static_cast<hipStream_t>(stream),
+                                                 static_cast<float*>(workspace), static_cast<size_t>(workspace_bytes));
 }
 
 extern "C" int w8a16_gemm_residual(const void* A, const void* Wq, const void* scale, const void* residual,

@@ -24,8 +24,8 @@
  * must check the layout before calling, as the Python binding does.
  *
  * Ownership: the caller owns every buffer it passes; the library keeps no
- * pointer to them after a call returns. The only memory the library allocates
- * is the GEMM workspace described at w8a16_gemm. The decode-step entry points
+ * pointer to them after a call returns, and allocates no device memory of its
+ * own (no entry point calls hipMalloc). The decode-step entry points
  * (w8a16_conv1d_update, w8a16_ssm_decode) update the caller's state buffers in
  * place; every other entry point only writes `out`.
  * Streams: `stream` is a hipStream_t (NULL = the legacy default stream). Every
@@ -53,7 +53,7 @@ enum w8a16_status {
     W8A16_ERR_LAUNCH = -4, /* the HIP launch failed                             */
     W8A16_ERR_ALIAS = -5,  /* out overlaps an input                             */
     W8A16_ERR_ARG = -6,    /* another argument is invalid                       */
-    W8A16_ERR_MEMORY = -7  /* the GEMM workspace could not be allocated         */
+    W8A16_ERR_WORKSPACE = -7 /* w8a16_gemm_ws: the workspace is too small         */
 };
 
 /*
@@ -103,26 +103,25 @@ int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
  * the weights are read once for all N tokens as one GEMM with M = N), and
  * the skinny case of a few tokens (speculative verify, batched decode).
  * M >= 0 (any), N >= 0, 16 <= K < 2^23, K % 16 == 0; M == 0 or N == 0 is a
- * no-op. The block scale is applied in fp32 per 128-wide k-block, as in the
- * GEMV. Paths, chosen by M and K only:
+ * no-op. Paths, chosen by M, N, K and the device's CU count only:
  *  - M <= 16 and K <= 4096, or 12 <= M <= 16 and K <= 8192 (two passes over
  *    K): the weights stream from HBM straight into the
  *    matrix-core operands (one kernel, no workspace);
+ *  - M >= 65 where 256 x 256 output tiles fill every round of CU-many tiles
+ *    to at least 85 % (e.g. the 8192-token prefill): one workgroup per CU
+ *    walks those tiles; each weight is converted once per tile as
+ *    bf16(e * s), the block scale folded in (e * s is exact in fp32, rounded
+ *    once), and the matrix cores accumulate over the whole K range;
  *  - otherwise output tiles of 32 (M <= 32), 64 (M <= 64) or 128 rows by 128
  *    columns: the E4M3 weight bytes of a tile are staged once per workgroup
- *    and decoded in registers. When there are fewer tiles than the GPU holds
- *    at once, or the last wave of tiles would be less than a quarter full,
- *    the k-blocks of the remaining tiles are split between workgroups; their
- *    fp32 partial sums are stored to a workspace and a second kernel,
- *    enqueued on the same stream, adds them in k order.
+ *    and decoded in registers, and the block scale multiplies each 128-wide
+ *    k-block's fp32 partial sum. 128-row tiles numbering between three
+ *    quarters of the CUs and the CUs split their k-range between two halves
+ *    of one workgroup, added in LDS. Every tile is computed whole by one
+ *    workgroup: w8a16_gemm needs no workspace and allocates nothing (it may
+ *    be captured in a HIP graph on any stream).
  * Every choice depends only on M, N, K and the device's compute-unit count,
  * so the bits are the same on every call.
- * Workspace: the first call that splits tiles on a given (device, stream)
- * allocates that pair's workspace (at most 64 MB on a 256-CU device; grown
- * if a later shape needs more) and keeps it until the process ends; make
- * that first call outside stream capture. Calls on one stream reuse it in
- * stream order; calls on different streams never share one. Returns
- * W8A16_ERR_MEMORY if it cannot be allocated (nothing is launched then).
  */
 int w8a16_gemm(const void* A, const void* Wq, const void* scale, void* out,
                int64_t M, int64_t N, int64_t K, void* stream);
@@ -141,6 +140,30 @@ int w8a16_gemv_ex(const void* A, const void* Wq, const void* scale, int scale_fo
                   int64_t M, int64_t N, int64_t K, void* stream);
 int w8a16_gemm_ex(const void* A, const void* Wq, const void* scale, int scale_format, void* out,
                   int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * The GEMM with a caller-supplied workspace, for shapes whose 32-, 64- or
+ * 128-row tiles do not fill the GPU (fewer tiles than it holds at once, or a
+ * last wave less than a quarter full; typically a few dozen to a few hundred
+ * tokens against weights with few rows, like the Mamba-2 out_proj): the
+ * k-blocks of the remaining tiles are then split between workgroups, whose
+ * fp32 partial tiles go to the workspace, and a second kernel enqueued on the
+ * same stream adds them in k order (deterministic: the split depends only on
+ * M, N, K and the CU count). Same operands, shapes, paths and result
+ * contract as w8a16_gemm (BF16 block grid).
+ * w8a16_gemm_workspace_size returns the bytes this needs for (M, N, K) on the
+ * current device (0: the shape does not split), or W8A16_ERR_SHAPE for an
+ * invalid shape.
+ * workspace: device memory of workspace_bytes bytes, 256-byte aligned
+ * (W8A16_ERR_ALIGN), not overlapping an operand (W8A16_ERR_ALIAS), at least
+ * w8a16_gemm_workspace_size(M, N, K) bytes (else W8A16_ERR_WORKSPACE;
+ * nothing is launched). NULL runs w8a16_gemm. The call owns the workspace
+ * from enqueue until the stream passes the call: calls that may run at the
+ * same time need separate workspaces.
+ */
+int64_t w8a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+int w8a16_gemm_ws(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
+                  void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Norm prologues and the residual epilogue of the Mamba-2 layer around its

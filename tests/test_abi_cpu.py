@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_covers_every_status():
     for st in (binding.OK, binding.ERR_NULL, binding.ERR_SHAPE, binding.ERR_ALIGN,
-               binding.ERR_LAUNCH, binding.ERR_ALIAS, binding.ERR_ARG, binding.ERR_MEMORY):
+               binding.ERR_LAUNCH, binding.ERR_ALIAS, binding.ERR_ARG, binding.ERR_WORKSPACE):
         s = binding.strerror(st)
         assert s and "unknown" not in s
     assert "unknown" in binding.strerror(12345)
@@ -300,3 +300,33 @@ def test_in_proj_rejections():
     assert ip(A, Wn, 1e-5, Wq, S, O + 64, Cw, Cb, 0, 64, 4, O, 1, 256, 256, 0) == binding.ERR_ALIAS  # state in out
     assert ip(A, Wn, 1e-5, Wq, S, St, Cw, Cb, 0, 64, 4, Cw - 64, 1, 256, 256, 0) == binding.ERR_ALIAS
     assert ip(A, Wn, 1e-5, Wq, S, A + 16, Cw, Cb, 0, 64, 4, O, 1, 256, 256, 0) == binding.ERR_ALIAS   # state over A
+
+
+def test_gemm_workspace_size_follows_the_split_schedule():
+    """Host-only: which shapes split their tiles (and need a workspace) on a
+    256-CU device; computed from M, N, K and the CU count, nothing launched."""
+    ws = binding.gemm_workspace_size
+    assert ws(-1, 256, 256) == binding.ERR_SHAPE
+    assert ws(4, 256, 136) == binding.ERR_SHAPE
+    assert ws(0, 4096, 8192) == 0
+    assert ws(8, 18560, 4096) == 0                      # skinny kernel: no split
+    assert ws(1024, 18560, 4096) == 0                   # whole 128 x 128 tiles
+    assert ws(1024, 4096, 8192) == 0                    # k split inside the workgroup
+    assert ws(8192, 35072, 8192) == 0                   # 256 x 256 tiles
+    need = ws(128, 4096, 8192)                          # 32 tiles of 128 x 128 on 512 slots
+    assert need > 0 and need % (128 * 128 * 4) == 0
+    assert ws(32, 4096, 8192) > 0
+
+
+def test_gemm_ws_rejections_before_any_hip_call():
+    A, Wq, scale, out = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    M, N, K = 128, 4096, 8192
+    need = binding.gemm_workspace_size(M, N, K)
+    wsp = FAKE + (4 << 30)
+    call = binding.gemm_ws_raw
+    assert call(A, Wq, scale, out, M, N, K, wsp + 16, need, 0) == binding.ERR_ALIGN
+    assert call(A, Wq, scale, out, M, N, K, wsp, need - 1, 0) == binding.ERR_WORKSPACE
+    assert call(A, Wq, scale, out, M, N, K, wsp, -1, 0) == binding.ERR_ARG
+    assert call(A, Wq, scale, out, M, N, K, out, need, 0) == binding.ERR_ALIAS
+    assert call(A, Wq, scale, out, M, N, 136, wsp, need, 0) == binding.ERR_SHAPE
+    assert call(A, Wq, scale, out, 0, N, K, wsp, 0, 0) == binding.OK        # no-op

@@ -98,3 +98,41 @@ def test_layer_decode_step_graph_replays_match_eager(dev, M):
             assert torch.equal(g.view(torch.int16) if g.dtype == torch.bfloat16 else g.view(torch.int32),
                                r.view(torch.int16) if r.dtype == torch.bfloat16 else r.view(torch.int32)), \
                 f"replay {rep}: {name} differs from the eager run"
+
+
+# GEMM shapes of every tile schedule: whole 128 x 128 tiles (16 tiles), the
+# k-split inside the workgroup (192..256 tiles), the 256 x 256 tiles (one
+# round of 256), the skinny kernel, and 32-row tiles.
+CAPTURE_SHAPES = [(129, 1000, 1040), (200, 12200, 1280), (256, 65536, 64), (16, 4096, 8192), (20, 4096, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", CAPTURE_SHAPES)
+@pytest.mark.parametrize("with_workspace", [False, True])
+def test_gemm_captured_as_first_call_on_a_fresh_stream(dev, M, N, K, with_workspace):
+    """The GEMM allocates nothing, so its first call on a new stream can be
+    inside a capture; with a caller workspace the split tiles' partial sums
+    and the second (combine) kernel are captured too. Every replay, with eager
+    work between replays, equals the eager result bit for bit."""
+    A = bf(inputs.activations(M, K, 9200 + M), dev)
+    W, S = inputs.weights(N, K, 0.02, 9300 + N)
+    dW, dS = u8(W, dev), bf(S, dev)
+    ws = binding.gemm_workspace(M, N, K, dev) if with_workspace else None
+    if with_workspace and M == 20:
+        assert ws is not None, "32-row tiles at this shape split their k-blocks"
+    ref = binding.w8a16_gemm_ws(A, dW, dS, ws) if with_workspace else binding.w8a16_gemm(A, dW, dS)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    fresh = torch.cuda.Stream(device=dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=fresh):
+        if with_workspace:
+            binding.w8a16_gemm_ws(A, dW, dS, ws, out=out)
+        else:
+            binding.w8a16_gemm(A, dW, dS, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(3.0)                                 # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep} differs"

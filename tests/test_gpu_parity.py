@@ -4,9 +4,9 @@ Bar: bit-exact for the dequant-only path (E4M3 decode and scale indexing);
 for the products every checked element satisfies
     |gpu - ref| <= 4e-3 * sum_k |A[m,k] * Wdeq[n,k]| + 1e-6
 (one BF16 output ulp plus fp32 reordering), with ref and the sum from the
-fp64 oracle on the same seeded inputs. Shapes the oracle finishes in seconds
-are checked on every element; the full prefill sizes on whole sampled rows,
-whole sampled columns and random points. Invariants with a unique answer
+fp64 oracle on the same seeded inputs. Every element is checked, up to the
+1024-token prefill; the 8192-token prefill of the large layer is checked along
+a whole row and a whole column of every 128 x 128 output block. Invariants with a unique answer
 (one-hot rows, zero weights, sign and power-of-two scaling, row permutation,
 run-to-run determinism) are checked bit for bit.
 """
@@ -139,29 +139,22 @@ def test_gemv_k_edges(dev, M, N, K):
 
 # --- GEMM ------------------------------------------------------------------------
 
-# M <= 16 with K <= 4096 (M >= 12: K <= 8192) streams the weights through the
-# skinny kernel (16-row weight blocks, K split over 4 to 16 waves, ring of 2
-# blocks per wave; ragged N, idle waves when K is short, several blocks per
-# workgroup; K above 4096 in two passes: M = 16, N = 4096, K = 8192 is the
-# Mamba-2 out_proj, K = 4224 and 6160 leave idle waves and a ragged k-block in
-# the second pass). Otherwise the
-# GEMM has three tile shapes: 32 x 128 for M <= 32 (4 workgroups per CU),
-# 64 x 128 for M <= 64 (3 per CU) and 128 x 128 above (2 per CU). For each,
-# the shapes span whole tiles only (few tiles, short K), tiles whose k-blocks
-# are split between workgroups (fewer tiles than the grid's slots), and more
-# tiles than one round of the grid on a 256-CU device:
-#  * 128 x 128: N = 65704 and 78339 with 65 <= M <= 128 give 514 and 613
-#    tiles (a whole round of 512 plus a split remainder), N = 89603 gives 701
-#    (whole tiles only, the last wave over a quarter full);
-#  * 32 x 128: N = 140000 gives 1094 tiles (a round of 1024 plus a split
-#    remainder), N = 166400 gives 1300 (whole tiles only);
-#  * 64 x 128: N = 98400 gives 769 tiles (a round of 768 plus one split tile);
-#  * 128 x 128 with the k-steps split between two wave groups of one
-#    workgroup (192..256 tiles on 256 CUs, K a multiple of 256): M = 200,
-#    N = 12200, K = 1280 (ragged M and N; 10 k-steps per group: a steady
-#    chunk and a partial one) and M = 256, N = 12288, K = 512 (4 per group);
-#  * a round of 512 128 x 128 tiles and a split remainder of 88 with ragged M
-#    and N: M = 130, N = 38300, K = 512.
+# Paths of the GEMM entry (w8a16_gemm, which computes every tile whole in one
+# workgroup and uses no workspace): M <= 16 with K <= 4096 (M >= 12: K <= 8192)
+# streams the weights through the skinny kernel (16-row weight blocks, K split
+# over 4 to 16 waves, ring of 2 blocks per wave; ragged N, idle waves when K is
+# short, several blocks per workgroup; K above 4096 in two passes: M = 16,
+# N = 4096, K = 8192 is the Mamba-2 out_proj, K = 4224 and 6160 leave idle
+# waves and a ragged k-block in the second pass). Otherwise the tiles are 32 x
+# 128 for M <= 32, 64 x 128 for M <= 64 and 128 x 128 above; 128 x 128 tiles
+# numbering 192..256 (on 256 CUs) with K a multiple of 256 split their
+# k-steps between two wave groups of one workgroup (M = 200, N = 12200,
+# K = 1280: ragged M and N, 10 k-steps per group; M = 256, N = 12288, K = 512:
+# 4 per group). The shapes span few tiles, more tiles than one round of the
+# grid (N = 65704, 78339, 89603 with 65 <= M <= 128; N = 140000, 166400 with
+# M <= 32; N = 98400 with M <= 64) and ragged M, N and K tails. The
+# 256 x 256 tiles have their own tests (test_gpu_wide.py), and the split
+# schedules of w8a16_gemm_ws theirs below.
 @pytest.mark.parametrize("M,N,K", [(1, 384, 256), (17, 130, 144), (127, 300, 272), (129, 1000, 1040),
                                    (300, 257, 4096), (256, 256, 128), (1, 1, 16), (64, 4096, 512),
                                    (513, 640, 1024), (130, 18560, 128), (66, 65704, 1040),
@@ -179,24 +172,47 @@ def test_gemm_every_element(dev, M, N, K):
     assert_within_tol(got, ref, den, f"gemm M={M} N={N} K={K}")
 
 
-def _sample(M, N, seed, rows=4, cols=4, points=20000):
-    rng = np.random.default_rng(seed)
-    rs = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, rows - 2)]))
-    cs = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, cols - 2)]))
-    mi = [np.repeat(rs, N), np.repeat(np.arange(M), cs.size), rng.integers(0, M, points)]
-    ni = [np.tile(np.arange(N), rs.size), np.tile(cs, M), rng.integers(0, N, points)]
-    return np.concatenate(mi), np.concatenate(ni)
+@pytest.mark.parametrize("proj", [0, 1])
+def test_gemm_prefill_1k_every_element(dev, proj):
+    """The 1024-token prefill through in_proj (1024 x 18560 x 4096) or out_proj
+    (1024 x 4096 x 8192): every element against the oracle, which takes its
+    rows in chunks (about a minute of host time per projection)."""
+    p = inputs.WORKLOADS["prefill_1k"][proj]
+    say(f"gemm prefill_1k {p.name} M={p.M} N={p.N} K={p.K} (every element)")
+    A, W, S = inputs.make(p)
+    got = run(binding.w8a16_gemm, A, W, S, dev)
+    worst = 0.0
+    for r0 in range(0, p.M, 128):
+        ref, den = oracle.w8a16(A[r0:r0 + 128], W, S)
+        worst = max(worst, assert_within_tol(got[r0:r0 + 128], ref, den, f"{p.name} rows {r0}.."))
+    say(f"  {p.name}: max err/tol over all rows {worst:.4f}")
 
 
-@pytest.mark.parametrize("workload", ["prefill_1k", "prefill_8k_large"])
-def test_gemm_full_size_sampled(dev, workload):
-    for p in inputs.WORKLOADS[workload]:
-        say(f"gemm {workload} {p.name} M={p.M} N={p.N} K={p.K} (sampled)")
-        A, W, S = inputs.make(p)
-        got = run(binding.w8a16_gemm, A, W, S, dev)
-        mi, ni = _sample(p.M, p.N, p.seed_a)
-        ref, den = oracle.w8a16_points(A, W, S, mi, ni)
-        assert_within_tol(got[mi, ni], ref, den, f"{workload}/{p.name}")
+def _tile_rows_cols(M, N, tile=128):
+    """One row in every 128-row block and one column in every 128-column block
+    (a different offset inside each block), so every output tile of every tile
+    shape (128 x 128 and 256 x 256) is checked along a whole row and a whole
+    column."""
+    rows = np.array([min(M - 1, b * tile + (37 * b + 5) % tile) for b in range((M + tile - 1) // tile)])
+    cols = np.array([min(N - 1, b * tile + (53 * b + 11) % tile) for b in range((N + tile - 1) // tile)])
+    return rows, cols
+
+
+@pytest.mark.parametrize("proj", [0, 1])
+def test_gemm_prefill_8k_every_tile(dev, proj):
+    """The 8192-token prefill of the large layer: a whole row in every 128-row
+    block and a whole column in every 128-column block, against the oracle."""
+    p = inputs.WORKLOADS["prefill_8k_large"][proj]
+    say(f"gemm prefill_8k_large {p.name} M={p.M} N={p.N} K={p.K} (a row and a column per tile)")
+    A, W, S = inputs.make(p)
+    got = run(binding.w8a16_gemm, A, W, S, dev)
+    rows, cols = _tile_rows_cols(p.M, p.N)
+    ref, den = oracle.w8a16(A[rows], W, S)
+    assert_within_tol(got[rows], ref, den, f"{p.name}: {rows.size} whole rows")
+    mi = np.repeat(np.arange(p.M), cols.size)
+    ni = np.tile(cols, p.M)
+    ref, den = oracle.w8a16_points(A, W, S, mi, ni)
+    assert_within_tol(got[mi, ni], ref, den, f"{p.name}: {cols.size} whole columns")
 
 
 def test_gemv_matches_gemm_on_decode_shapes(dev):
@@ -306,9 +322,56 @@ def test_empty_and_rejected_calls(dev, entry):
     torch.cuda.synchronize()
 
 
+# Shapes whose tiles split their k-blocks between workgroups when a workspace
+# is given (w8a16_gemm_ws): fewer tiles than slots (32-, 64- and 128-row
+# tiles), a whole round plus a split remainder, and one split tile.
+SPLIT_SHAPES = [(129, 1000, 1040), (300, 257, 4096), (20, 4096, 8192), (48, 18560, 2048), (130, 38300, 512),
+                (66, 65704, 1040), (17, 140000, 1040), (40, 98400, 528), (128, 4096, 8192), (256, 4096, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_gemm_ws_split_tiles_every_element(dev, M, N, K):
+    say(f"gemm_ws M={M} N={N} K={K}")
+    A = inputs.activations(M, K, 950 + M)
+    W, S = inputs.weights(N, K, 0.02, 1050 + N + K)
+    ws = binding.gemm_workspace(M, N, K, dev)
+    assert ws is not None, "this shape splits"
+    dA, dW, dS = upload(A, W, S, dev)
+    got = binding.w8a16_gemm_ws(dA, dW, dS, ws)
+    again = binding.w8a16_gemm_ws(dA, dW, dS, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), again.view(torch.int16)), "not deterministic"
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(bf16_bits(got), ref, den, f"gemm_ws M={M} N={N} K={K}")
+
+
+def test_gemm_ws_on_two_streams_with_two_workspaces(dev):
+    """Two split GEMMs run concurrently on two streams, each with its own
+    workspace: neither result is disturbed, and repeats agree bit for bit."""
+    shapes = [(129, 1000, 1040, 21), (300, 257, 4096, 22)]
+    ops = []
+    for M, N, K, seed in shapes:
+        A = inputs.activations(M, K, seed)
+        W, S = inputs.weights(N, K, 0.02, seed + 100)
+        ops.append((A, W, S, *upload(A, W, S, dev), binding.gemm_workspace(M, N, K, dev)))
+    streams = [torch.cuda.Stream(device=dev) for _ in shapes]
+    outs = []
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for (A, W, S, dA, dW, dS, ws), s in zip(ops, streams):
+            with torch.cuda.stream(s):
+                outs.append(binding.w8a16_gemm_ws(dA, dW, dS, ws))
+    torch.cuda.synchronize()
+    for i, (A, W, S, *_) in enumerate(ops):
+        ref, den = oracle.w8a16(A, W, S)
+        got = [bf16_bits(outs[rep * len(ops) + i]) for rep in range(3)]
+        assert_within_tol(got[0], ref, den, f"stream {i}")
+        assert all(np.array_equal(g, got[0]) for g in got[1:]), "repeats differ"
+
+
 def test_gemm_on_two_streams_at_once(dev):
-    """Two GEMMs with split tiles run concurrently on two streams: each stream
-    has its own workspace, so neither result is disturbed."""
+    """Two GEMMs run concurrently on two streams (no shared state: the plain
+    entry point uses no workspace), each result exact to the oracle's bar."""
     shapes = [(129, 1000, 1040, 11), (300, 257, 4096, 12)]
     ops = []
     for M, N, K, seed in shapes:

@@ -131,6 +131,56 @@ def test_ssm_geometric_series_closed_form():
             assert np.allclose(h[b, hh], want, rtol=1e-11, atol=1e-14)
 
 
+def test_ssm_output_selects_c_of_its_group_closed_form():
+    """Output pin independent of the oracle's contraction: C of group g is one-hot
+    at state index n_g (and a two-hot mix), B, x, dt constant, so every state
+    element follows the geometric series h_t = dA^t h0 + u (1 - dA^t) / (1 - dA)
+    and the output after step t is y[h, p] = h_t[h, p, n_g(h)] + D[h] x[h, p]
+    (resp. 2 h_t[.., a] - h_t[.., b] / 2 + D x). A C read from the wrong group or
+    from B's columns, or outputs in another order, pick other state elements."""
+    Bn, heads, hd, st, groups, T = 1, 8, 3, 5, 4, 6
+    a_log, d_param, dt_bias = inputs.ssm_params(heads, 21)
+    d_inner = heads * hd
+    per = heads // groups
+    h0 = inputs.ssm_state(Bn, heads, hd, st, 22).astype(np.float64)
+    row = inputs.activations(Bn, d_inner + 2 * groups * st, 23)       # x and B random
+    pick = [(2 * g + 1) % st for g in range(groups)]
+    c0 = d_inner + groups * st
+    row[0, c0:] = 0
+    for g in range(groups):
+        row[0, c0 + g * st + pick[g]] = 0x3F80                          # C_g = e_pick[g]
+    dt_raw = inputs.activations(Bn, heads, 24)
+    dt = np.array([oracle.softplus(bf16_f64(dt_raw[0, hh:hh + 1])[0] + np.float64(dt_bias[hh])) for hh in range(heads)])
+    dA = np.exp(dt * -np.exp(np.float64(a_log)))
+    xv = bf16_f64(row[0, :d_inner]).reshape(heads, hd)
+    Bv = bf16_f64(row[0, d_inner:d_inner + groups * st]).reshape(groups, st)
+
+    def h_closed(t):
+        u = dt[:, None, None] * xv[:, :, None] * Bv[np.arange(heads) // per][:, None, :]
+        a = dA[:, None, None]
+        return a ** t * h0[0] + u * (1 - a ** t) / (1 - a)
+
+    h = h0.copy()
+    for t in range(1, T + 1):
+        y, _, _ = oracle.ssm_decode(h, row, dt_raw, a_log, d_param, dt_bias, groups)
+        ht = h_closed(t)
+        want = np.array([[ht[hh, p, pick[hh // per]] + np.float64(d_param[hh]) * xv[hh, p] for p in range(hd)]
+                         for hh in range(heads)])
+        assert np.allclose(y[0].reshape(heads, hd), want, rtol=1e-12, atol=1e-15), t
+    # a two-hot C: y = 2 h[a] - h[b] / 2 + D x, from the same closed form
+    a_i, b_i = 0, st - 1
+    row[0, c0:] = 0
+    for g in range(groups):
+        row[0, c0 + g * st + a_i] = 0x4000                              # 2.0
+        row[0, c0 + g * st + b_i] = 0xBF00                              # -0.5
+    h = h0.copy()
+    for t in range(1, 3):
+        y, _, _ = oracle.ssm_decode(h, row, dt_raw, a_log, d_param, dt_bias, groups)
+    ht = h_closed(2)
+    want = 2 * ht[:, :, a_i] - 0.5 * ht[:, :, b_i] + np.float64(d_param)[:, None] * xv
+    assert np.allclose(y[0].reshape(heads, hd), want, rtol=1e-12, atol=1e-15)
+
+
 def test_ssm_groups_clamp_and_skip():
     Bn, heads, hd, st, groups = 1, 8, 2, 4, 4
     a_log, d_param, dt_bias = inputs.ssm_params(heads, 13)
