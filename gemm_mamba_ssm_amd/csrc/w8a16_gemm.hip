@@ -120,6 +120,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // with start(w) = floor(w * shared_units / shared_groups); then full rounds
 // give workgroup w the tiles r * G + w, r < full_rounds.
 struct Schedule {
+    int64_t ldo;         // row stride of out and of the residual, in elements (>= N)
     int tiles_m;         // tile t covers rows (t % tiles_m) * TM and columns (t / tiles_m) * TN
     int k_blocks;        // ceil(K / 128)
     int full_rounds;
@@ -293,7 +294,7 @@ __device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ A, const 
                 for (int v = 0; v < 16; ++v) {
                     const int m = m0 + wm * kWaveRows + bi * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
                     if (m < M && n < N) {
-                        const int64_t o = static_cast<int64_t>(m) * N + n;
+                        const int64_t o = static_cast<int64_t>(m) * sc.ldo + n;
                         if constexpr (RES)
                             out[o] = residual_out(r[bi][bj][v] * rs, res[o]);
                         else
@@ -670,7 +671,7 @@ combine_kernel(const float* __restrict__ partials, uint16_t* __restrict__ out, c
     for (int r = 0; r < 4; ++r) {
         const int m = m0 + row0 + r * 8;
         if (m >= M) break;
-        const int64_t o = static_cast<int64_t>(m) * N + n0 + col;
+        const int64_t o = static_cast<int64_t>(m) * sc.ldo + n0 + col;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if (n0 + col + e < N) {
@@ -747,7 +748,7 @@ int64_t split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 // every tile is computed whole by one workgroup.
 template <class C, int SF, bool RES>
 int run_gemm(const void* A, const void* Wq, const void* scale, const void* residual, void* out, int64_t M,
-             int64_t N, int64_t K, float* partials, size_t workspace_bytes, hipStream_t s) {
+             int64_t N, int64_t K, int64_t ldo, float* partials, size_t workspace_bytes, hipStream_t s) {
     // Buffer offsets are 32-bit: one tile's rows of A must span less than 2 GiB.
     if (static_cast<int64_t>(C::TM) * K * 2 >= static_cast<int64_t>(kOutOfRange)) return W8A16_ERR_SHAPE;
     const int64_t tiles_m = ceil_div(M, C::TM);
@@ -760,12 +761,14 @@ int run_gemm(const void* A, const void* Wq, const void* scale, const void* resid
     const bool may_split = C::kSplit == 1 && partials != nullptr;
     if (!may_split) {
         sc = Schedule{};                             // whole tiles, one per workgroup
+        sc.ldo = ldo;
         sc.tiles_m = static_cast<int>(tiles_m);
         sc.k_blocks = k_blocks;
         sc.full_rounds = 1;
         grid = static_cast<int>(tiles);
     } else {
         grid = plan(tiles, tiles_m, k_blocks, slots, C::kMinShareBlocks, &sc);
+        sc.ldo = ldo;
         if (sc.shared_groups > 0 &&
             workspace_bytes < static_cast<size_t>(2) * sc.shared_groups * C::kTileFloats * sizeof(float))
             return W8A16_ERR_WORKSPACE;
@@ -788,14 +791,23 @@ int run_gemm(const void* A, const void* Wq, const void* scale, const void* resid
 }
 
 // The kernel family for (M, N, K) on this device; depends on nothing else.
-enum class Path { kSkinny, kTile32, kTile64, kWide, kBigSplit, kBigTile };
+//  kWideSplitN: 256 x 256 tiles for whole rounds of CU-many tiles over the
+//  first columns, the rest of the columns (less than a round) with the
+//  128-row tiles; e.g. the 1024-token in_proj: 256 tiles over columns
+//  0..16383, then 8 x 17 tiles of 128 x 128.
+enum class Path { kSkinny, kTile32, kTile64, kWide, kWideSplitN, kBigSplit, kBigTile };
 
-Path choose_path(int64_t M, int64_t N, int64_t K) {
+Path choose_path(int64_t M, int64_t N, int64_t K, int64_t* n_wide = nullptr) {
     if (skinny_fits(M, K)) return Path::kSkinny;
     if (M <= Skinny32::TM) return Path::kTile32;
     if (M <= Skinny64::TM) return Path::kTile64;
     const int cus = device_cu_count();
     if (wide_gemm_pays(M, N, K, cus)) return Path::kWide;
+    const int64_t nw = wide_gemm_columns(M, N, K, cus);
+    if (nw > 0 && nw < N) {
+        if (n_wide) *n_wide = nw;
+        return Path::kWideSplitN;
+    }
     // About as many 128 x 128 tiles as CUs (at least three quarters of them,
     // so no more than a quarter idles) and whole k-steps in two equal halves
     // of whole scale blocks: one workgroup per tile, k split inside it.
@@ -804,11 +816,21 @@ Path choose_path(int64_t M, int64_t N, int64_t K) {
     return Path::kBigTile;
 }
 
+// The 128-row kernel for the columns the 256 x 256 tiles leave: the k-split
+// workgroups when the tiles fit one per CU, else whole (or, with a
+// workspace, split) tiles.
+bool tail_in_bigsplit(int64_t M, int64_t N, int64_t K) {
+    return ceil_div(M, BigTile::TM) * ceil_div(N, TN) <= device_cu_count() && K % (4 * TK) == 0;
+}
+
 int64_t workspace_bytes_for(int64_t M, int64_t N, int64_t K) {
-    switch (choose_path(M, N, K)) {
+    int64_t nw = 0;
+    switch (choose_path(M, N, K, &nw)) {
         case Path::kTile32: return split_workspace_bytes<Skinny32>(M, N, K);
         case Path::kTile64: return split_workspace_bytes<Skinny64>(M, N, K);
         case Path::kBigTile: return split_workspace_bytes<BigTile>(M, N, K);
+        case Path::kWideSplitN:
+            return tail_in_bigsplit(M, N - nw, K) ? 0 : split_workspace_bytes<BigTile>(M, N - nw, K);
         default: return 0;
     }
 }
@@ -816,17 +838,37 @@ int64_t workspace_bytes_for(int64_t M, int64_t N, int64_t K) {
 template <int SF, bool RES>
 int gemm_by_shape(const void* A, const void* Wq, const void* scale, const void* residual, void* out, int64_t M,
                   int64_t N, int64_t K, hipStream_t s, float* partials = nullptr, size_t workspace_bytes = 0) {
-    switch (choose_path(M, N, K)) {
+    int64_t nw = 0;
+    switch (choose_path(M, N, K, &nw)) {
         case Path::kSkinny: return skinny_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
         case Path::kTile32:
-            return run_gemm<Skinny32, SF, RES>(A, Wq, scale, residual, out, M, N, K, partials, workspace_bytes, s);
+            return run_gemm<Skinny32, SF, RES>(A, Wq, scale, residual, out, M, N, K, N, partials, workspace_bytes, s);
         case Path::kTile64:
-            return run_gemm<Skinny64, SF, RES>(A, Wq, scale, residual, out, M, N, K, partials, workspace_bytes, s);
-        case Path::kWide: return wide_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
+            return run_gemm<Skinny64, SF, RES>(A, Wq, scale, residual, out, M, N, K, N, partials, workspace_bytes, s);
+        case Path::kWide: return wide_gemm(A, Wq, scale, SF, residual, out, M, N, K, N, s);
+        case Path::kWideSplitN: {
+            // Columns [0, nw) on 256 x 256 tiles, [nw, N) on 128 x 128 tiles:
+            // the weight rows, their scale rows (nw is a multiple of 128) and
+            // the output columns of the second part start at nw.
+            int st = wide_gemm(A, Wq, scale, SF, residual, out, M, nw, K, N, s);
+            if (st != W8A16_OK) return st;
+            const int64_t nt = N - nw;
+            const void* W2 = static_cast<const uint8_t*>(Wq) + nw * K;
+            const void* S2 = SF == kScaleRowF32
+                                 ? static_cast<const void*>(static_cast<const float*>(scale) + nw)
+                                 : static_cast<const void*>(static_cast<const uint8_t*>(scale) +
+                                                            (nw / kScaleBlockHost) * ceil_div(K, kScaleBlockHost) *
+                                                                (SF == kScaleBlockBf16 ? 2 : 4));
+            void* O2 = static_cast<uint16_t*>(out) + nw;
+            const void* R2 = residual ? static_cast<const uint16_t*>(residual) + nw : nullptr;
+            if (tail_in_bigsplit(M, nt, K))
+                return run_gemm<BigSplit, SF, RES>(A, W2, S2, R2, O2, M, nt, K, N, nullptr, 0, s);
+            return run_gemm<BigTile, SF, RES>(A, W2, S2, R2, O2, M, nt, K, N, partials, workspace_bytes, s);
+        }
         case Path::kBigSplit:
-            return run_gemm<BigSplit, SF, RES>(A, Wq, scale, residual, out, M, N, K, nullptr, 0, s);
+            return run_gemm<BigSplit, SF, RES>(A, Wq, scale, residual, out, M, N, K, N, nullptr, 0, s);
         default:
-            return run_gemm<BigTile, SF, RES>(A, Wq, scale, residual, out, M, N, K, partials, workspace_bytes, s);
+            return run_gemm<BigTile, SF, RES>(A, Wq, scale, residual, out, M, N, K, N, partials, workspace_bytes, s);
     }
 }
 

@@ -161,8 +161,8 @@ __device__ __forceinline__ uint32_t residual_add_bf16x2(uint32_t y, uint32_t r) 
 template <int SF, bool RES>
 __global__ void __launch_bounds__(kThreads, 1)
 wide_gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,
-                 const uint16_t* __restrict__ res, uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
-                 int tiles, bool vec_out) {
+                 const uint16_t* __restrict__ res, uint16_t* __restrict__ out, int M, int N, int K, int ldo_elems,
+                 int tiles_m, int tiles, bool vec_out) {
     // One LDS array only (a second one makes the compiler wait for every
     // in-flight DMA before each LDS read).
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
@@ -369,16 +369,17 @@ wide_gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, 
         // one row (8 bytes of the output). Buffer stores over this tile's
         // rows: rows past M fall past the range and are dropped, columns past
         // N get an out-of-range offset.
-        const int rows_out = min(kTM, M - m0);
-        const __amdgpu_buffer_rsrc_t rsrc_o =
-            __builtin_amdgcn_make_buffer_rsrc(out + static_cast<int64_t>(m0) * N, 0, rows_out * N * 2, kBufferFlags);
-        __amdgpu_buffer_rsrc_t rsrc_r = rsrc_o;
-        if constexpr (RES)
-            rsrc_r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(res + static_cast<int64_t>(m0) * N), 0,
-                                                       rows_out * N * 2, kBufferFlags);
         // The row stride is recomputed here (not hoisted out of the tile loop
         // with its multiples, which would hold that many scalar registers).
-        const int ldo = __builtin_amdgcn_readfirstlane(opaque(N)) * 2;
+        const int ldo = __builtin_amdgcn_readfirstlane(opaque(ldo_elems)) * 2;
+        const int rows_out = min(kTM, M - m0);
+        const int out_bytes = (rows_out - 1) * ldo + N * 2;        // through column N - 1 of the last row
+        const __amdgpu_buffer_rsrc_t rsrc_o = __builtin_amdgcn_make_buffer_rsrc(
+            out + static_cast<int64_t>(m0) * ldo_elems, 0, out_bytes, kBufferFlags);
+        __amdgpu_buffer_rsrc_t rsrc_r = rsrc_o;
+        if constexpr (RES)
+            rsrc_r = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(res + static_cast<int64_t>(m0) * ldo_elems), 0, out_bytes, kBufferFlags);
         const int l = opaque(lane);
         const int row = kWaveRows * wm + (l & 31);                  // + 32 bi
         const int col = n0 + kWaveCols * wn + 4 * (l >> 5);         // + 32 bj + 8 a
@@ -437,37 +438,44 @@ wide_gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, 
 
 }  // namespace
 
-bool wide_gemm_fits(int64_t M, int64_t N, int64_t K) {
+bool wide_gemm_fits(int64_t M, int64_t N, int64_t K, int64_t ldo) {
     // Buffer offsets are 32-bit: one tile's rows of A, W and out must span
     // less than 2 GiB, so that an out-of-range offset plus any in-range part
     // stays past the range.
-    return M >= 1 && N >= 1 && K <= 128 * 64 * kScaleRegs &&
+    return M >= 1 && N >= 1 && ldo >= N && K <= 128 * 64 * kScaleRegs &&
            static_cast<int64_t>(kTM) * K * 2 < static_cast<int64_t>(kOutOfRange) &&
            static_cast<int64_t>(kTN) * K < static_cast<int64_t>(kOutOfRange) &&
-           static_cast<int64_t>(kTM) * N * 2 < static_cast<int64_t>(kOutOfRange);
+           static_cast<int64_t>(kTM) * ldo * 2 < static_cast<int64_t>(kOutOfRange);
 }
 
 bool wide_gemm_pays(int64_t M, int64_t N, int64_t K, int cus) {
-    if (!wide_gemm_fits(M, N, K) || cus <= 0) return false;
+    if (!wide_gemm_fits(M, N, K, N) || cus <= 0) return false;
     const int64_t tiles = ceil_div(M, kTM) * ceil_div(N, kTN);
     const int64_t rounds = ceil_div(tiles, cus);
     return tiles >= cus && 100 * tiles >= 85 * rounds * cus;
 }
 
+int64_t wide_gemm_columns(int64_t M, int64_t N, int64_t K, int cus) {
+    if (!wide_gemm_fits(M, N, K, N) || cus <= 0) return 0;
+    const int64_t tiles_m = ceil_div(M, kTM), tiles_n = ceil_div(N, kTN);
+    const int64_t rounds = tiles_m * tiles_n / cus;
+    return std::min(tiles_n, rounds * cus / tiles_m) * kTN;
+}
+
 int wide_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out, int64_t M,
-              int64_t N, int64_t K, hipStream_t stream) {
-    if (!wide_gemm_fits(M, N, K)) return W8A16_ERR_SHAPE;
+              int64_t N, int64_t K, int64_t ldo, hipStream_t stream) {
+    if (!wide_gemm_fits(M, N, K, ldo)) return W8A16_ERR_SHAPE;
     const int64_t tiles_m = ceil_div(M, kTM), tiles = tiles_m * ceil_div(N, kTN);
     if (tiles > INT32_MAX) return W8A16_ERR_SHAPE;
     const int grid = static_cast<int>(std::min<int64_t>(tiles, device_cu_count()));
     // 8-byte output stores need every run of 4 columns 8-byte aligned.
-    const bool vec_out = N % 4 == 0 && aligned(out, 8) && (!residual || aligned(residual, 8));
+    const bool vec_out = N % 4 == 0 && ldo % 4 == 0 && aligned(out, 8) && (!residual || aligned(residual, 8));
     auto go = [&](auto kernel) {
         return launch(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), stream,
                       static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
                       static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out), static_cast<int>(M),
-                      static_cast<int>(N), static_cast<int>(K), static_cast<int>(tiles_m), static_cast<int>(tiles),
-                      vec_out);
+                      static_cast<int>(N), static_cast<int>(K), static_cast<int>(ldo), static_cast<int>(tiles_m),
+                      static_cast<int>(tiles), vec_out);
     };
     if (residual) return go(&wide_gemm_kernel<kScaleBlockBf16, true>);
     switch (fmt) {

@@ -86,13 +86,18 @@ int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const
 // convert is done once per workgroup tile, with the block scale folded in.
 // K up to 32768; arguments as for w8a16_gemm (already checked by the
 // caller), `residual` as for skinny_gemm (BF16 block scales only).
-bool wide_gemm_fits(int64_t M, int64_t N, int64_t K);
+bool wide_gemm_fits(int64_t M, int64_t N, int64_t K, int64_t ldo);
 // Whether the 256 x 256 tiles keep the grid busy: at least one tile per CU
 // and every round of CU-many tiles at least 85 % full (a nearly empty last
 // round costs a whole tile time; the 128-row kernels then finish first).
 bool wide_gemm_pays(int64_t M, int64_t N, int64_t K, int cus);
+// Columns [0, n) that whole rounds of CU-many 256 x 256 tiles cover (a
+// multiple of 256, 0 if not even one round fits); the rest of the columns go
+// to the 128-row tiles.
+int64_t wide_gemm_columns(int64_t M, int64_t N, int64_t K, int cus);
+// ldo: the row stride of out and residual, in elements (>= N).
 int wide_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
-              int64_t M, int64_t N, int64_t K, hipStream_t stream);
+              int64_t M, int64_t N, int64_t K, int64_t ldo, hipStream_t stream);
 
 // Launch `kernel` with exactly the argument types of its signature; the HIP
 // launch status becomes W8A16_OK / W8A16_ERR_LAUNCH.

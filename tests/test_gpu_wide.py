@@ -168,3 +168,49 @@ def test_wide_scale_doubling_touches_only_its_block(dev):
     assert np.array_equal(got[:, ~cols], base[:, ~cols])
     ref, den = oracle.w8a16(A, W, S2)
     assert_within_tol(got, ref, den, "scale x2")
+
+
+# Columns split between the two tile families: when 256 x 256 tiles cover
+# at least one whole round of CU-many tiles but the rest is less than 85 %
+# of a round, whole rounds of them take the first columns (a multiple of
+# 256) and the 128-row tiles the remaining ones, written at their column
+# offset with the full row stride. M = 1000, N = 18000, K = 1040: 4 x 71
+# tiles of 256 x 256; the first 4 x 64 take columns 0..16383, and 8 x 13
+# tiles of 128 x 128 (a ragged last one: 1616 = 12 * 128 + 80) the rest
+# (K is not a multiple of 256, so whole tiles; with a workspace they split).
+# M = 1024, N = 18560, K = 4096 (the 1024-token in_proj; every element in
+# test_gpu_parity.py) takes the k-split workgroups for its 8 x 17 rest.
+SPLIT_N = (1000, 18000, 1040)
+
+
+@pytest.mark.parametrize("fmt", [None, "block_f32", "row_f32"])
+def test_wide_split_columns_every_element(dev, fmt):
+    M, N, K = SPLIT_N
+    say(f"wide + 128-row tiles {fmt or 'block_bf16'} M={M} N={N} K={K}")
+    A = inputs.activations(M, K, 3100)
+    if fmt is None:
+        W, S = inputs.weights(N, K, 0.02, 3200)
+    else:
+        W, S = inputs.weights_fmt(N, K, 0.02, 3200, fmt)
+    got = gemm(A, W, S, dev, fmt)
+    ref, den = oracle.w8a16(A, W, S, fmt=fmt or "block_bf16")
+    assert_within_tol(got, ref, den, f"split columns {fmt}")
+
+
+def test_wide_split_columns_residual_and_workspace(dev):
+    M, N, K = SPLIT_N
+    A = inputs.activations(M, K, 3300)
+    W, S = inputs.weights(N, K, 0.02, 3400)
+    R = inputs.activations(M, N, 3500)
+    dA, dW, dS = to_dev(A, torch.bfloat16, dev), to_dev(W, torch.uint8, dev), to_dev(S, torch.bfloat16, dev)
+    y = binding.w8a16_gemm(dA, dW, dS)
+    z = binding.w8a16_gemm_residual(dA, dW, dS, to_dev(R, torch.bfloat16, dev))
+    ws = binding.gemm_workspace(M, N, K, dev)
+    assert ws is not None
+    yw = binding.w8a16_gemm_ws(dA, dW, dS, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(z), oracle.bf16_rne(oracle.bf16_value(R) + oracle.bf16_value(bits(y))))
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(bits(yw), ref, den, "split columns, tail tiles split through the workspace")
+    # the 256 x 256 part is the same kernel either way: its columns are bit-identical
+    assert np.array_equal(bits(yw)[:, :16384], bits(y)[:, :16384])
