@@ -65,6 +65,8 @@ constexpr uint32_t kOutOfRange = 0x80000000u;           // buffer offset that re
 constexpr int kBufferFlags = 0x00020000;                // raw buffer, 32-bit data format
 constexpr int kXcds = 8;
 constexpr int kBandM = 4;                               // M-tiles per band of the tile order
+constexpr int kStRow = 528;                             // LDS row stride of the staged output tile (bytes)
+static_assert(kTM * kStRow <= kStages * kStageBytes, "the output tile fits in the stages");
 
 static_assert(kAChunks == 4 && kWChunks == 2, "DMA layout below");
 static_assert(2 * kWaveRows == kTM && 4 * kWaveCols == kTN, "2 x 4 waves");
@@ -146,6 +148,7 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t lo, uint32_t hi, float s) {
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
 // Two fp32 -> two BF16 (round to nearest even) in one dword, first in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
@@ -384,7 +387,17 @@ wide_gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, 
         const int row = kWaveRows * wm + (l & 31);                  // + 32 bi
         const int col = n0 + kWaveCols * wn + 4 * (l >> 5);         // + 32 bj + 8 a
         if (vec_out) {
-            // N % 4 == 0 and `out` 8-byte aligned: one 8-byte store per run.
+            // N and the row stride multiples of 8, out 16-byte aligned: the
+            // tile is staged in LDS as BF16 (rows 528 bytes apart, so the
+            // 8-byte writes of 32 lanes with 32 different rows spread over
+            // the banks) and written back as whole 512-byte rows, 16 bytes
+            // per lane: 16 wide stores per lane instead of 32 narrow ones,
+            // each instruction covering two whole rows of the tile. Before
+            // the stages are reused: every DMA of this wave (the zero loads
+            // past K included) has landed and its LDS reads have completed,
+            // then the barrier.
+            wait_vmem_lgkm<0, 0>();
+            lds_barrier();
 #pragma unroll
             for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
@@ -396,20 +409,26 @@ wide_gemm_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, 
                         for (int b = 0; b < 4; ++b) rs[b] = n < N ? row_scale<SF>(S, n + b) : 0.0f;
 #pragma unroll
                     for (int bi = 0; bi < BI; ++bi) {
-                        const uint32_t voff = n < N ? static_cast<uint32_t>(row * ldo + 2 * n) : kOutOfRange;
-                        const int soff = 32 * bi * ldo;
-                        uint32_t lo = pack_bf16x2(acc[bi][bj][4 * a] * rs[0], acc[bi][bj][4 * a + 1] * rs[1]);
-                        uint32_t hi = pack_bf16x2(acc[bi][bj][4 * a + 2] * rs[2], acc[bi][bj][4 * a + 3] * rs[3]);
-                        if constexpr (RES) {
-                            const u32x2_t r = __builtin_bit_cast(
-                                u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc_r, voff, soff, 0));
-                            lo = residual_add_bf16x2(lo, r[0]);
-                            hi = residual_add_bf16x2(hi, r[1]);
-                        }
-                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i32_t, u32x2_t{lo, hi}), rsrc_o,
-                                                              voff, soff, 0);
+                        const uint32_t lo = pack_bf16x2(acc[bi][bj][4 * a] * rs[0], acc[bi][bj][4 * a + 1] * rs[1]);
+                        const uint32_t hi = pack_bf16x2(acc[bi][bj][4 * a + 2] * rs[2], acc[bi][bj][4 * a + 3] * rs[3]);
+                        *reinterpret_cast<u32x2_t*>(smem + (row + 32 * bi) * kStRow + (n - n0) * 2) = u32x2_t{lo, hi};
                     }
                 }
+            lds_barrier();
+            const int tr = tid >> 5, tc = tid & 31;                  // 16 rows of 32 x 16 bytes per round
+            const int n = n0 + 8 * tc;
+#pragma unroll 4
+            for (int r = 0; r < kTM / 16; ++r) {
+                const int orow = 16 * r + tr;
+                u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + orow * kStRow + tc * 16);
+                const uint32_t voff = n < N ? static_cast<uint32_t>(orow * ldo + 2 * n) : kOutOfRange;
+                if constexpr (RES) {
+                    const u32x4_t rv = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc_r, voff, 0, 0));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = residual_add_bf16x2(v[i], rv[i]);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i32_t, v), rsrc_o, voff, 0, 0);
+            }
         } else {
 #pragma unroll
             for (int bj = 0; bj < BJ; ++bj)
@@ -469,7 +488,7 @@ int wide_gemm(const void* A, const void* Wq, const void* scale, int fmt, const v
     if (tiles > INT32_MAX) return W8A16_ERR_SHAPE;
     const int grid = static_cast<int>(std::min<int64_t>(tiles, device_cu_count()));
     // 8-byte output stores need every run of 4 columns 8-byte aligned.
-    const bool vec_out = N % 4 == 0 && ldo % 4 == 0 && aligned(out, 8) && (!residual || aligned(residual, 8));
+    const bool vec_out = N % 8 == 0 && ldo % 8 == 0 && aligned(out, 16) && (!residual || aligned(residual, 16));
     auto go = [&](auto kernel) {
         return launch(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), stream,
                       static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
