@@ -14,14 +14,20 @@ Cache, as decode over a real layer stack does.
 
 The JSON line reports the decode GEMV's HBM bandwidth as `value` (GB/s over
 both projections: algorithmic bytes / kernel time) and the prefill GEMM's
-TFLOP/s under `prefill`, each with a roofline object for its larger
-(in_proj) kernel. Kernel times come from HIP events on the launch stream:
-the GEMVs of one projection run back to back between two events (so the
-average launch duration is not inflated by per-event overhead), the GEMMs
-each between their own two events. `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workloads. `few_tokens` (outside the timed step)
-reports the same projections at M = 2..16 through the GEMV entry point (the
-multi-sequence decode workloads) and at M = 32..256 through the GEMM.
+TFLOP/s under `prefill`, each with a roofline object for the pair of
+launches it is quoted on (in_proj + out_proj), and `launches` has one
+roofline object per launch of the step. Kernel times come from HIP events
+on the launch stream: the GEMVs of one projection run back to back between
+two events (so the average launch duration is not inflated by per-event
+overhead), the GEMMs each between their own two events. `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workloads. `large_layer`
+(outside the timed step) times the 8192-token prefill GEMMs and the M = 1
+GEMVs of the hidden-8192 layer (in_proj K=8192 N=35072, out_proj K=16384
+N=8192). `few_tokens` (outside the timed step) reports the same projections
+at M = 2..16 through the GEMV entry point (the multi-sequence decode
+workloads) and at M = 32..256 through the GEMM, without and with a
+workspace (w8a16_gemm_ws), each against its binding roof max(bytes / HBM
+peak, flop / MFMA peak).
 `layer_ends` (outside the timed step) times the norm prologues and the
 residual epilogue: fused into the decode GEMV against the unfused chain, and
 the prefill norms and residual GEMM at M = 1024. `decode_layer` times one
@@ -29,7 +35,7 @@ Mamba-2 layer's whole decode step for one token (fused in_proj, conv1d
 update, SSM decode, fused out_proj) and the conv / SSM kernels alone.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-few-tokens]
-                    [--no-layer-ends]
+                    [--no-layer-ends] [--no-large-layer]
 
 Profile helpers (read rocprofv3 CSV output; no GPU needed):
     python bench.py --summarize-trace <dir>/<name>_kernel_trace.csv
@@ -60,7 +66,8 @@ ROTATE_BYTES = 1.2e9            # weight copies per projection span at least thi
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "gemv": ["gemm_mamba_ssm_amd/csrc/w8a16_gemv.hip", "gemm_mamba_ssm_amd/csrc/w8a16_device.h"],
-    "gemm": ["gemm_mamba_ssm_amd/csrc/w8a16_gemm.hip", "gemm_mamba_ssm_amd/csrc/w8a16_device.h"],
+    "gemm": ["gemm_mamba_ssm_amd/csrc/w8a16_gemm.hip", "gemm_mamba_ssm_amd/csrc/w8a16_gemm_wide.hip",
+             "gemm_mamba_ssm_amd/csrc/w8a16_device.h"],
 }
 METRIC = "M=1 GEMV HBM GB/s (%peak) + 1k-token prefill GEMM TFLOP/s (%MFMA peak)"
 CALIBRATION_BYTES = 256 << 20   # the plain copy run with --copy-calibration reads and writes this much
@@ -68,40 +75,54 @@ CALIBRATION_BYTES = 256 << 20   # the plain copy run with --copy-calibration rea
 # Launches of the timed step, told apart in profiler output by kernel name and
 # dispatch order: every step issues LAYERS in_proj GEMVs, LAYERS out_proj GEMVs,
 # then the in_proj GEMM and the out_proj GEMM, and nothing else in the process
-# launches these kernels. (label, kernel-name fragment)
-LAUNCHES = [
-    ("gemv_in_proj", "gemv_kernel"),
-    ("gemv_out_proj", "gemv_kernel"),
-    ("gemm_in_proj", "gemm_kernel"),
-    ("gemm_out_proj", "gemm_kernel"),
-]
+# launches these kernels. The 1024-token in_proj GEMM is two kernels (256 x 256
+# tiles over the first 16384 columns, then the k-split 128 x 128 tiles over the
+# rest), the out_proj GEMM one: of the GEMM dispatches that follow a step's
+# GEMVs, the last is the out_proj's and the others the in_proj's.
+LAUNCHES = ["gemv_in_proj", "gemv_out_proj", "gemm_in_proj", "gemm_out_proj"]
 DEFAULT_LAYERS = 8
+
+
+def _kernel_kind(name):
+    if "gemv" in name and "kernel" in name:
+        return "gemv"
+    if "gemm_kernel" in name or "combine_kernel" in name or "skinny" in name:
+        return "gemm"
+    return None
 
 
 def label_dispatches(rows, layers=DEFAULT_LAYERS):
     """Label each rocprofv3 CSV row (one per dispatch, or per dispatch and
-    counter) with its launch, from the dispatch order; None for other kernels."""
-    order = sorted({int(r["Dispatch_Id"]) for r in rows})
-    seen = {"gemv_kernel": {}, "gemm_kernel": {}}
-    labels_by_id = {}
+    counter) with its launch, from the dispatch order; None for other kernels.
+    GEMM labels carry the kernel too: 'gemm_in_proj:<kernel>'."""
     names = {int(r["Dispatch_Id"]): r["Kernel_Name"] for r in rows}
-    prev_gemm = None
+    order = sorted(names)
+    labels_by_id = {}
+    gemv_seen = 0
+    pending = []                                 # GEMM dispatches since the last GEMV
+
+    def flush():
+        for j, d in enumerate(pending):
+            proj = "gemm_out_proj" if j == len(pending) - 1 else "gemm_in_proj"
+            labels_by_id[d] = f"{proj}:{short_name(names[d])}"
+        pending.clear()
+
     for d in order:
-        name = names[d]
-        if "combine_kernel" in name:            # the split-tile combine after a GEMM
-            labels_by_id[d] = f"{prev_gemm}_combine" if prev_gemm else None
-            continue
-        frag = next((f for f in seen if f in name), None)
-        if frag is None:
-            labels_by_id[d] = None
-            continue
-        i = len(seen[frag])
-        seen[frag][d] = i
-        if frag == "gemv_kernel":
-            labels_by_id[d] = "gemv_in_proj" if (i // layers) % 2 == 0 else "gemv_out_proj"
+        kind = _kernel_kind(names[d])
+        if kind == "gemv":
+            flush()
+            labels_by_id[d] = "gemv_in_proj" if (gemv_seen // layers) % 2 == 0 else "gemv_out_proj"
+            gemv_seen += 1
+        elif kind == "gemm":
+            pending.append(d)
         else:
-            labels_by_id[d] = prev_gemm = "gemm_in_proj" if i % 2 == 0 else "gemm_out_proj"
+            labels_by_id[d] = None
+    flush()
     return [labels_by_id[int(r["Dispatch_Id"])] for r in rows]
+
+
+def short_name(name):
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").replace("w8a16::", "").split("(")[0]
 
 
 def source_digest(kind: str) -> str:
@@ -143,7 +164,7 @@ def summarize_trace(path, layers=DEFAULT_LAYERS):
     print("| launch | kernel | grid (threads) | dispatches | mean us | min us | max us |")
     print("|---|---|---|---|---|---|---|")
     for (lab, name, grid), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        short = short_name(name)
         print(f"| {lab} | {short} | {grid} | {len(d)} | {np.mean(d) / 1e3:.2f} | "
               f"{np.min(d) / 1e3:.2f} | {np.max(d) / 1e3:.2f} |")
 
@@ -164,7 +185,11 @@ def summarize_counters(fetch_csv, write_csv, layers=DEFAULT_LAYERS):
         if not calib:
             raise SystemExit(f"no calibration copy found in {path}")
         factor = (CALIBRATION_BYTES / 1024) / float(np.median(calib))
-        return {k: float(np.median(v)) for k, v in vals.items()}, factor
+        per = {k: float(np.median(v)) for k, v in vals.items()}
+        launch = {}                              # a launch's kernels add up
+        for k, v in per.items():
+            launch[k.split(":")[0]] = launch.get(k.split(":")[0], 0.0) + v
+        return launch, factor
 
     fetch, f_fac = per_launch(fetch_csv, "FETCH_SIZE")
     write, w_fac = per_launch(write_csv, "WRITE_SIZE")
@@ -224,16 +249,25 @@ FEW_TOKEN_GEMV_M = (2, 4, 8, 16)            # multi-sequence decode (w8a16_gemv)
 FEW_TOKEN_GEMM_M = (32, 64, 128, 256)        # skinny prefill / verify (w8a16_gemm)
 
 
+def binding_roof_s(nbytes, flop):
+    """Time at the binding roof: the larger of bytes at the HBM peak and flop
+    at the dense bf16 MFMA peak (seconds)."""
+    return max(nbytes / (HBM_PEAK_GBS * 1e9), flop / (BF16_PEAK_TFLOPS * 1e12))
+
+
 def few_token_report(projs, device, stream, L, check, reps=10):
     """Outside the timed step: the same projections at a few tokens, through
     w8a16_gemv (M = 2..16, the multi-sequence decode workloads) and w8a16_gemm
-    (M = 32..256). Weight copies rotate as in the decode step; each figure is
-    the mean over `reps` runs of L back-to-back launches between two events."""
+    (M = 32..256), the GEMM also through w8a16_gemm_ws with a workspace (the
+    k-split schedule of shapes whose tiles do not fill the GPU). Weight copies
+    rotate as in the decode step; each figure is the mean over `reps` runs of
+    L back-to-back launches between two events. `roof` is the fraction of the
+    binding roof max(bytes / 8 TB/s, flop / 2.5166 PFLOP/s)."""
     sh = stream.cuda_stream
-    out = {"unit": "us per launch; GB/s = algorithmic bytes / time; frac = of 8 TB/s",
-           "gemv": [], "gemm": []}
-    for entry, ms in (("gemv", FEW_TOKEN_GEMV_M), ("gemm", FEW_TOKEN_GEMM_M)):
-        raw = binding.gemv_raw if entry == "gemv" else binding.gemm_raw
+    out = {"unit": "us per launch; GB/s = algorithmic bytes / time; roof = binding-roof time / time, "
+                   "binding roof = max(bytes / 8 TB/s, flop / 2516.6 TFLOP/s)",
+           "gemv": [], "gemm": [], "gemm_ws": []}
+    for entry, ms in (("gemv", FEW_TOKEN_GEMV_M), ("gemm", FEW_TOKEN_GEMM_M), ("gemm_ws", FEW_TOKEN_GEMM_M)):
         for m in ms:
             row = {"M": m}
             for proj in projs:
@@ -245,10 +279,19 @@ def few_token_report(projs, device, stream, L, check, reps=10):
                     A = inputs.activations(m, p.K, 5000 + m)
                 dA = to_dev(A, torch.bfloat16, device)
                 dO = torch.empty((m, p.N), dtype=torch.bfloat16, device=device)
+                ws = binding.gemm_workspace(m, p.N, p.K, device) if entry == "gemm_ws" else None
 
                 def launch(i):
-                    check(raw(dA.data_ptr(), proj.W[i % proj.copies].data_ptr(), proj.S[i % proj.copies].data_ptr(),
-                              dO.data_ptr(), m, p.N, p.K, sh), entry)
+                    w, s_ = proj.W[i % proj.copies].data_ptr(), proj.S[i % proj.copies].data_ptr()
+                    if entry == "gemv":
+                        st = binding.gemv_raw(dA.data_ptr(), w, s_, dO.data_ptr(), m, p.N, p.K, sh)
+                    elif entry == "gemm":
+                        st = binding.gemm_raw(dA.data_ptr(), w, s_, dO.data_ptr(), m, p.N, p.K, sh)
+                    else:
+                        st = binding.gemm_ws_raw(dA.data_ptr(), w, s_, dO.data_ptr(), m, p.N, p.K,
+                                                 ws.data_ptr() if ws is not None else 0,
+                                                 ws.numel() if ws is not None else 0, sh)
+                    check(st, entry)
 
                 for i in range(L):
                     launch(i)
@@ -261,10 +304,72 @@ def few_token_report(projs, device, stream, L, check, reps=10):
                 torch.cuda.synchronize()
                 t = np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e-3 for r in range(reps)]) / L
                 nbytes = p.N * p.K + 2 * (-(-p.N // 128)) * (-(-p.K // 128)) + 2 * m * p.K + 2 * m * p.N
+                flop = 2 * m * p.N * p.K
                 row[p.name] = {"us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
-                               "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                               "TFLOP/s": round(2 * m * p.N * p.K / t / 1e12, 2)}
+                               "TFLOP/s": round(flop / t / 1e12, 2),
+                               "roof": round(binding_roof_s(nbytes, flop) / t, 4),
+                               "workspace_bytes": ws.numel() if ws is not None else 0}
+                if entry != "gemm_ws":
+                    del row[p.name]["workspace_bytes"]
             out[entry].append(row)
+    return out
+
+
+def large_layer_report(device, stream, check, reps=5, L=4):
+    """Outside the timed step: the hidden-8192 layer (in_proj K=8192 N=35072,
+    out_proj K=16384 N=8192): the 8192-token prefill GEMM of each projection
+    (mean over `reps` launches, each between two events) and the M = 1 decode
+    GEMV (L back-to-back launches over rotating weight copies, `reps` times),
+    on the same seeded generator as the tests."""
+    sh = stream.cuda_stream
+    out = {"unit": "us per launch", "workload": "prefill_8k_large (M=8192) and decode_m1_large (M=1)"}
+    for p_pre, p_dec in zip(inputs.WORKLOADS["prefill_8k_large"], inputs.WORKLOADS["decode_m1_large"]):
+        A, W, S = inputs.make(p_pre)
+        dA, dW, dS = to_dev(A, torch.bfloat16, device), to_dev(W, torch.uint8, device), to_dev(S, torch.bfloat16, device)
+        del A
+        dO = torch.empty((p_pre.M, p_pre.N), dtype=torch.bfloat16, device=device)
+
+        def gemm():
+            check(binding.gemm_raw(dA.data_ptr(), dW.data_ptr(), dS.data_ptr(), dO.data_ptr(), p_pre.M, p_pre.N,
+                                   p_pre.K, sh), "gemm")
+
+        gemm()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for r in range(reps):
+            ev[2 * r].record(stream)
+            gemm()
+            ev[2 * r + 1].record(stream)
+        torch.cuda.synchronize()
+        t = float(np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e-3 for r in range(reps)]))
+        f = p_pre.flops()
+        rec = {"gemm": {"M": p_pre.M, "us": round(t * 1e6, 1), "TFLOP/s": round(f / t / 1e12, 1),
+                        "frac_of_mfma_peak": round(f / t / 1e12 / BF16_PEAK_TFLOPS, 4)}}
+        del dA, dO
+        copies = max(2, math.ceil(ROTATE_BYTES / W.nbytes))
+        Ws = [dW] + [dW.clone() for _ in range(copies - 1)]
+        a1 = to_dev(inputs.make(p_dec)[0], torch.bfloat16, device)
+        o1 = torch.empty((1, p_dec.N), dtype=torch.bfloat16, device=device)
+
+        def gemv(i):
+            check(binding.gemv_raw(a1.data_ptr(), Ws[i % copies].data_ptr(), dS.data_ptr(), o1.data_ptr(), 1,
+                                   p_dec.N, p_dec.K, sh), "gemv")
+
+        for i in range(L):
+            gemv(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for r in range(reps):
+            ev[2 * r].record(stream)
+            for i in range(L):
+                gemv(r * L + i)
+            ev[2 * r + 1].record(stream)
+        torch.cuda.synchronize()
+        t = float(np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e-3 for r in range(reps)])) / L
+        b = p_dec.bytes_moved()
+        rec["gemv"] = {"M": 1, "us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                       "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "weight_copies_rotated": copies}
+        out[p_pre.name] = rec
+        del Ws, dW
+        torch.cuda.empty_cache()
     return out
 
 
@@ -601,6 +706,8 @@ def main():
                          "--summarize-trace / --summarize-counters label)")
     ap.add_argument("--no-layer-ends", action="store_true",
                     help="skip the norm prologue / residual epilogue and layer decode-step timings (profiler runs)")
+    ap.add_argument("--no-large-layer", action="store_true",
+                    help="skip the hidden-8192 layer's 8192-token GEMMs and M = 1 GEMVs (profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--layers", type=int, default=DEFAULT_LAYERS, help="decode layers (weight copies) per step")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -665,6 +772,7 @@ def main():
     wall = time.perf_counter() - t0
 
     few = None if args.no_few_tokens else few_token_report(projs, device, stream, L, check)
+    large = None if args.no_large_layer else large_layer_report(device, stream, check)
     ends = None if args.no_layer_ends else layer_ends_report(projs, device, stream, L, check)
     layer = None if args.no_layer_ends else decode_layer_report(projs, device, stream, L, check)
 
@@ -687,6 +795,21 @@ def main():
         return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic}
 
+    def pair_traffic(kind):
+        t = [measured_traffic(kind, f"{kind}_{p}") for p in ("in_proj", "out_proj")]
+        return None if None in t else sum(t)
+
+    launches = {
+        "gemv_in_proj": roof("hbm", b_in / mean[0] / 1e9, HBM_PEAK_GBS, "GB/s", measured_traffic("gemv", "gemv_in_proj")),
+        "gemv_out_proj": roof("hbm", b_out / mean[1] / 1e9, HBM_PEAK_GBS, "GB/s",
+                              measured_traffic("gemv", "gemv_out_proj")),
+        "gemm_in_proj": roof("mfma", f_in / mean[2] / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s",
+                             measured_traffic("gemm", "gemm_in_proj")),
+        "gemm_out_proj": roof("mfma", f_out / mean[3] / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s",
+                              measured_traffic("gemm", "gemm_out_proj")),
+    }
+    for k, i in zip(LAUNCHES, range(4)):
+        launches[k]["us"] = round(mean[i] * 1e6, 3)
     rec = {
         "metric": METRIC,
         "value": round(gemv_gbs, 1),
@@ -710,14 +833,15 @@ def main():
         "frac_of_hbm_peak": round(gemv_gbs / HBM_PEAK_GBS, 4),
         "kernel_us": {"gemv_in_proj": round(mean[0] * 1e6, 3), "gemv_out_proj": round(mean[1] * 1e6, 3),
                       "gemm_in_proj": round(mean[2] * 1e6, 3), "gemm_out_proj": round(mean[3] * 1e6, 3)},
-        "roofline": roof("hbm", b_in / mean[0] / 1e9, HBM_PEAK_GBS, "GB/s",
-                         measured_traffic("gemv", "gemv_in_proj")),
+        # the pair of decode GEMV launches the metric is quoted on (in_proj + out_proj)
+        "roofline": roof("hbm", gemv_gbs, HBM_PEAK_GBS, "GB/s", pair_traffic("gemv")),
         "prefill": {
             "value": round(gemm_tfs, 2), "unit": "TFLOP/s",
             "frac_of_mfma_peak": round(gemm_tfs / BF16_PEAK_TFLOPS, 4),
-            "roofline": roof("mfma", f_in / mean[2] / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s",
-                             measured_traffic("gemm", "gemm_in_proj")),
+            "roofline": roof("mfma", gemm_tfs, BF16_PEAK_TFLOPS, "TFLOP/s", pair_traffic("gemm")),
         },
+        "launches": launches,
+        "large_layer": large,
         "few_tokens": few,
         "layer_ends": ends,
         "decode_layer": layer,
