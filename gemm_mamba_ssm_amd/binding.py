@@ -32,13 +32,15 @@ BLOCK = 128
 
 EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_gemv_ex", "w8a16_gemm_ex", "w8a16_gemm_workspace_size",
            "w8a16_gemm_ws", "w8a16_rmsnorm", "w8a16_gemv_fused", "w8a16_gemm_residual", "w8a16_conv1d_update",
-           "w8a16_gemv_in_proj", "w8a16_ssm_decode", "w8a16_dequant", "w8a16_strerror")
+           "w8a16_gemv_in_proj", "w8a16_ssm_decode", "w8a16_dequant", "w8a16_strerror",
+           "w8a16_gemm_noalloc", "w8a16_gemm_noalloc_scratch_bytes")
 
 # enum w8a16_scale_format
 SCALE_BLOCK_BF16, SCALE_BLOCK_F32, SCALE_ROW_F32 = 0, 1, 2
 SCALE_FORMATS = {"block_bf16": SCALE_BLOCK_BF16, "block_f32": SCALE_BLOCK_F32, "row_f32": SCALE_ROW_F32}
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_ALIAS, ERR_ARG, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7
+ERR_SCRATCH = -8
 WORKSPACE_ALIGN = 256
 GEMV_MAX_M = 16
 GEMV_MAX_K_SMALL_M = 16384   # M <= 8
@@ -78,6 +80,10 @@ def load() -> ctypes.CDLL:
     lib.w8a16_gemm_workspace_size.argtypes = [I64, I64, I64]
     lib.w8a16_gemm_ws.restype = ctypes.c_int
     lib.w8a16_gemm_ws.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P]
+    lib.w8a16_gemm_noalloc.restype = ctypes.c_int
+    lib.w8a16_gemm_noalloc.argtypes = [P, P, P, P, I64, I64, I64, P]
+    lib.w8a16_gemm_noalloc_scratch_bytes.restype = I64
+    lib.w8a16_gemm_noalloc_scratch_bytes.argtypes = []
     F = ctypes.c_float
     lib.w8a16_rmsnorm.restype = ctypes.c_int
     lib.w8a16_rmsnorm.argtypes = [P, P, P, F, P, I64, I64, P]
@@ -121,6 +127,15 @@ def gemm_workspace_size(M: int, N: int, K: int) -> int:
 def gemm_ws_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: int, workspace: int,
                 workspace_bytes: int, stream: int = 0) -> int:
     return load().w8a16_gemm_ws(A, Wq, scale, out, M, N, K, workspace or None, workspace_bytes, stream)
+
+
+def gemm_noalloc_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    return load().w8a16_gemm_noalloc(A, Wq, scale, out, M, N, K, stream)
+
+
+def gemm_noalloc_scratch_bytes() -> int:
+    """Bytes of the library's static scratch that w8a16_gemm_noalloc uses per GPU."""
+    return load().w8a16_gemm_noalloc_scratch_bytes()
 
 
 def gemv_ex_raw(A: int, Wq: int, scale: int, scale_format: int, out: int, M: int, N: int, K: int,

@@ -31,6 +31,8 @@ extern "C" const char* w8a16_strerror(int status) {
         case W8A16_ERR_ALIAS: return "out overlaps an input buffer";
         case W8A16_ERR_ARG: return "invalid argument";
         case W8A16_ERR_WORKSPACE: return "the GEMM workspace is smaller than w8a16_gemm_workspace_size";
+        case W8A16_ERR_SCRATCH:
+            return "the shape needs more scratch than w8a16_gemm_noalloc holds (w8a16_gemm_noalloc_scratch_bytes)";
         default: return "unknown w8a16 status";
     }
 }

@@ -56,6 +56,7 @@
 // of the tile's k-steps on its own LDS stages, and the two fp32 halves are
 // added in LDS at the end, so nothing goes through memory twice and no second
 // kernel runs (BigSplit below).
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -923,6 +924,60 @@ extern "C" int w8a16_gemm_ws(const void* A, const void* Wq, const void* scale, v
         return W8A16_ERR_ALIAS;
     return gemm_by_shape<kScaleBlockBf16, false>(A, Wq, scale, nullptr, out, M, N, K, static_cast<hipStream_t>(stream),
                                                  static_cast<float*>(workspace), static_cast<size_t>(workspace_bytes));
+}
+
+// Scratch of the allocation-free GEMM: the split schedule's fp32 partial
+// tiles, in a device array of the code object (each GPU holds its own copy,
+// from the first call on it until the process ends). 64 MiB is what the
+// largest split schedule on a 256-CU device needs: two 128 x 128 fp32 tiles
+// for each of 512 workgroups.
+constexpr int64_t kScratchBytes = 64ll << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace w8a16 {
+namespace {
+
+constexpr int kScratchDevices = 64;
+
+// The scratch array's device address on the current device, looked up once
+// per device with that device current (host code names the array only
+// through this address). nullptr when the lookup fails.
+float* scratch_on_current_device() {
+    static std::mutex mu;
+    static float* addr[kScratchDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        addr[dev] = static_cast<float*>(p);
+    }
+    return addr[dev];
+}
+
+}  // namespace
+}  // namespace w8a16
+
+extern "C" int64_t w8a16_gemm_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int w8a16_gemm_noalloc(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N,
+                                  int64_t K, void* stream) {
+    using namespace w8a16;
+    bool noop = false;
+    const int st = check_product_args(A, Wq, scale, out, M, N, K, &noop);
+    if (st != W8A16_OK || noop) return st;
+    const int64_t need = workspace_bytes_for(M, N, K);
+    if (need > kScratchBytes) return W8A16_ERR_SCRATCH;
+    if (need == 0)                                   // whole tiles: no scratch
+        return gemm_by_shape<kScaleBlockBf16, false>(A, Wq, scale, nullptr, out, M, N, K,
+                                                     static_cast<hipStream_t>(stream));
+    float* ws = scratch_on_current_device();
+    if (ws == nullptr) return W8A16_ERR_LAUNCH;
+    // Every partial tile is written by its workgroup before the combine
+    // kernel reads it, so nothing in the scratch needs clearing first.
+    return gemm_by_shape<kScaleBlockBf16, false>(A, Wq, scale, nullptr, out, M, N, K, static_cast<hipStream_t>(stream),
+                                                 ws, static_cast<size_t>(kScratchBytes));
 }
 
 extern "C" int w8a16_gemm_residual(const void* A, const void* Wq, const void* scale, const void* residual,

@@ -53,7 +53,9 @@ enum w8a16_status {
     W8A16_ERR_LAUNCH = -4, /* the HIP launch failed                             */
     W8A16_ERR_ALIAS = -5,  /* out overlaps an input                             */
     W8A16_ERR_ARG = -6,    /* another argument is invalid                       */
-    W8A16_ERR_WORKSPACE = -7 /* w8a16_gemm_ws: the workspace is too small         */
+    W8A16_ERR_WORKSPACE = -7, /* w8a16_gemm_ws: the workspace is too small        */
+    W8A16_ERR_SCRATCH = -8  /* w8a16_gemm_noalloc: the shape needs more scratch
+                               than w8a16_gemm_noalloc_scratch_bytes()          */
 };
 
 /*
@@ -164,6 +166,28 @@ int w8a16_gemm_ex(const void* A, const void* Wq, const void* scale, int scale_fo
 int64_t w8a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 int w8a16_gemm_ws(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * The GEMM for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc) and
+ * still want w8a16_gemm_ws's split schedule: the same kernels and the same
+ * result, bit for bit, as w8a16_gemm_ws with a large enough workspace, but
+ * the partial tiles go to a scratch array that the library holds in device
+ * memory, w8a16_gemm_noalloc_scratch_bytes() bytes (64 MiB) per GPU, from
+ * the first call on a GPU until the process ends. Nothing is allocated per
+ * call. A shape whose schedule needs more scratch than that (none on a
+ * 256-CU MI355X; w8a16_gemm_workspace_size reports the need) returns
+ * W8A16_ERR_SCRATCH and launches nothing. Operands, shapes, alignment,
+ * aliasing and the other errors are those of w8a16_gemm; W8A16_ERR_LAUNCH
+ * also reports a failed lookup of the scratch array's device address.
+ * Every call on one GPU shares that GPU's scratch: calls that may run at the
+ * same time on one GPU (two streams, two host threads) race and must be
+ * serialised by the caller. The scratch keeps the last call's partial tiles;
+ * no call needs it cleared.
+ */
+int64_t w8a16_gemm_noalloc_scratch_bytes(void);
+int w8a16_gemm_noalloc(const void* A, const void* Wq, const void* scale, void* out, int64_t M, int64_t N, int64_t K,
+                       void* stream);
 
 /*
  * Norm prologues and the residual epilogue of the Mamba-2 layer around its

@@ -31,7 +31,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_covers_every_status():
     for st in (binding.OK, binding.ERR_NULL, binding.ERR_SHAPE, binding.ERR_ALIGN,
-               binding.ERR_LAUNCH, binding.ERR_ALIAS, binding.ERR_ARG, binding.ERR_WORKSPACE):
+               binding.ERR_LAUNCH, binding.ERR_ALIAS, binding.ERR_ARG, binding.ERR_WORKSPACE,
+               binding.ERR_SCRATCH):
         s = binding.strerror(st)
         assert s and "unknown" not in s
     assert "unknown" in binding.strerror(12345)
@@ -330,3 +331,19 @@ def test_gemm_ws_rejections_before_any_hip_call():
     assert call(A, Wq, scale, out, M, N, K, out, need, 0) == binding.ERR_ALIAS
     assert call(A, Wq, scale, out, M, N, 136, wsp, need, 0) == binding.ERR_SHAPE
     assert call(A, Wq, scale, out, 0, N, K, wsp, 0, 0) == binding.OK        # no-op
+
+
+def test_gemm_noalloc_scratch_and_rejections_before_any_hip_call():
+    # 64 MiB: two 128 x 128 fp32 partial tiles for each of 512 workgroups,
+    # the largest split schedule on a 256-CU device
+    assert binding.gemm_noalloc_scratch_bytes() == 64 << 20
+    for M, N, K in ((32, 4096, 8192), (128, 4096, 8192), (256, 18560, 4096), (129, 1000, 1040)):
+        assert 0 < binding.gemm_workspace_size(M, N, K) <= binding.gemm_noalloc_scratch_bytes()
+    A, Wq, scale, out = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    call = binding.gemm_noalloc_raw
+    assert call(A, Wq, scale, out, 128, 4096, 136, 0) == binding.ERR_SHAPE
+    assert call(A, Wq, scale, out, -1, 4096, 8192, 0) == binding.ERR_SHAPE
+    assert call(0, Wq, scale, out, 128, 4096, 8192, 0) == binding.ERR_NULL
+    assert call(A + 2, Wq, scale, out, 128, 4096, 8192, 0) == binding.ERR_ALIGN
+    assert call(A, Wq, scale, A, 128, 4096, 8192, 0) == binding.ERR_ALIAS
+    assert call(A, Wq, scale, out, 0, 4096, 8192, 0) == binding.OK          # no-op
