@@ -121,6 +121,89 @@ def label_dispatches(rows, layers=DEFAULT_LAYERS):
     return [labels_by_id[int(r["Dispatch_Id"])] for r in rows]
 
 
+LARGE_REPS, LARGE_L = 5, 4                     # large_layer_report's repetitions and GEMVs per repetition
+
+
+def label_large(rows, reps=LARGE_REPS, L=LARGE_L):
+    """Labels for a --large-layer-only run, which issues per projection (in_proj,
+    then out_proj) 1 + reps GEMMs and then L + reps * L GEMVs."""
+    names = {int(r["Dispatch_Id"]): r["Kernel_Name"] for r in rows}
+    labels_by_id, gemvs, gemms = {}, 0, 0
+    per_proj_gemv = L + reps * L
+    for d in sorted(names):
+        kind = _kernel_kind(names[d])
+        if kind == "gemm":
+            proj = "in_proj" if gemms < 1 + reps else "out_proj"
+            labels_by_id[d] = f"gemm8k_{proj}:{short_name(names[d])}"
+            gemms += 1
+        elif kind == "gemv":
+            labels_by_id[d] = "gemv_large_" + ("in_proj" if gemvs < per_proj_gemv else "out_proj")
+            gemvs += 1
+        else:
+            labels_by_id[d] = None
+    return [labels_by_id[int(r["Dispatch_Id"])] for r in rows]
+
+
+def summarize_sq(csvs, layers=DEFAULT_LAYERS, large=False):
+    """Matrix-core and LDS counters per GEMM launch (and per kernel of it) from
+    rocprofv3 --pmc runs (several CSVs, one per pass). Per dispatch, counters
+    are summed over the GPU; GRBM_GUI_ACTIVE over its 8 XCDs."""
+    XCDS, SIMDS = 8, 4
+    per = {}                                     # (label) -> counter -> [values per dispatch]
+    dur = {}
+    for path in csvs:
+        rows = _read_csv(path)
+        labels = label_large(rows) if large else label_dispatches(rows, layers)
+        if rows and "Counter_Name" not in rows[0]:           # a kernel trace of one of the runs
+            for r, lab in zip(rows, labels):
+                if lab is not None and lab.startswith("gemm"):
+                    dur.setdefault(lab, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+            continue
+        acc = {}
+        for r, lab in zip(rows, labels):
+            if lab is None or not lab.startswith("gemm"):
+                continue
+            key = (lab, int(r["Dispatch_Id"]), r["Counter_Name"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        for (lab, _, c), v in acc.items():
+            per.setdefault(lab, {}).setdefault(c, []).append(v)
+    flops = {}
+    wl = inputs.WORKLOADS["prefill_8k_large" if large else "prefill_1k"]
+    for p in wl:
+        flops[("gemm8k_" if large else "gemm_") + p.name] = p.flops()
+    cus = 256
+    print("| launch : kernel | dispatches | median us | MOPS_BF16 x 512 / (2MNK) | clock GHz (GUI/XCD per us) | "
+          "MFMA busy (of GUI cycles) | MFMA busy cycles / (us x 2.4 GHz) | LDS bank conflict / LDS active | "
+          "LDS cmd FIFO full / LDS active |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    launch_mops = {}
+    for lab in sorted(per):
+        c = {k: float(np.median(v)) for k, v in per[lab].items()}
+        n = max(len(v) for v in per[lab].values())
+        base = lab.split(":")[0]
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        if mops is not None:
+            launch_mops[base] = launch_mops.get(base, 0.0) + mops
+        gui = c.get("GRBM_GUI_ACTIVE")
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        util = busy / (gui / XCDS * cus * SIMDS) if gui and busy is not None else None
+        lds = c.get("SQ_LDS_IDX_ACTIVE")
+        conf = c.get("SQ_LDS_BANK_CONFLICT")
+        fifo = c.get("SQ_LDS_CMD_FIFO_FULL")
+        t = float(np.median(dur[lab])) if lab in dur else None
+
+        def f(x, fmt):
+            return format(x, fmt) if x is not None else "-"
+        print(f"| {lab} | {n} | {f(t, '.1f')} | {f(mops * 512 / flops[base] if mops is not None and base in flops else None, '.4f')} | "
+              f"{f(gui / XCDS / t / 1e3 if gui and t else None, '.2f')} | {f(util, '.3f')} | "
+              f"{f(busy / (t * 1e-6 * 2.4e9 * cus * SIMDS) if busy is not None and t else None, '.3f')} | "
+              f"{f(conf / lds if lds and conf is not None else None, '.4f')} | {f(fifo / lds if lds and fifo is not None else None, '.4f')} |")
+    for base, m in sorted(launch_mops.items()):
+        if base in flops:
+            print(f"\n{base}: MOPS_BF16 x 512 = {m * 512:.6g} flop per launch, 2MNK = {flops[base]:.6g} "
+                  f"(ratio {m * 512 / flops[base]:.4f})")
+
+
 def short_name(name):
     return name.replace("(anonymous namespace)::", "").replace("void ", "").replace("w8a16::", "").split("(")[0]
 
@@ -153,11 +236,11 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-def summarize_trace(path, layers=DEFAULT_LAYERS):
+def summarize_trace(path, layers=DEFAULT_LAYERS, large=False):
     """Average duration per launch (and per other kernel) from a rocprofv3 kernel_trace.csv."""
     rows = _read_csv(path)
     by = {}
-    for r, lab in zip(rows, label_dispatches(rows, layers)):
+    for r, lab in zip(rows, label_large(rows) if large else label_dispatches(rows, layers)):
         name = r["Kernel_Name"]
         grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1)
         by.setdefault((lab or "", name, grid), []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
@@ -194,7 +277,8 @@ def summarize_counters(fetch_csv, write_csv, layers=DEFAULT_LAYERS):
     fetch, f_fac = per_launch(fetch_csv, "FETCH_SIZE")
     write, w_fac = per_launch(write_csv, "WRITE_SIZE")
     rec = {"source": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, of "
-                     "`python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-few-tokens --no-layer-ends --copy-calibration`",
+                     "`python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-few-tokens --no-layer-ends --no-large-layer "
+                     "--copy-calibration`",
            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4), "kernels": {}}
     for lab in fetch:
         kind = lab.split("_")[0]
@@ -315,7 +399,7 @@ def few_token_report(projs, device, stream, L, check, reps=10):
     return out
 
 
-def large_layer_report(device, stream, check, reps=5, L=4):
+def large_layer_report(device, stream, check, reps=LARGE_REPS, L=LARGE_L):
     """Outside the timed step: the hidden-8192 layer (in_proj K=8192 N=35072,
     out_proj K=16384 N=8192): the 8192-token prefill GEMM of each projection
     (mean over `reps` launches, each between two events) and the M = 1 decode
@@ -714,12 +798,21 @@ def main():
                     help="end with a plain device copy of 256 MiB (for HBM counter calibration)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-sq", nargs="+", metavar="CSV",
+                    help="matrix-core / LDS counter summary of the GEMM launches: the counter_collection.csv of "
+                         "each --pmc pass and the kernel_trace.csv of those runs")
+    ap.add_argument("--large-layer-only", action="store_true",
+                    help="run only the hidden-8192 layer's leg and print it (profiler runs; with --summarize-* "
+                         "label dispatches as that leg's)")
     args = ap.parse_args()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.layers)
+        summarize_trace(args.summarize_trace, args.layers, large=args.large_layer_only)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, layers=args.layers)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.layers, large=args.large_layer_only)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path; "
@@ -731,6 +824,14 @@ def main():
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     binding.load()
+    if args.large_layer_only:
+        stream = torch.cuda.current_stream(device)
+
+        def check_large(st, kind):
+            if st != binding.OK:
+                raise binding.W8A16Error(f"w8a16_{kind}", st)
+        print(json.dumps({"large_layer": large_layer_report(device, stream, check_large)}), flush=True)
+        return
 
     dec, pre = inputs.WORKLOADS["decode_m1"], inputs.WORKLOADS["prefill_1k"]
     projs = [Projection(dec[i], pre[i], device) for i in range(2)]

@@ -46,3 +46,32 @@ def test_binding_roof_is_the_larger_time():
     assert abs(bench.binding_roof_s(8e12, 0) - 1.0) < 1e-12          # 8 TB at 8 TB/s
     assert abs(bench.binding_roof_s(0, 2516.6e12) - 1.0) < 1e-12     # 2516.6 Tflop at the MFMA peak
     assert abs(bench.binding_roof_s(8e12, 2 * 2516.6e12) - 2.0) < 1e-12
+
+
+def test_summarize_sq_on_synthetic_csvs(tmp_path, capsys):
+    import csv
+    layers = 2
+    gemv = "void w8a16::gemv_kernel<4>(...)"
+    wide = "void w8a16::wide_gemm_kernel<0, false>(...)"
+    tile = "void w8a16::gemm_kernel_128(...)"
+    names = [gemv] * 4 + [wide, tile, tile]
+    pmc, trace = tmp_path / "p_counter_collection.csv", tmp_path / "t_kernel_trace.csv"
+    with open(pmc, "w", newline="") as f:
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for d, n in enumerate(names, 1):
+            for c, v in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e6), ("GRBM_GUI_ACTIVE", 8e5),
+                         ("SQ_VALU_MFMA_BUSY_CYCLES", 2.048e8)):
+                for _ in range(2):                   # two rows per counter: summed
+                    w.writerow({"Dispatch_Id": d, "Kernel_Name": n, "Counter_Name": c, "Counter_Value": v / 2})
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for d, n in enumerate(names, 1):
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": n, "Start_Timestamp": 0, "End_Timestamp": 100000})
+    bench.summarize_sq([str(pmc), str(trace)], layers=layers)
+    out = capsys.readouterr().out
+    # GUI 8e5 over 8 XCDs in 100 us: 1 GHz; busy 2.048e8 over 1e5 cycles x 1024 SIMDs: 2.0
+    assert "| gemm_in_proj:wide_gemm_kernel<0, false> | 1 | 100.0 |" in out
+    assert "| 1.00 | 2.000 | 0.833 |" in out
+    assert "gemm_in_proj: MOPS_BF16 x 512 = 1.024e+09" in out
