@@ -28,6 +28,9 @@ at M = 2..16 through the GEMV entry point (the multi-sequence decode
 workloads) and at M = 32..256 through the GEMM, without and with a
 workspace (w8a16_gemm_ws), each against its binding roof max(bytes / HBM
 peak, flop / MFMA peak).
+`read_floor` (outside the timed step) times a plain read of each projection's
+weight bytes (w8a16_hbm_read, several launch shapes, the same rotating copies
+and event timing as the GEMVs): the floor the GEMV pair is compared against.
 `layer_ends` (outside the timed step) times the norm prologues and the
 residual epilogue: fused into the decode GEMV against the unfused chain, and
 the prefill norms and residual GEMM at M = 1024. `decode_layer` times one
@@ -35,7 +38,7 @@ Mamba-2 layer's whole decode step for one token (fused in_proj, conv1d
 update, SSM decode, fused out_proj) and the conv / SSM kernels alone.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-few-tokens]
-                    [--no-layer-ends] [--no-large-layer]
+                    [--no-layer-ends] [--no-large-layer] [--no-read-floor]
 
 Profile helpers (read rocprofv3 CSV output; no GPU needed):
     python bench.py --summarize-trace <dir>/<name>_kernel_trace.csv
@@ -327,6 +330,53 @@ class Projection:
         return binding.gemm_raw(self.Ap.data_ptr(), self.W[i % self.copies].data_ptr(),
                                 self.S[i % self.copies].data_ptr(), self.outp.data_ptr(),
                                 self.p_pre.M, self.p_pre.N, self.p_pre.K, stream)
+
+
+# Launch shapes (threads, loads per lane) of the plain-read floor: the fastest
+# one-shot shapes for the two weight sizes on MI355X, and the GEMVs' own.
+READ_SHAPES = ((512, 2), (256, 8), (64, 8), (256, 2), (128, 8), (256, 4), (512, 4), (512, 8))
+
+
+def read_floor_report(projs, device, stream, L, check, gemv_us, reps=10):
+    """Outside the timed step: the plain read of each projection's weight
+    bytes (w8a16_hbm_read over the same rotating weight copies the GEMVs
+    read, L back-to-back launches between two events, like the GEMVs), at the
+    launch shapes in READ_SHAPES; the fastest is the floor the GEMV is
+    compared against."""
+    sh = stream.cuda_stream
+    sink = torch.zeros(1024, dtype=torch.int32, device=device)
+    out = {"unit": "us per launch (HIP events over L back-to-back launches, weight copies rotated)"}
+    best = []
+    for proj, g_us in zip(projs, gemv_us):
+        nbytes = proj.p_dec.N * proj.p_dec.K
+        rows = {}
+        for threads, loads in READ_SHAPES:
+            def launch(i):
+                check(binding.hbm_read_raw(proj.W[i % proj.copies].data_ptr(), nbytes, threads, loads,
+                                           sink.data_ptr(), sh), "hbm_read")
+            for i in range(L):
+                launch(i)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+            for r in range(reps):
+                ev[2 * r].record(stream)
+                for i in range(L):
+                    launch(r * L + i)
+                ev[2 * r + 1].record(stream)
+            torch.cuda.synchronize()
+            t = float(np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e-3 for r in range(reps)])) / L
+            rows[f"{threads}x{loads}"] = round(t * 1e6, 3)
+        shape, t_best = min(rows.items(), key=lambda kv: kv[1])
+        best.append(t_best)
+        out[proj.p_dec.name] = {"weight_bytes": nbytes, "us_by_shape (threads x loads per lane)": rows,
+                                "best_us": t_best, "best_shape": shape,
+                                "frac_of_hbm_peak": round(nbytes / (t_best * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "gemv_us": round(g_us, 3), "gemv_over_floor": round(g_us / t_best, 3)}
+    assert not bool(sink.any()), "the read helper wrote to its sink"
+    b = sum(p.p_dec.N * p.p_dec.K for p in projs)
+    out["pair"] = {"floor_us": round(sum(best), 3),
+                   "floor_frac_of_hbm_peak": round(b / (sum(best) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "gemv_us": round(sum(gemv_us), 3), "gemv_over_floor": round(sum(gemv_us) / sum(best), 3)}
+    return out
 
 
 FEW_TOKEN_GEMV_M = (2, 4, 8, 16)            # multi-sequence decode (w8a16_gemv)
@@ -790,6 +840,8 @@ def main():
                          "--summarize-trace / --summarize-counters label)")
     ap.add_argument("--no-layer-ends", action="store_true",
                     help="skip the norm prologue / residual epilogue and layer decode-step timings (profiler runs)")
+    ap.add_argument("--no-read-floor", action="store_true",
+                    help="skip the plain-read floor of the decode weights (profiler runs)")
     ap.add_argument("--no-large-layer", action="store_true",
                     help="skip the hidden-8192 layer's 8192-token GEMMs and M = 1 GEMVs (profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -872,6 +924,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    dur = np.array([[ev[j].elapsed_time(ev[j + 1]) * 1e-3 for j in range(4)] for ev in events])
+    dur[:, :2] /= L                                  # per GEMV launch
+    mean = dur.mean(axis=0)                          # seconds per launch: gemv in, gemv out, gemm in, gemm out
+    floor = None if args.no_read_floor else read_floor_report(projs, device, stream, L, check,
+                                                              [mean[0] * 1e6, mean[1] * 1e6])
     few = None if args.no_few_tokens else few_token_report(projs, device, stream, L, check)
     large = None if args.no_large_layer else large_layer_report(device, stream, check)
     ends = None if args.no_layer_ends else layer_ends_report(projs, device, stream, L, check)
@@ -884,9 +941,6 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
-    dur = np.array([[ev[j].elapsed_time(ev[j + 1]) * 1e-3 for j in range(4)] for ev in events])
-    dur[:, :2] /= L                                  # per GEMV launch
-    mean = dur.mean(axis=0)                          # seconds per launch: gemv in, gemv out, gemm in, gemm out
     b_in, b_out = projs[0].p_dec.bytes_moved(), projs[1].p_dec.bytes_moved()
     f_in, f_out = projs[0].p_pre.flops(), projs[1].p_pre.flops()
     gemv_gbs = (b_in + b_out) / (mean[0] + mean[1]) / 1e9
@@ -942,6 +996,7 @@ def main():
             "roofline": roof("mfma", gemm_tfs, BF16_PEAK_TFLOPS, "TFLOP/s", pair_traffic("gemm")),
         },
         "launches": launches,
+        "read_floor": floor,
         "large_layer": large,
         "few_tokens": few,
         "layer_ends": ends,

@@ -33,7 +33,7 @@ BLOCK = 128
 EXPORTS = ("w8a16_gemv", "w8a16_gemm", "w8a16_gemv_ex", "w8a16_gemm_ex", "w8a16_gemm_workspace_size",
            "w8a16_gemm_ws", "w8a16_rmsnorm", "w8a16_gemv_fused", "w8a16_gemm_residual", "w8a16_conv1d_update",
            "w8a16_gemv_in_proj", "w8a16_ssm_decode", "w8a16_dequant", "w8a16_strerror",
-           "w8a16_gemm_noalloc", "w8a16_gemm_noalloc_scratch_bytes")
+           "w8a16_gemm_noalloc", "w8a16_gemm_noalloc_scratch_bytes", "w8a16_hbm_read")
 
 # enum w8a16_scale_format
 SCALE_BLOCK_BF16, SCALE_BLOCK_F32, SCALE_ROW_F32 = 0, 1, 2
@@ -84,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.w8a16_gemm_noalloc.argtypes = [P, P, P, P, I64, I64, I64, P]
     lib.w8a16_gemm_noalloc_scratch_bytes.restype = I64
     lib.w8a16_gemm_noalloc_scratch_bytes.argtypes = []
+    lib.w8a16_hbm_read.restype = ctypes.c_int
+    lib.w8a16_hbm_read.argtypes = [P, I64, ctypes.c_int, ctypes.c_int, P, P]
     F = ctypes.c_float
     lib.w8a16_rmsnorm.restype = ctypes.c_int
     lib.w8a16_rmsnorm.argtypes = [P, P, P, F, P, I64, I64, P]
@@ -136,6 +138,11 @@ def gemm_noalloc_raw(A: int, Wq: int, scale: int, out: int, M: int, N: int, K: i
 def gemm_noalloc_scratch_bytes() -> int:
     """Bytes of the library's static scratch that w8a16_gemm_noalloc uses per GPU."""
     return load().w8a16_gemm_noalloc_scratch_bytes()
+
+
+def hbm_read_raw(buf: int, nbytes: int, threads: int, loads: int, sink: int, stream: int = 0) -> int:
+    """Plain read of nbytes at buf (the HBM floor the GEMV is compared against); writes nothing."""
+    return load().w8a16_hbm_read(buf, nbytes, threads, loads, sink, stream)
 
 
 def gemv_ex_raw(A: int, Wq: int, scale: int, scale_format: int, out: int, M: int, N: int, K: int,

@@ -190,6 +190,20 @@ int w8a16_gemm_noalloc(const void* A, const void* Wq, const void* scale, void* o
                        void* stream);
 
 /*
+ * Measurement helper, not a step of the projection: reads bytes of device
+ * memory at buf once (16-byte loads, non-temporal like the decode GEMV's
+ * weight loads), loads_per_lane loads per lane all issued before any is used,
+ * in workgroups of `threads` threads. Its time is the plain-read floor that
+ * the decode GEMV's weight stream (one read of N*K bytes) is compared against.
+ * Writes nothing: sink (4-byte aligned, at least `threads` words) is only
+ * named so that the loads are kept.
+ * bytes: a multiple of 16, at most 2^31 (else W8A16_ERR_SHAPE; 0 is a no-op);
+ * threads in {64, 128, 256, 512, 1024} and loads_per_lane in {1, 2, 4, 8, 16}
+ * (else W8A16_ERR_ARG); buf 16-byte aligned (W8A16_ERR_ALIGN).
+ */
+int w8a16_hbm_read(const void* buf, int64_t bytes, int threads, int loads_per_lane, void* sink, void* stream);
+
+/*
  * Norm prologues and the residual epilogue of the Mamba-2 layer around its
  * two projections (nemotron_mamba2.rs module docs, forward pass: step 1, RMS
  * norm scaled by its weight, before in_proj; step 6, the gated norm

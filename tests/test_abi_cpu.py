@@ -347,3 +347,15 @@ def test_gemm_noalloc_scratch_and_rejections_before_any_hip_call():
     assert call(A + 2, Wq, scale, out, 128, 4096, 8192, 0) == binding.ERR_ALIGN
     assert call(A, Wq, scale, A, 128, 4096, 8192, 0) == binding.ERR_ALIAS
     assert call(A, Wq, scale, out, 0, 4096, 8192, 0) == binding.OK          # no-op
+
+
+def test_hbm_read_rejections_before_any_hip_call():
+    call = binding.hbm_read_raw
+    assert call(FAKE, 100, 256, 8, FAKE + (1 << 30), 0) == binding.ERR_SHAPE          # not a multiple of 16
+    assert call(FAKE, (1 << 31) + 16, 256, 8, FAKE + (1 << 30), 0) == binding.ERR_SHAPE
+    assert call(FAKE, -16, 256, 8, FAKE + (1 << 30), 0) == binding.ERR_SHAPE
+    assert call(FAKE, 1 << 20, 96, 8, FAKE + (1 << 30), 0) == binding.ERR_ARG
+    assert call(FAKE, 1 << 20, 256, 3, FAKE + (1 << 30), 0) == binding.ERR_ARG
+    assert call(0, 1 << 20, 256, 8, FAKE + (1 << 30), 0) == binding.ERR_NULL
+    assert call(FAKE + 8, 1 << 20, 256, 8, FAKE + (1 << 30), 0) == binding.ERR_ALIGN
+    assert call(FAKE, 0, 256, 8, 0, 0) == binding.OK                                 # no-op
