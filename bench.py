@@ -31,6 +31,8 @@ peak, flop / MFMA peak).
 `read_floor` (outside the timed step) times a plain read of each projection's
 weight bytes (w8a16_hbm_read, several launch shapes, the same rotating copies
 and event timing as the GEMVs): the floor the GEMV pair is compared against.
+`vendor_bf16_gemm` (outside the timed step, context only) times torch.matmul
+(hipBLASLt) in bf16 on the same prefill shapes with the weights dequantized.
 `layer_ends` (outside the timed step) times the norm prologues and the
 residual epilogue: fused into the decode GEMV against the unfused chain, and
 the prefill norms and residual GEMM at M = 1024. `decode_layer` times one
@@ -38,7 +40,7 @@ Mamba-2 layer's whole decode step for one token (fused in_proj, conv1d
 update, SSM decode, fused out_proj) and the conv / SSM kernels alone.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-few-tokens]
-                    [--no-layer-ends] [--no-large-layer] [--no-read-floor]
+                    [--no-layer-ends] [--no-large-layer] [--no-read-floor] [--no-vendor]
 
 Profile helpers (read rocprofv3 CSV output; no GPU needed):
     python bench.py --summarize-trace <dir>/<name>_kernel_trace.csv
@@ -507,6 +509,41 @@ def large_layer_report(device, stream, check, reps=LARGE_REPS, L=LARGE_L):
     return out
 
 
+def vendor_gemm_report(device, stream, reps=5):
+    """Context, outside the timed step: the vendor library's plain bf16 x bf16
+    GEMM (torch.matmul, which calls hipBLASLt) on the prefill shapes, with the
+    same activations and the dequantized weights rounded to BF16 ([K, N]
+    contiguous). Not this library's path: it reads twice the weight bytes and
+    applies no scales in the kernel; it shows what the chip's own GEMM reaches
+    on these shapes at the clock they run at."""
+    out = {"unit": "us per launch (HIP events around each launch); frac of 2516.6 TFLOP/s",
+           "what": "torch.matmul(A bf16 [M,K], B bf16 [K,N]) with B = bf16(dequantized W)^T"}
+    for wl in ("prefill_1k", "prefill_8k_large"):
+        for p in inputs.WORKLOADS[wl]:
+            A, W, S = inputs.make(p)
+            dA = to_dev(A, torch.bfloat16, device)
+            del A
+            deq = binding.w8a16_dequant(to_dev(W, torch.uint8, device), to_dev(S, torch.bfloat16, device))
+            B = deq.to(torch.bfloat16).t().contiguous()
+            del deq
+            for _ in range(2):
+                C = torch.matmul(dA, B)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+            for r in range(reps):
+                ev[2 * r].record(stream)
+                C = torch.matmul(dA, B)
+                ev[2 * r + 1].record(stream)
+            torch.cuda.synchronize()
+            t = float(np.mean([ev[2 * r].elapsed_time(ev[2 * r + 1]) * 1e-3 for r in range(reps)]))
+            f = p.flops()
+            out[f"{wl}/{p.name}"] = {"M": p.M, "N": p.N, "K": p.K, "us": round(t * 1e6, 1),
+                                     "TFLOP/s": round(f / t / 1e12, 1),
+                                     "frac": round(f / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            del dA, B, C
+            torch.cuda.empty_cache()
+    return out
+
+
 def layer_ends_report(projs, device, stream, L, check, reps=10):
     """Outside the timed step: the layer's norm prologues and residual epilogue
     around the projections (forward steps 1, 6 and 8 of the Mamba-2 layer).
@@ -840,6 +877,8 @@ def main():
                          "--summarize-trace / --summarize-counters label)")
     ap.add_argument("--no-layer-ends", action="store_true",
                     help="skip the norm prologue / residual epilogue and layer decode-step timings (profiler runs)")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the vendor bf16 GEMM context leg (torch.matmul on the prefill shapes)")
     ap.add_argument("--no-read-floor", action="store_true",
                     help="skip the plain-read floor of the decode weights (profiler runs)")
     ap.add_argument("--no-large-layer", action="store_true",
@@ -931,6 +970,7 @@ def main():
                                                               [mean[0] * 1e6, mean[1] * 1e6])
     few = None if args.no_few_tokens else few_token_report(projs, device, stream, L, check)
     large = None if args.no_large_layer else large_layer_report(device, stream, check)
+    vendor = None if args.no_vendor else vendor_gemm_report(device, stream)
     ends = None if args.no_layer_ends else layer_ends_report(projs, device, stream, L, check)
     layer = None if args.no_layer_ends else decode_layer_report(projs, device, stream, L, check)
 
@@ -998,6 +1038,7 @@ def main():
         "launches": launches,
         "read_floor": floor,
         "large_layer": large,
+        "vendor_bf16_gemm": vendor,
         "few_tokens": few,
         "layer_ends": ends,
         "decode_layer": layer,

@@ -33,10 +33,11 @@
 //    k-block accumulate into `blk`, which is then added to the result as
 //    acc += scale * blk (TN = 128 keeps a wave's columns in one scale row).
 //
-// Schedule (persistent grid of G = 2 workgroups per CU): the 128 x 128 output
-// tiles rarely come in a multiple of G (the 1024-token in_proj has 1160 tiles
-// for 512 slots, the out_proj 256), so whole-tile waves would leave up to half
-// of the chip idle in the last wave. Instead:
+// Schedule. Without a workspace every tile is computed whole by one
+// workgroup. With one (w8a16_gemm_ws, or the static scratch of
+// w8a16_gemm_noalloc) the grid is persistent, G = 2 workgroups per CU: the
+// 128 x 128 output tiles rarely come in a multiple of G, so whole-tile waves
+// would leave up to half of the chip idle in the last wave. Instead:
 //  * shared part: the tiles past the last whole round of G are cut into
 //    units of one 128-wide k-block, and the units are dealt to the workgroups
 //    in equal contiguous ranges, so every workgroup gets the same work. A tile
