@@ -800,7 +800,7 @@ int run_gemm(const void* A, const void* Wq, const void* scale, const void* resid
 enum class Path { kSkinny, kTile32, kTile64, kWide, kWideSplitN, kBigSplit, kBigTile };
 
 Path choose_path(int64_t M, int64_t N, int64_t K, int64_t* n_wide = nullptr) {
-    if (skinny_fits(M, K)) return Path::kSkinny;
+    if (skinny_fits(M, K) || skinny_lds_fits(M, N, K, device_cu_count())) return Path::kSkinny;
     if (M <= Skinny32::TM) return Path::kTile32;
     if (M <= Skinny64::TM) return Path::kTile64;
     const int cus = device_cu_count();

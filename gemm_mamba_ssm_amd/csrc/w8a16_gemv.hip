@@ -524,12 +524,15 @@ extern "C" int w8a16_gemv_ex(const void* A, const void* Wq, const void* scale, i
     if (M > W8A16_GEMV_MAX_M || K > (M <= 8 ? W8A16_GEMV_MAX_K_SMALL_M : W8A16_GEMV_MAX_K))
         return W8A16_ERR_SHAPE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // From 4 rows on, the products cost this kernel more VALU time than the
-    // weight stream takes; the skinny GEMM (same single weight pass, products
-    // on the matrix cores) is faster where it applies (measured on the
-    // Mamba-2 in_proj shape: 21 against 23 us at M = 4, 22 against 49 us at
-    // M = 16).
-    if (M >= 4 && skinny_fits(M, K)) return skinny_gemm(A, Wq, scale, scale_format, nullptr, out, M, N, K, s);
+    // From 2 rows on, the skinny GEMM (the same single weight pass, products
+    // on the matrix cores) is faster where its one-shot form applies
+    // (measured on the Mamba-2 shapes: in_proj 17.3 against 18.8 us at M = 2;
+    // out_proj 8.6 against 10.0 us at M = 4, 9.2 against 14.4 at M = 8); from
+    // 4 rows on its ring form is too, where it applies (in_proj: 21 against
+    // 23 us at M = 4, 22 against 49 us at M = 16): the products cost the VALU
+    // GEMV more than the weight stream takes.
+    if ((M >= 2 && skinny_lds_fits(M, N, K, device_cu_count())) || (M >= 4 && skinny_fits(M, K)))
+        return skinny_gemm(A, Wq, scale, scale_format, nullptr, out, M, N, K, s);
     switch (scale_format) {
         case W8A16_SCALE_BLOCK_F32: return run_gemv<kScaleBlockF32, kFuseNone>(A, Wq, scale, out, M, N, K, s);
         case W8A16_SCALE_ROW_F32: return run_gemv<kScaleRowF32, kFuseNone>(A, Wq, scale, out, M, N, K, s);

@@ -78,6 +78,16 @@ inline bool skinny_fits(int64_t M, int64_t K) {
     return M >= 1 && M <= kSkinnyMaxM &&
            (K <= kSkinnyOnePassK || (K <= kSkinnyMaxK && M >= kSkinnyTwoPassMinM));
 }
+// One-shot skinny form (one 16-row weight block per workgroup, every weight
+// load issued up front, activations in LDS): whether it applies to (M, N, K)
+// on `cus` CUs, and its k-blocks per wave.
+bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb);
+inline bool skinny_lds_fits(int64_t M, int64_t N, int64_t K, int cus) {
+    int kb = 0;
+    return skinny_lds_plan(M, N, K, cus, &kb);
+}
+int skinny_lds_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
+                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
 // `residual` ([M][N] BF16, or nullptr) adds the residual epilogue.
 int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
@@ -106,6 +116,20 @@ inline int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s
                   KArgs... args) {
     void* argv[] = {static_cast<void*>(&args)...};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
+    return e == hipSuccess ? W8A16_OK : W8A16_ERR_LAUNCH;
+}
+
+// The same with `lds_bytes` of dynamic LDS (the kernel's limit is raised
+// first when that exceeds 64 KB).
+template <typename... KArgs>
+inline int launch_with_lds(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream,
+                           KArgs... args) {
+    if (lds_bytes > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds_bytes)) != hipSuccess)
+        return W8A16_ERR_LAUNCH;
+    void* argv[] = {static_cast<void*>(&args)...};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds_bytes, stream);
     return e == hipSuccess ? W8A16_OK : W8A16_ERR_LAUNCH;
 }
 
