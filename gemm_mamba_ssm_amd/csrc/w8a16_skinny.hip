@@ -296,7 +296,7 @@ __device__ __forceinline__ void lds_sync() {
 // touches at one k land in 16 different 16-byte slots of a 256-byte line.
 __device__ __forceinline__ int a_chunk_swz(int q, int m) { return (q & ~15) | ((q ^ m) & 15); }
 
-template <int KB, int NB, int SF>
+template <int KB, int NB, int SF, bool AREG>
 __global__ void __launch_bounds__(64 * kLdsWaves, 1)
 skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,
                   const uint16_t* __restrict__ res, uint16_t* __restrict__ out, int M, int N, int K, int nblk) {
@@ -325,7 +325,7 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     const int nch = M * cpr;
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, M * K * 2, kBufferFlags);
-    for (int i = wave; i * 64 < nch; i += kLdsWaves) {
+    for (int i = wave; !AREG && i * 64 < nch; i += kLdsWaves) {
         const int p = i * 64 + lane;
         const int m = p / cpr, pc = p - m * cpr;
         const int k = a_chunk_swz(pc, m) * 8;           // the swizzle is its own inverse
@@ -363,6 +363,22 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
         }
     }
 
+    // AREG: the wave's own activations straight into registers instead (all
+    // M rows of its k-range, as MFMA A operands; rows past M are not loaded).
+    u32x4_t a_reg[AREG ? KB : 1][2][2];
+    if constexpr (AREG) {
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = (wave * KB + j) * kScaleBlock + 64 * c + 16 * g + 8 * h;
+                    a_reg[j][c][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                     ra, (r < M && k < K) ? static_cast<uint32_t>((r * K + k) * 2) : kOutOfRange, 0, 0));
+                }
+    }
+
     // 3. Every weight load of the workgroup: slot i, k-block j, chunk c (16
     //    codes of row r from k = (wave*KB + j)*128 + 64c + 16g). Slots past
     //    the last block, rows past N and k past K read zeros.
@@ -387,8 +403,10 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
 
     // 4. The activations (and scales) are the oldest loads: wait for them
     //    only, then make the DMA's LDS writes visible to the workgroup.
-    __builtin_amdgcn_s_waitcnt((kLoads & 15) | (0x7 << 4) | (0xF << 8) | ((kLoads >> 4) << 14));
-    lds_sync();
+    if constexpr (!AREG) {
+        __builtin_amdgcn_s_waitcnt((kLoads & 15) | (0x7 << 4) | (0xF << 8) | ((kLoads >> 4) << 14));
+        lds_sync();
+    }
 
     // MFMA A operand of (k-block j, chunk c, half h): row min(r, M - 1) (rows
     // past M feed output rows that are never stored), k = (wave*KB + j)*128 +
@@ -410,7 +428,11 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int q = ((wave * KB + j) * kScaleBlock + 64 * c + 16 * g + 8 * h) / 8;
-                    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(a_row + a_chunk_swz(q, am) * 16);
+                    u32x4_t av;
+                    if constexpr (AREG)
+                        av = a_reg[j][c][h];
+                    else
+                        av = *reinterpret_cast<const u32x4_t*>(a_row + a_chunk_swz(q, am) * 16);
                     blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), h ? bw1 : bw0, blk,
                                                                   0, 0, 0);
                 }
@@ -451,11 +473,14 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
 }
 
 template <int KB, int SF>
-int launch_lds(dim3 grid, hipStream_t s, const uint16_t* a, const uint8_t* w, const void* scale, const uint16_t* r,
-               uint16_t* o, int m, int n, int k, int nblk) {
+int launch_lds(bool areg, dim3 grid, hipStream_t s, const uint16_t* a, const uint8_t* w, const void* scale,
+               const uint16_t* r, uint16_t* o, int m, int n, int k, int nblk) {
+    if (areg)
+        return launch_with_lds(&skinny_lds_kernel<KB, 1, SF, true>, grid, dim3(64 * kLdsWaves), 0, s, a, w, scale, r, o,
+                               m, n, k, nblk);
     const size_t lds = static_cast<size_t>((m * KB * kLdsWaves * kScaleBlock * 2 + 1023) / 1024 * 1024);
-    return launch_with_lds(&skinny_lds_kernel<KB, 1, SF>, grid, dim3(64 * kLdsWaves), lds, s, a, w, scale, r, o, m, n,
-                           k, nblk);
+    return launch_with_lds(&skinny_lds_kernel<KB, 1, SF, false>, grid, dim3(64 * kLdsWaves), lds, s, a, w, scale, r,
+                           o, m, n, k, nblk);
 }
 
 }  // namespace
@@ -513,18 +538,22 @@ int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const
 // LDS budget, or (with more weight blocks than CUs) above 32 KB, where fewer
 // than three workgroups fit a CU and the ring form is faster (measured on the
 // Mamba-2 in_proj: 23 against 20 us at M = 8).
-bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb) {
+bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, bool* areg) {
     if (M < 1 || M > kSkinnyMaxM || N < 1 || K < 16 || cus < 1) return false;
     const int64_t k_blocks = ceil_div(K, kScaleBlockHost);
     int per_wave = 1;
     while (per_wave * kLdsWaves < k_blocks) per_wave *= 2;
     if (per_wave > 8) return false;
-    const int64_t a_bytes = M * per_wave * kLdsWaves * kScaleBlockHost * 2;
-    if (a_bytes > kLdsABytes) return false;
     if (static_cast<int64_t>(kRows) * K >= static_cast<int64_t>(kOutOfRange)) return false;
     const int64_t nblk = ceil_div(N, kRows);
     if (nblk > INT32_MAX) return false;
-    if (nblk > cus && a_bytes > 32 * 1024) return false;
+    const int64_t a_bytes = M * per_wave * kLdsWaves * kScaleBlockHost * 2;
+    // Activations in registers where they do not fit the LDS and every
+    // weight block has a CU of its own (each workgroup then re-reads only
+    // its waves' k-ranges of A from L2; the Mamba-2 out_proj at 9..16 rows).
+    *areg = a_bytes > kLdsABytes;
+    if (*areg && nblk > cus) return false;
+    if (!*areg && nblk > cus && a_bytes > 32 * 1024) return false;
     *kb = per_wave;
     return true;
 }
@@ -532,7 +561,8 @@ bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb) {
 int skinny_lds_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
                     int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     int kb = 0;
-    if (!skinny_lds_plan(M, N, K, device_cu_count(), &kb)) return W8A16_ERR_SHAPE;
+    bool areg = false;
+    if (!skinny_lds_plan(M, N, K, device_cu_count(), &kb, &areg)) return W8A16_ERR_SHAPE;
     if (scale_bytes(fmt, N, K) >= static_cast<int64_t>(kOutOfRange)) return W8A16_ERR_SHAPE;
     const int nblk = static_cast<int>(ceil_div(N, kRows));
     const dim3 grid(static_cast<unsigned>(nblk));
@@ -544,10 +574,10 @@ int skinny_lds_gemm(const void* A, const void* Wq, const void* scale, int fmt, c
     auto by_kb = [&](auto sf) {
         constexpr int SF = decltype(sf)::value;
         switch (kb) {
-            case 1: return launch_lds<1, SF>(grid, stream, a, w, scale, r, o, m, n, k, nblk);
-            case 2: return launch_lds<2, SF>(grid, stream, a, w, scale, r, o, m, n, k, nblk);
-            case 4: return launch_lds<4, SF>(grid, stream, a, w, scale, r, o, m, n, k, nblk);
-            default: return launch_lds<8, SF>(grid, stream, a, w, scale, r, o, m, n, k, nblk);
+            case 1: return launch_lds<1, SF>(areg, grid, stream, a, w, scale, r, o, m, n, k, nblk);
+            case 2: return launch_lds<2, SF>(areg, grid, stream, a, w, scale, r, o, m, n, k, nblk);
+            case 4: return launch_lds<4, SF>(areg, grid, stream, a, w, scale, r, o, m, n, k, nblk);
+            default: return launch_lds<8, SF>(areg, grid, stream, a, w, scale, r, o, m, n, k, nblk);
         }
     };
     switch (fmt) {

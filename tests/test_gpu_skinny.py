@@ -12,7 +12,10 @@ shapes below are chosen for that (on a 256-CU MI355X):
   * M = 8, N = 4096, K = 8192: 128 KB of activations (the Mamba-2 out_proj);
   * M = 5, N = 1000, K = 1040: 2 k-blocks per wave, a ragged k-block;
   * M = 4, N = 18560, K = 4096: the Mamba-2 in_proj, 1160 blocks;
-  * M = 1 through the GEMM entry; M = 16 with a short K.
+  * M = 1 through the GEMM entry; M = 16 with a short K;
+  * activations in registers instead of LDS (more than 128 KB of them, every
+    weight block on a CU of its own): M = 16, N = 4096, K = 8192 (the Mamba-2
+    out_proj), M = 9 with a ragged N, M = 16 with a k-tail of 16.
 """
 import numpy as np
 import pytest
@@ -25,7 +28,7 @@ pytestmark = pytest.mark.gpu
 
 RTOL, ATOL = 4e-3, 1e-6
 SHAPES = [(2, 4100, 4096), (3, 129, 4112), (8, 4096, 8192), (5, 1000, 1040), (4, 18560, 4096), (1, 4096, 8192),
-          (16, 300, 2048)]
+          (16, 300, 2048), (16, 4096, 8192), (9, 300, 8192), (16, 129, 4112)]
 
 
 def say(*a):
@@ -86,7 +89,7 @@ def test_one_shot_matches_between_entries(dev):
     assert np.array_equal(run("gemv", A, W, S, dev), run("gemm", A, W, S, dev))
 
 
-@pytest.mark.parametrize("M,N,K", [(2, 4100, 4096), (6, 4096, 8192)])
+@pytest.mark.parametrize("M,N,K", [(2, 4100, 4096), (6, 4096, 8192), (12, 4096, 8192)])
 def test_one_shot_residual_epilogue_bits(dev, M, N, K):
     say(f"one-shot skinny + residual M={M} N={N} K={K}")
     A = inputs.activations(M, K, 4500 + M)
@@ -100,7 +103,7 @@ def test_one_shot_residual_epilogue_bits(dev, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["block_f32", "row_f32"])
-@pytest.mark.parametrize("M,N,K", [(3, 129, 4112), (6, 4096, 8192)])
+@pytest.mark.parametrize("M,N,K", [(3, 129, 4112), (6, 4096, 8192), (14, 300, 8192)])
 def test_one_shot_scale_formats(dev, fmt, M, N, K):
     say(f"one-shot skinny {fmt} M={M} N={N} K={K}")
     A = inputs.activations(M, K, 4800 + M)
