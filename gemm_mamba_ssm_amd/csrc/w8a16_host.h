@@ -79,14 +79,12 @@ inline bool skinny_fits(int64_t M, int64_t K) {
            (K <= kSkinnyOnePassK || (K <= kSkinnyMaxK && M >= kSkinnyTwoPassMinM));
 }
 // One-shot skinny form (one 16-row weight block per workgroup, every weight
-// load issued up front, activations in LDS or registers): whether it applies
-// to (M, N, K) on `cus` CUs, its k-blocks per wave and where the activations
-// go.
-bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, bool* areg);
+// load issued up front, activations in LDS): whether it applies to (M, N, K)
+// on `cus` CUs, its k-blocks per wave and its activation phases (1 or 2).
+bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, int* phases);
 inline bool skinny_lds_fits(int64_t M, int64_t N, int64_t K, int cus) {
-    int kb = 0;
-    bool areg = false;
-    return skinny_lds_plan(M, N, K, cus, &kb, &areg);
+    int kb = 0, phases = 1;
+    return skinny_lds_plan(M, N, K, cus, &kb, &phases);
 }
 int skinny_lds_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
                     int64_t M, int64_t N, int64_t K, hipStream_t stream);

@@ -273,13 +273,15 @@ skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, con
 // (one 16-row weight block each), which a plain read of W measures as the
 // fastest way to stream it. The registers the ring form spends on
 // activations go to the weights here: the activations (all M rows, all of K,
-// at most 128 KB) are copied to LDS by DMA at the start of every workgroup
-// and each wave reads its MFMA A operands from LDS. 8 waves per workgroup;
-// wave w owns k-blocks [w*KB, (w+1)*KB) of the block; the 8 partial 16 x 16
-// tiles are added in LDS in wave order (ascending k), so the result is
-// deterministic. (Several blocks per workgroup, strided or contiguous, one
-// workgroup per CU, measured slower on the Mamba-2 in_proj: 20-23 against
-// 17-18 us at M = 1..4.)
+// at most 128 KB; above that, half of K at a time in two phases) are copied
+// to LDS by DMA at the start of every workgroup and each wave reads its MFMA
+// A operands from LDS. 8 waves per workgroup; in each phase wave w owns the
+// phase's k-blocks [w*KB/PH, (w+1)*KB/PH); the 8 partial 16 x 16 tiles are
+// added in LDS in wave order, so the result is deterministic. (Measured and
+// not kept, on the Mamba-2 shapes: several blocks per workgroup, strided or
+// contiguous, one workgroup per CU: 20-23 against 17-18 us for in_proj at
+// M = 1..4; the activations in registers instead of LDS: 10.6-33 against
+// 9.0-26 us.)
 constexpr int kLdsWaves = 8;
 constexpr int kLdsABytes = 128 * 1024;          // activation region: M * Kpad * 2 bytes at most
 
@@ -296,143 +298,123 @@ __device__ __forceinline__ void lds_sync() {
 // touches at one k land in 16 different 16-byte slots of a 256-byte line.
 __device__ __forceinline__ int a_chunk_swz(int q, int m) { return (q & ~15) | ((q ^ m) & 15); }
 
-template <int KB, int NB, int SF, bool AREG>
+template <int KB, int PH, int SF>
 __global__ void __launch_bounds__(64 * kLdsWaves, 1)
 skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,
-                  const uint16_t* __restrict__ res, uint16_t* __restrict__ out, int M, int N, int K, int nblk) {
+                  const uint16_t* __restrict__ res, uint16_t* __restrict__ out, int M, int N, int K) {
     constexpr bool kRowScale = SF == kScaleRowF32;
-    constexpr int kLoads = NB * KB * 2;                 // weight loads per lane
+    constexpr int KBP = KB / PH;                        // k-blocks per wave and phase
+    static_assert(PH == 1 || (PH == 2 && KB % 2 == 0), "one or two phases");
+    constexpr int kLoads = KB * 2;                      // weight loads per lane
     static_assert(kLoads < 64, "vmcnt field");
-    extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];   // M * kpad * 2 bytes, rounded to 1 KB
-    __shared__ f32x4_t red[2][kLdsWaves * 64];
-    __shared__ uint16_t outs[NB * 256];
-    __shared__ float row_s[kRowScale ? NB * kRows : 1];
+    extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];   // M * kph * 2 bytes, rounded to 1 KB
+    __shared__ f32x4_t red[kLdsWaves * 64];
+    __shared__ uint16_t outs[256];
+    __shared__ float row_s[kRowScale ? kRows : 1];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int lane = threadIdx.x % 64;
     const int r = lane % 16, g = lane / 16;
     const int k_blocks = (K + kScaleBlock - 1) / kScaleBlock;
-    const int kpad = kLdsWaves * KB * kScaleBlock;      // K padded to the waves' k-blocks
-    // Slot i of workgroup x takes 16-row block x + i * G: at any time the
-    // workgroups stream neighbouring blocks, a contiguous window of W.
-    const int G = gridDim.x;
-    auto block_of = [&](int i) { return static_cast<int>(blockIdx.x) + i * G; };
+    const int kph = kLdsWaves * KBP * kScaleBlock;      // K of one phase (K padded to the waves' k-blocks / PH)
+    const int b = blockIdx.x;                           // this workgroup's 16-row weight block
+    const int n0 = b * kRows;
+    // Global k-block of the wave's j-th k-block (phase j / KBP).
+    auto kblock = [&](int j) { return (j / KBP) * (kLdsWaves * KBP) + wave * KBP + j % KBP; };
 
-    // 1. Activations to LDS by DMA: LDS chunk p (16 bytes) holds row
-    //    p / cpr, logical chunk q with a_chunk_swz(q, m) == p % cpr; chunks
-    //    past K (and past M rows) read as zero.
-    const int cpr = kpad / 8;                           // 16-byte chunks per row
-    const int nch = M * cpr;
+    // Activations of phase p to LDS by DMA: LDS chunk e (16 bytes) holds row
+    // e / cph, logical chunk q (k = p * kph + 8q) with a_chunk_swz(q, m) ==
+    // e % cph; chunks past K read as zero.
+    const int cph = kph / 8;                            // 16-byte chunks per row and phase
+    const int nch = M * cph;
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0, M * K * 2, kBufferFlags);
-    for (int i = wave; !AREG && i * 64 < nch; i += kLdsWaves) {
-        const int p = i * 64 + lane;
-        const int m = p / cpr, pc = p - m * cpr;
-        const int k = a_chunk_swz(pc, m) * 8;           // the swizzle is its own inverse
-        const uint32_t off = (p < nch && k < K) ? static_cast<uint32_t>((m * K + k) * 2) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(a_lds + i * 1024), 16, off, 0, 0, 0);
-    }
+    auto stage_a = [&](int p) {
+        for (int i = wave; i * 64 < nch; i += kLdsWaves) {
+            const int e = i * 64 + lane;
+            const int m = e / cph, pc = e - m * cph;
+            const int k = p * kph + a_chunk_swz(pc, m) * 8;   // the swizzle is its own inverse
+            const uint32_t off = (e < nch && k < K) ? static_cast<uint32_t>((m * K + k) * 2) : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(a_lds + i * 1024), 16, off, 0, 0, 0);
+        }
+    };
+    stage_a(0);
 
-    // 2. Scales: for slot i, lane l holds the scale of k-block wave*KB + l % KB
-    //    in the block's scale row (block formats); the row format's scales go
-    //    to LDS.
+    // Scales: lane l holds the block's scale for the wave's k-block l % KB
+    // (block formats); the row format's 16 row scales go to LDS.
     constexpr int kScaleBytes = SF == kScaleBlockBf16 ? 2 : 4;
     const int scale_elems = kRowScale ? N : ((N + kScaleBlock - 1) / kScaleBlock) * k_blocks;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(S), 0, scale_elems * kScaleBytes, kBufferFlags);
-    float s_lane[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) s_lane[i] = 1.0f;
+    float s_lane = 1.0f;
     if constexpr (SF == kScaleBlockBf16 || SF == kScaleBlockF32) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int b = block_of(i);
-            const int srow = b * kRows / kScaleBlock, kb = wave * KB + lane % KB;
-            const bool ok = b < nblk && kb < k_blocks;
-            const uint32_t off = ok ? static_cast<uint32_t>(srow * k_blocks + kb) * kScaleBytes : kOutOfRange;
-            if constexpr (SF == kScaleBlockBf16)
-                s_lane[i] = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
-            else
-                s_lane[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
-        }
+        const int kb = kblock(lane % KB);
+        const uint32_t off =
+            kb < k_blocks ? static_cast<uint32_t>((n0 / kScaleBlock) * k_blocks + kb) * kScaleBytes : kOutOfRange;
+        if constexpr (SF == kScaleBlockBf16)
+            s_lane = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+        else
+            s_lane = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
     } else {
-        for (int e = threadIdx.x; e < NB * kRows; e += blockDim.x) {
-            const int n = block_of(e / kRows) * kRows + e % kRows;
-            row_s[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        if (threadIdx.x < kRows) {
+            const int n = n0 + threadIdx.x;
+            row_s[threadIdx.x] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                 rs, n < N ? static_cast<uint32_t>(n) * 4 : kOutOfRange, 0, 0));
         }
     }
 
-    // AREG: the wave's own activations straight into registers instead (all
-    // M rows of its k-range, as MFMA A operands; rows past M are not loaded).
-    u32x4_t a_reg[AREG ? KB : 1][2][2];
-    if constexpr (AREG) {
+    // Every weight load of the workgroup, phase by phase: k-block j, chunk c
+    // (16 codes of row r from k = kblock(j)*128 + 64c + 16g). Rows past N and
+    // k past K read zeros.
+    u32x4_t w[KB][2];
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, min(kRows, N - n0) * K, kBufferFlags);
 #pragma unroll
-        for (int j = 0; j < KB; ++j)
+    for (int j = 0; j < KB; ++j)
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int k = (wave * KB + j) * kScaleBlock + 64 * c + 16 * g + 8 * h;
-                    a_reg[j][c][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                     ra, (r < M && k < K) ? static_cast<uint32_t>((r * K + k) * 2) : kOutOfRange, 0, 0));
-                }
-    }
-
-    // 3. Every weight load of the workgroup: slot i, k-block j, chunk c (16
-    //    codes of row r from k = (wave*KB + j)*128 + 64c + 16g). Slots past
-    //    the last block, rows past N and k past K read zeros.
-    u32x4_t w[NB][KB][2];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int b = block_of(i);
-        const bool live = b < nblk;
-        const int n0 = (live ? b : 0) * kRows;
-        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, live ? min(kRows, N - n0) * K : 0, kBufferFlags);
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int k = (wave * KB + j) * kScaleBlock + 64 * c + 16 * g;
-                w[i][j][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                             rw, k < K ? static_cast<uint32_t>(r * K + k) : kOutOfRange, 0, 0));
-            }
-    }
+        for (int c = 0; c < 2; ++c) {
+            const int k = kblock(j) * kScaleBlock + 64 * c + 16 * g;
+            w[j][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rw, k < K ? static_cast<uint32_t>(r * K + k) : kOutOfRange, 0, 0));
+        }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 4. The activations (and scales) are the oldest loads: wait for them
-    //    only, then make the DMA's LDS writes visible to the workgroup.
-    if constexpr (!AREG) {
-        __builtin_amdgcn_s_waitcnt((kLoads & 15) | (0x7 << 4) | (0xF << 8) | ((kLoads >> 4) << 14));
-        lds_sync();
-    }
-
     // MFMA A operand of (k-block j, chunk c, half h): row min(r, M - 1) (rows
-    // past M feed output rows that are never stored), k = (wave*KB + j)*128 +
-    // 64c + 16g + 8h, the same k-slot order as the weights.
+    // past M feed output rows that are never stored), k = kblock(j)*128 + 64c
+    // + 16g + 8h, the same k-slot order as the weights.
     const int am = min(r, M - 1);
-    const uint8_t* a_row = a_lds + am * (cpr * 16);
+    const uint8_t* a_row = a_lds + am * (cph * 16);
     const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    int parity = 0;
+    f32x4_t acc = zero;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        f32x4_t acc = zero;
+    for (int p = 0; p < PH; ++p) {
+        if (p == 0) {
+            // The activations (and scales) are older than every weight load:
+            // wait for them (and this wave's LDS writes) only, then make the
+            // DMA's LDS writes visible. (__syncthreads would also wait for
+            // every weight load in flight.)
+            __builtin_amdgcn_s_waitcnt((kLoads & 15) | (0x7 << 4) | ((kLoads >> 4) << 14));
+        } else {
+            // Every wave is done reading phase p - 1's activations; stage
+            // phase p's (the youngest loads: waiting for them waits for all).
+            __builtin_amdgcn_s_waitcnt(15 | (0x7 << 4) | (0x3 << 14));   // LDS reads only
+            lds_sync();
+            stage_a(p);
+            __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+        }
+        lds_sync();
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane[i]), j));
+        for (int jj = 0; jj < KBP; ++jj) {
+            const int j = p * KBP + jj;
+            const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), j));
             f32x4_t blk = zero;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const bf16x8_t bw0 = e4m3x8(w[i][j][c][0], w[i][j][c][1]), bw1 = e4m3x8(w[i][j][c][2], w[i][j][c][3]);
+                const bf16x8_t bw0 = e4m3x8(w[j][c][0], w[j][c][1]), bw1 = e4m3x8(w[j][c][2], w[j][c][3]);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int q = ((wave * KB + j) * kScaleBlock + 64 * c + 16 * g + 8 * h) / 8;
-                    u32x4_t av;
-                    if constexpr (AREG)
-                        av = a_reg[j][c][h];
-                    else
-                        av = *reinterpret_cast<const u32x4_t*>(a_row + a_chunk_swz(q, am) * 16);
+                    const int q = ((wave * KBP + jj) * kScaleBlock + 64 * c + 16 * g + 8 * h) / 8;
+                    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(a_row + a_chunk_swz(q, am) * 16);
                     blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), h ? bw1 : bw0, blk,
                                                                   0, 0, 0);
                 }
@@ -440,47 +422,43 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], s, acc[v]);
         }
-        // Lane l holds output column l % 16, rows 4(l/16) + v; thread t < 256
-        // adds output (row t / 16, column t % 16) over the waves in k order.
-        red[parity][wave * 64 + lane] = acc;
-        lds_sync();
-        if (threadIdx.x < 256) {
-            const int t = threadIdx.x, row = t / 16, col = t % 16;
-            const int l = col + 16 * (row / 4), v = row % 4;
-            float sum = red[parity][l][v];
-#pragma unroll
-            for (int w2 = 1; w2 < kLdsWaves; ++w2) sum += red[parity][w2 * 64 + l][v];
-            if constexpr (kRowScale) sum *= row_s[i * kRows + col];
-            outs[i * 256 + t] = f32_to_bf16_bits(sum);
-        }
-        // red[parity] is written again two blocks later, after the next
-        // barrier, which every thread reaches only once done reading it.
-        parity ^= 1;
     }
-    lds_sync();
-    // Outputs: slot i's (row, column) at outs[i * 256 + row * 16 + column];
-    // threads take 16-column runs of one row of one slot.
-    for (int e = threadIdx.x; e < NB * M * 16; e += blockDim.x) {
-        const int i = e / (M * 16), rest = e - i * (M * 16);
-        const int row = rest / 16, col = rest % 16;
-        const int b = block_of(i), n = b * kRows + col;
-        if (b < nblk && n < N) {
+    // Lane l holds output column l % 16, rows 4(l/16) + v; thread t < 256
+    // adds output (row t / 16, column t % 16) over the waves in order of
+    // their k-blocks (phase-major, so the order is fixed).
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int t = threadIdx.x, row = t / 16, col = t % 16;
+        const int l = col + 16 * (row / 4), v = row % 4;
+        float sum = red[l][v];
+#pragma unroll
+        for (int w2 = 1; w2 < kLdsWaves; ++w2) sum += red[w2 * 64 + l][v];
+        if constexpr (kRowScale) sum *= row_s[col];
+        outs[t] = f32_to_bf16_bits(sum);
+    }
+    __syncthreads();
+    // Outputs: (row, column) at outs[row * 16 + column].
+    for (int e = threadIdx.x; e < M * 16; e += blockDim.x) {
+        const int row = e / 16, col = e % 16, n = n0 + col;
+        if (n < N) {
             const int64_t o = static_cast<int64_t>(row) * N + n;
-            const uint16_t y = outs[i * 256 + row * 16 + col];
+            const uint16_t y = outs[row * 16 + col];
             out[o] = res ? residual_add_bits(y, res[o]) : y;
         }
     }
 }
 
 template <int KB, int SF>
-int launch_lds(bool areg, dim3 grid, hipStream_t s, const uint16_t* a, const uint8_t* w, const void* scale,
-               const uint16_t* r, uint16_t* o, int m, int n, int k, int nblk) {
-    if (areg)
-        return launch_with_lds(&skinny_lds_kernel<KB, 1, SF, true>, grid, dim3(64 * kLdsWaves), 0, s, a, w, scale, r, o,
-                               m, n, k, nblk);
-    const size_t lds = static_cast<size_t>((m * KB * kLdsWaves * kScaleBlock * 2 + 1023) / 1024 * 1024);
-    return launch_with_lds(&skinny_lds_kernel<KB, 1, SF, false>, grid, dim3(64 * kLdsWaves), lds, s, a, w, scale, r,
-                           o, m, n, k, nblk);
+int launch_lds(int phases, dim3 grid, hipStream_t s, const uint16_t* a, const uint8_t* w, const void* scale,
+               const uint16_t* r, uint16_t* o, int m, int n, int k) {
+    const size_t lds = static_cast<size_t>((m * KB / phases * kLdsWaves * kScaleBlock * 2 + 1023) / 1024 * 1024);
+    if constexpr (KB % 2 == 0)
+        if (phases == 2)
+            return launch_with_lds(&skinny_lds_kernel<KB, 2, SF>, grid, dim3(64 * kLdsWaves), lds, s, a, w, scale, r,
+                                   o, m, n, k);
+    return launch_with_lds(&skinny_lds_kernel<KB, 1, SF>, grid, dim3(64 * kLdsWaves), lds, s, a, w, scale, r, o, m, n,
+                           k);
 }
 
 }  // namespace
@@ -538,7 +516,7 @@ int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const
 // LDS budget, or (with more weight blocks than CUs) above 32 KB, where fewer
 // than three workgroups fit a CU and the ring form is faster (measured on the
 // Mamba-2 in_proj: 23 against 20 us at M = 8).
-bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, bool* areg) {
+bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, int* phases) {
     if (M < 1 || M > kSkinnyMaxM || N < 1 || K < 16 || cus < 1) return false;
     const int64_t k_blocks = ceil_div(K, kScaleBlockHost);
     int per_wave = 1;
@@ -548,24 +526,23 @@ bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, bool* ar
     const int64_t nblk = ceil_div(N, kRows);
     if (nblk > INT32_MAX) return false;
     const int64_t a_bytes = M * per_wave * kLdsWaves * kScaleBlockHost * 2;
-    // Activations in registers where they do not fit the LDS and every
-    // weight block has a CU of its own (each workgroup then re-reads only
-    // its waves' k-ranges of A from L2; the Mamba-2 out_proj at 9..16 rows).
-    *areg = a_bytes > kLdsABytes;
-    if (*areg && nblk > cus) return false;
-    if (!*areg && nblk > cus && a_bytes > 32 * 1024) return false;
+    // Activations over the LDS budget go in two phases of half of K each
+    // where every weight block has a CU of its own (one workgroup per CU
+    // anyway: the Mamba-2 out_proj at 9..16 rows); the second phase's copy
+    // waits for the first phase's products.
+    *phases = a_bytes > kLdsABytes ? 2 : 1;
+    if (*phases == 2 && (nblk > cus || per_wave < 2 || a_bytes > 2 * kLdsABytes)) return false;
+    if (*phases == 1 && nblk > cus && a_bytes > 32 * 1024) return false;
     *kb = per_wave;
     return true;
 }
 
 int skinny_lds_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
                     int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    int kb = 0;
-    bool areg = false;
-    if (!skinny_lds_plan(M, N, K, device_cu_count(), &kb, &areg)) return W8A16_ERR_SHAPE;
+    int kb = 0, phases = 1;
+    if (!skinny_lds_plan(M, N, K, device_cu_count(), &kb, &phases)) return W8A16_ERR_SHAPE;
     if (scale_bytes(fmt, N, K) >= static_cast<int64_t>(kOutOfRange)) return W8A16_ERR_SHAPE;
-    const int nblk = static_cast<int>(ceil_div(N, kRows));
-    const dim3 grid(static_cast<unsigned>(nblk));
+    const dim3 grid(static_cast<unsigned>(ceil_div(N, kRows)));
     auto a = static_cast<const uint16_t*>(A);
     auto w = static_cast<const uint8_t*>(Wq);
     auto o = static_cast<uint16_t*>(out);
@@ -574,10 +551,10 @@ int skinny_lds_gemm(const void* A, const void* Wq, const void* scale, int fmt, c
     auto by_kb = [&](auto sf) {
         constexpr int SF = decltype(sf)::value;
         switch (kb) {
-            case 1: return launch_lds<1, SF>(areg, grid, stream, a, w, scale, r, o, m, n, k, nblk);
-            case 2: return launch_lds<2, SF>(areg, grid, stream, a, w, scale, r, o, m, n, k, nblk);
-            case 4: return launch_lds<4, SF>(areg, grid, stream, a, w, scale, r, o, m, n, k, nblk);
-            default: return launch_lds<8, SF>(areg, grid, stream, a, w, scale, r, o, m, n, k, nblk);
+            case 1: return launch_lds<1, SF>(phases, grid, stream, a, w, scale, r, o, m, n, k);
+            case 2: return launch_lds<2, SF>(phases, grid, stream, a, w, scale, r, o, m, n, k);
+            case 4: return launch_lds<4, SF>(phases, grid, stream, a, w, scale, r, o, m, n, k);
+            default: return launch_lds<8, SF>(phases, grid, stream, a, w, scale, r, o, m, n, k);
         }
     };
     switch (fmt) {
