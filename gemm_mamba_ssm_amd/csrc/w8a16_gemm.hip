@@ -8,9 +8,13 @@
 // The pages measure (nemotron_mamba2.rs, `set_bf16_weights` docs) that a
 // prefill GEMM which rewrites a dequantized weight tile in shared memory for
 // every M-block pays N*K*M/M_TILE of that work. Here the raw E4M3 bytes are
-// staged once per workgroup tile and never rewritten: each wave decodes the
-// 16-byte rows it feeds to the matrix cores in registers, with the exact
-// packed E4M3->BF16 convert, right before the MFMA that uses them.
+// staged once per workgroup tile and LDS is never rewritten, but the decode
+// itself is still repeated: each wave decodes the 16-byte rows it feeds to
+// the matrix cores in registers (the exact packed E4M3->BF16 convert, right
+// before the MFMA that uses them), so every weight is decoded by the two
+// waves that share its columns in each 128-row M-tile, 2*N*K*ceil(M/128)
+// converts in all, on the vector ALU beside the matrix cores. (The 256 x 256
+// tiles of w8a16_gemm_wide.hip halve that per token.)
 //
 // Tiling (CDNA4: 64-wide wavefronts, bf16 MFMA v_mfma_f32_32x32x16_bf16,
 // 160 KB LDS with 64 four-byte banks, direct-to-LDS buffer loads):
