@@ -74,13 +74,15 @@ constexpr int64_t kSkinnyMaxM = 16;
 constexpr int64_t kSkinnyOnePassK = 4096;
 constexpr int64_t kSkinnyMaxK = 8192;
 constexpr int64_t kSkinnyTwoPassMinM = 12;
+constexpr int64_t kSkinnyLdsMaxM = 64;          // the one-shot form: up to four 16-row blocks of A
 inline bool skinny_fits(int64_t M, int64_t K) {
     return M >= 1 && M <= kSkinnyMaxM &&
            (K <= kSkinnyOnePassK || (K <= kSkinnyMaxK && M >= kSkinnyTwoPassMinM));
 }
 // One-shot skinny form (one 16-row weight block per workgroup, every weight
-// load issued up front, activations in LDS): whether it applies to (M, N, K)
-// on `cus` CUs, its k-blocks per wave and its activation phases (1 or 2).
+// load issued up front, activations in LDS; M <= kSkinnyLdsMaxM): whether it
+// applies to (M, N, K) on `cus` CUs, its k-blocks per wave and its
+// activation phases (1 to 8).
 bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, int* phases);
 inline bool skinny_lds_fits(int64_t M, int64_t N, int64_t K, int cus) {
     int kb = 0, phases = 1;

@@ -283,7 +283,7 @@ skinny_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, con
 // M = 1..4; the activations in registers instead of LDS: 10.6-33 against
 // 9.0-26 us.)
 constexpr int kLdsWaves = 8;
-constexpr int kLdsABytes = 128 * 1024;          // activation region: M * Kpad * 2 bytes at most
+constexpr int kLdsABytes = 128 * 1024;          // activation region of one phase: M * Kpad * 2 / PH bytes at most
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -298,18 +298,19 @@ __device__ __forceinline__ void lds_sync() {
 // touches at one k land in 16 different 16-byte slots of a 256-byte line.
 __device__ __forceinline__ int a_chunk_swz(int q, int m) { return (q & ~15) | ((q ^ m) & 15); }
 
-template <int KB, int PH, int SF>
+template <int KB, int PH, int MB, int SF>
 __global__ void __launch_bounds__(64 * kLdsWaves, 1)
 skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,
                   const uint16_t* __restrict__ res, uint16_t* __restrict__ out, int M, int N, int K) {
     constexpr bool kRowScale = SF == kScaleRowF32;
     constexpr int KBP = KB / PH;                        // k-blocks per wave and phase
-    static_assert(PH == 1 || (PH == 2 && KB % 2 == 0), "one or two phases");
+    static_assert(PH >= 1 && PH <= 8 && KB % PH == 0, "phases of whole k-blocks");
+    static_assert(MB == 1 || MB == 2 || MB == 4, "16, 32 or 64 rows of A");
     constexpr int kLoads = KB * 2;                      // weight loads per lane
     static_assert(kLoads < 64, "vmcnt field");
     extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];   // M * kph * 2 bytes, rounded to 1 KB
     __shared__ f32x4_t red[kLdsWaves * 64];
-    __shared__ uint16_t outs[256];
+    __shared__ uint16_t outs[256 * MB];
     __shared__ float row_s[kRowScale ? kRows : 1];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -379,13 +380,21 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
         }
     __builtin_amdgcn_sched_barrier(0);
 
-    // MFMA A operand of (k-block j, chunk c, half h): row min(r, M - 1) (rows
-    // past M feed output rows that are never stored), k = kblock(j)*128 + 64c
-    // + 16g + 8h, the same k-slot order as the weights.
-    const int am = min(r, M - 1);
-    const uint8_t* a_row = a_lds + am * (cph * 16);
+    // MFMA A operand of row block mb, (k-block j, chunk c, half h): row
+    // min(16mb + r, M - 1) (rows past M feed output rows that are never
+    // stored), k = kblock(j)*128 + 64c + 16g + 8h, the same k-slot order as
+    // the weights. One decoded weight fragment feeds all MB row blocks.
+    int am[MB];
+    const uint8_t* a_row[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        am[mb] = min(16 * mb + r, M - 1);
+        a_row[mb] = a_lds + am[mb] * (cph * 16);
+    }
     const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4_t acc = zero;
+    f32x4_t acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = zero;
 #pragma unroll
     for (int p = 0; p < PH; ++p) {
         if (p == 0) {
@@ -407,37 +416,48 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
         for (int jj = 0; jj < KBP; ++jj) {
             const int j = p * KBP + jj;
             const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), j));
-            f32x4_t blk = zero;
+            f32x4_t blk[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) blk[mb] = zero;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const bf16x8_t bw0 = e4m3x8(w[j][c][0], w[j][c][1]), bw1 = e4m3x8(w[j][c][2], w[j][c][3]);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int q = ((wave * KBP + jj) * kScaleBlock + 64 * c + 16 * g + 8 * h) / 8;
-                    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(a_row + a_chunk_swz(q, am) * 16);
-                    blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), h ? bw1 : bw0, blk,
-                                                                  0, 0, 0);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(a_row[mb] + a_chunk_swz(q, am[mb]) * 16);
+                        blk[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                          h ? bw1 : bw0, blk[mb], 0, 0, 0);
+                    }
                 }
             }
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], s, acc[v]);
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[mb][v] = fmaf(blk[mb][v], s, acc[mb][v]);
         }
     }
-    // Lane l holds output column l % 16, rows 4(l/16) + v; thread t < 256
-    // adds output (row t / 16, column t % 16) over the waves in order of
-    // their k-blocks (phase-major, so the order is fixed).
-    red[wave * 64 + lane] = acc;
-    __syncthreads();
-    if (threadIdx.x < 256) {
-        const int t = threadIdx.x, row = t / 16, col = t % 16;
-        const int l = col + 16 * (row / 4), v = row % 4;
-        float sum = red[l][v];
+    // Lane l holds output column l % 16, rows 16mb + 4(l/16) + v; thread
+    // t < 256 adds output (row 16mb + t / 16, column t % 16) over the waves
+    // in order of their k-blocks (phase-major, so the order is fixed), one
+    // row block at a time.
 #pragma unroll
-        for (int w2 = 1; w2 < kLdsWaves; ++w2) sum += red[w2 * 64 + l][v];
-        if constexpr (kRowScale) sum *= row_s[col];
-        outs[t] = f32_to_bf16_bits(sum);
+    for (int mb = 0; mb < MB; ++mb) {
+        red[wave * 64 + lane] = acc[mb];
+        __syncthreads();
+        if (threadIdx.x < 256) {
+            const int t = threadIdx.x, rr = t / 16, col = t % 16;
+            const int l = col + 16 * (rr / 4), v = rr % 4;
+            float sum = red[l][v];
+#pragma unroll
+            for (int w2 = 1; w2 < kLdsWaves; ++w2) sum += red[w2 * 64 + l][v];
+            if constexpr (kRowScale) sum *= row_s[col];
+            outs[mb * 256 + t] = f32_to_bf16_bits(sum);
+        }
+        __syncthreads();
     }
-    __syncthreads();
     // Outputs: (row, column) at outs[row * 16 + column].
     for (int e = threadIdx.x; e < M * 16; e += blockDim.x) {
         const int row = e / 16, col = e % 16, n = n0 + col;
@@ -449,16 +469,36 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     }
 }
 
+template <int KB, int MB, int SF>
+int launch_lds_mb(int phases, dim3 grid, hipStream_t s, const uint16_t* a, const uint8_t* w, const void* scale,
+                  const uint16_t* r, uint16_t* o, int m, int n, int k) {
+    const size_t lds = static_cast<size_t>((m * KB / phases * kLdsWaves * kScaleBlock * 2 + 1023) / 1024 * 1024);
+    const dim3 block(64 * kLdsWaves);
+    switch (phases) {
+        case 8:
+            if constexpr (KB % 8 == 0)
+                return launch_with_lds(&skinny_lds_kernel<KB, 8, MB, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
+            break;
+        case 4:
+            if constexpr (KB % 4 == 0)
+                return launch_with_lds(&skinny_lds_kernel<KB, 4, MB, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
+            break;
+        case 2:
+            if constexpr (KB % 2 == 0)
+                return launch_with_lds(&skinny_lds_kernel<KB, 2, MB, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
+            break;
+        default:
+            return launch_with_lds(&skinny_lds_kernel<KB, 1, MB, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
+    }
+    return W8A16_ERR_SHAPE;
+}
+
 template <int KB, int SF>
 int launch_lds(int phases, dim3 grid, hipStream_t s, const uint16_t* a, const uint8_t* w, const void* scale,
                const uint16_t* r, uint16_t* o, int m, int n, int k) {
-    const size_t lds = static_cast<size_t>((m * KB / phases * kLdsWaves * kScaleBlock * 2 + 1023) / 1024 * 1024);
-    if constexpr (KB % 2 == 0)
-        if (phases == 2)
-            return launch_with_lds(&skinny_lds_kernel<KB, 2, SF>, grid, dim3(64 * kLdsWaves), lds, s, a, w, scale, r,
-                                   o, m, n, k);
-    return launch_with_lds(&skinny_lds_kernel<KB, 1, SF>, grid, dim3(64 * kLdsWaves), lds, s, a, w, scale, r, o, m, n,
-                           k);
+    if (m > 32) return launch_lds_mb<KB, 4, SF>(phases, grid, s, a, w, scale, r, o, m, n, k);
+    if (m > 16) return launch_lds_mb<KB, 2, SF>(phases, grid, s, a, w, scale, r, o, m, n, k);
+    return launch_lds_mb<KB, 1, SF>(phases, grid, s, a, w, scale, r, o, m, n, k);
 }
 
 }  // namespace
@@ -517,7 +557,7 @@ int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const
 // than three workgroups fit a CU and the ring form is faster (measured on the
 // Mamba-2 in_proj: 23 against 20 us at M = 8).
 bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, int* phases) {
-    if (M < 1 || M > kSkinnyMaxM || N < 1 || K < 16 || cus < 1) return false;
+    if (M < 1 || M > kSkinnyLdsMaxM || N < 1 || K < 16 || cus < 1) return false;
     const int64_t k_blocks = ceil_div(K, kScaleBlockHost);
     int per_wave = 1;
     while (per_wave * kLdsWaves < k_blocks) per_wave *= 2;
@@ -526,13 +566,21 @@ bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, int* pha
     const int64_t nblk = ceil_div(N, kRows);
     if (nblk > INT32_MAX) return false;
     const int64_t a_bytes = M * per_wave * kLdsWaves * kScaleBlockHost * 2;
-    // Activations over the LDS budget go in two phases of half of K each
-    // where every weight block has a CU of its own (one workgroup per CU
-    // anyway: the Mamba-2 out_proj at 9..16 rows); the second phase's copy
-    // waits for the first phase's products.
-    *phases = a_bytes > kLdsABytes ? 2 : 1;
-    if (*phases == 2 && (nblk > cus || per_wave < 2 || a_bytes > 2 * kLdsABytes)) return false;
-    if (*phases == 1 && nblk > cus && a_bytes > 32 * 1024) return false;
+    // Activations over the LDS budget go in phases of a part of K each; each
+    // phase's copy waits for the previous phase's products. The budget:
+    // 128 KB where every weight block has a CU of its own, else 32 KB (so
+    // that several workgroups share a CU and cover each other's copies) and
+    // no more than two phases (measured on the Mamba-2 in_proj: 19.5 against
+    // 20.0 us for the ring form at M = 8 in two phases; 23.1 against 21.4 at
+    // M = 16 in four). Above 16 rows (two or four MFMA row blocks sharing
+    // each decoded weight fragment), only where every weight block has a CU.
+    const bool own_cu = nblk <= cus;
+    if (M > kSkinnyMaxM && !own_cu) return false;
+    const int64_t budget = own_cu ? kLdsABytes : 32 * 1024;
+    int ph = 1;
+    while (a_bytes > ph * budget && ph < (own_cu ? 8 : 2)) ph *= 2;
+    if (a_bytes > ph * budget || per_wave % ph != 0) return false;
+    *phases = ph;
     *kb = per_wave;
     return true;
 }

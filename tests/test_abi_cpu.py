@@ -316,7 +316,8 @@ def test_gemm_workspace_size_follows_the_split_schedule():
     assert ws(8192, 35072, 8192) == 0                   # 256 x 256 tiles
     need = ws(128, 4096, 8192)                          # 32 tiles of 128 x 128 on 512 slots
     assert need > 0 and need % (128 * 128 * 4) == 0
-    assert ws(32, 4096, 8192) > 0
+    assert ws(32, 4096, 8192) == 0                      # one-shot skinny kernel (every weight block on a CU)
+    assert ws(32, 18560, 4096) > 0                      # 145 tiles of 32 x 128 on 1024 slots
 
 
 def test_gemm_ws_rejections_before_any_hip_call():
@@ -337,7 +338,7 @@ def test_gemm_noalloc_scratch_and_rejections_before_any_hip_call():
     # 64 MiB: two 128 x 128 fp32 partial tiles for each of 512 workgroups,
     # the largest split schedule on a 256-CU device
     assert binding.gemm_noalloc_scratch_bytes() == 64 << 20
-    for M, N, K in ((32, 4096, 8192), (128, 4096, 8192), (256, 18560, 4096), (129, 1000, 1040)):
+    for M, N, K in ((32, 18560, 4096), (128, 4096, 8192), (256, 18560, 4096), (129, 1000, 1040)):
         assert 0 < binding.gemm_workspace_size(M, N, K) <= binding.gemm_noalloc_scratch_bytes()
     A, Wq, scale, out = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
     call = binding.gemm_noalloc_raw

@@ -102,8 +102,10 @@ def test_layer_decode_step_graph_replays_match_eager(dev, M):
 
 # GEMM shapes of every tile schedule: whole 128 x 128 tiles (16 tiles), the
 # k-split inside the workgroup (192..256 tiles), the 256 x 256 tiles (one
-# round of 256), the skinny kernel, and 32-row tiles.
-CAPTURE_SHAPES = [(129, 1000, 1040), (200, 12200, 1280), (256, 65536, 64), (16, 4096, 8192), (20, 4096, 8192)]
+# round of 256), the skinny kernel's one-shot form (two and four activation
+# phases of 128 KB of dynamic LDS), and 32-row tiles.
+CAPTURE_SHAPES = [(129, 1000, 1040), (200, 12200, 1280), (256, 65536, 64), (16, 4096, 8192), (32, 4096, 8192),
+                  (20, 18560, 8192)]
 
 
 @pytest.mark.parametrize("M,N,K", CAPTURE_SHAPES)

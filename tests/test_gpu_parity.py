@@ -140,21 +140,25 @@ def test_gemv_k_edges(dev, M, N, K):
 # --- GEMM ------------------------------------------------------------------------
 
 # Paths of the GEMM entry (w8a16_gemm, which computes every tile whole in one
-# workgroup and uses no workspace): M <= 16 with K <= 4096 (M >= 12: K <= 8192)
-# streams the weights through the skinny kernel (16-row weight blocks, K split
-# over 4 to 16 waves, ring of 2 blocks per wave; ragged N, idle waves when K is
-# short, several blocks per workgroup; K above 4096 in two passes: M = 16,
-# N = 4096, K = 8192 is the Mamba-2 out_proj, K = 4224 and 6160 leave idle
-# waves and a ragged k-block in the second pass). Otherwise the tiles are 32 x
-# 128 for M <= 32, 64 x 128 for M <= 64 and 128 x 128 above; 128 x 128 tiles
-# numbering 192..256 (on 256 CUs) with K a multiple of 256 split their
-# k-steps between two wave groups of one workgroup (M = 200, N = 12200,
-# K = 1280: ragged M and N, 10 k-steps per group; M = 256, N = 12288, K = 512:
-# 4 per group). The shapes span few tiles, more tiles than one round of the
-# grid (N = 65704, 78339, 89603 with 65 <= M <= 128; N = 140000, 166400 with
-# M <= 32; N = 98400 with M <= 64) and ragged M, N and K tails. The
-# 256 x 256 tiles have their own tests (test_gpu_wide.py), and the split
-# schedules of w8a16_gemm_ws theirs below.
+# workgroup and uses no workspace). M <= 64 takes the skinny kernel's one-shot
+# form (one 16-row weight block per workgroup, activations in LDS, in phases
+# of part of K) where its plan fits: every weight block on a CU of its own
+# (N <= 16 * CUs: here N = 130..4100 with M up to 64), or more blocks than
+# CUs with at most 16 rows and 64 KB of activations (N = 140000 / 166400 with
+# M = 3 / 5, N = 4100 with M = 2). Otherwise M <= 16 with
+# K <= 4096 (M >= 12: K <= 8192) takes its ring form (16-row weight blocks,
+# K split over 16 waves, ring of 2 blocks per wave, several blocks per
+# workgroup; M = 16, N = 18560, K = 4096). Otherwise the tiles are 32 x 128
+# for M <= 32 (N = 18560 at M = 32; M = 7 with K = 8208, past the one-shot
+# form's 64 k-blocks), 64 x 128 for M <= 64 (N = 18560, 98400
+# at M = 48, 40) and 128 x 128 above; 128 x 128 tiles numbering 192..256 (on
+# 256 CUs) with K a multiple of 256 split their k-steps between two wave
+# groups of one workgroup (M = 200, N = 12200, K = 1280: ragged M and N, 10
+# k-steps per group; M = 256, N = 12288, K = 512: 4 per group). The shapes
+# span few tiles, more tiles than one round of the grid (N = 65704, 78339,
+# 89603 with 65 <= M <= 128) and ragged M, N and K tails. The one-shot form,
+# the 256 x 256 tiles and the split schedules of w8a16_gemm_ws have their own
+# tests (test_gpu_skinny.py, test_gpu_wide.py, below).
 @pytest.mark.parametrize("M,N,K", [(1, 384, 256), (17, 130, 144), (127, 300, 272), (129, 1000, 1040),
                                    (300, 257, 4096), (256, 256, 128), (1, 1, 16), (64, 4096, 512),
                                    (513, 640, 1024), (130, 18560, 128), (66, 65704, 1040),
@@ -325,7 +329,7 @@ def test_empty_and_rejected_calls(dev, entry):
 # Shapes whose tiles split their k-blocks between workgroups when a workspace
 # is given (w8a16_gemm_ws): fewer tiles than slots (32-, 64- and 128-row
 # tiles), a whole round plus a split remainder, and one split tile.
-SPLIT_SHAPES = [(129, 1000, 1040), (300, 257, 4096), (20, 4096, 8192), (48, 18560, 2048), (130, 38300, 512),
+SPLIT_SHAPES = [(129, 1000, 1040), (300, 257, 4096), (20, 18560, 8192), (48, 18560, 2048), (130, 38300, 512),
                 (66, 65704, 1040), (17, 140000, 1040), (40, 98400, 528), (128, 4096, 8192), (256, 4096, 8192)]
 
 

@@ -13,9 +13,14 @@ shapes below are chosen for that (on a 256-CU MI355X):
   * M = 5, N = 1000, K = 1040: 2 k-blocks per wave, a ragged k-block;
   * M = 4, N = 18560, K = 4096: the Mamba-2 in_proj, 1160 blocks;
   * M = 1 through the GEMM entry; M = 16 with a short K;
-  * activations in registers instead of LDS (more than 128 KB of them, every
-    weight block on a CU of its own): M = 16, N = 4096, K = 8192 (the Mamba-2
-    out_proj), M = 9 with a ragged N, M = 16 with a k-tail of 16.
+  * activations in two phases of half of K (more than 128 KB of them with
+    every weight block on a CU of its own, or more than 32 KB with more
+    blocks than CUs): M = 16, N = 4096, K = 8192 (the Mamba-2 out_proj), M = 9
+    with a ragged N, M = 16 with a k-tail of 16, M = 8 with 257 blocks;
+  * 17 to 64 rows (two or four MFMA row blocks sharing each decoded weight
+    fragment; GEMM entry, every weight block on a CU of its own): M = 32 and
+    64 on the Mamba-2 out_proj (4 and 8 phases), M = 20 with a ragged k-block,
+    M = 40 with a k-tail (8 phases), M = 17 (one row in the second block).
 """
 import numpy as np
 import pytest
@@ -28,7 +33,8 @@ pytestmark = pytest.mark.gpu
 
 RTOL, ATOL = 4e-3, 1e-6
 SHAPES = [(2, 4100, 4096), (3, 129, 4112), (8, 4096, 8192), (5, 1000, 1040), (4, 18560, 4096), (1, 4096, 8192),
-          (16, 300, 2048), (16, 4096, 8192), (9, 300, 8192), (16, 129, 4112)]
+          (16, 300, 2048), (16, 4096, 8192), (9, 300, 8192), (16, 129, 4112), (8, 4100, 4096),
+          (32, 4096, 8192), (64, 4096, 8192), (20, 300, 1040), (40, 129, 4112), (17, 1000, 4096)]
 
 
 def say(*a):
@@ -71,8 +77,10 @@ def run(entry, A, W, S, device, fmt=None):
     return bits(out)
 
 
-# The GEMV entry keeps the VALU GEMV at M = 1, so M = 1 runs through the GEMM entry only.
-@pytest.mark.parametrize("entry,M,N,K", [(e, *s) for e in ("gemv", "gemm") for s in SHAPES if e == "gemm" or s[0] > 1])
+# The GEMV entry keeps the VALU GEMV at M = 1 and takes at most 16 rows, so
+# those shapes run through the GEMM entry only.
+@pytest.mark.parametrize("entry,M,N,K", [(e, *s) for e in ("gemv", "gemm") for s in SHAPES
+                                         if e == "gemm" or 1 < s[0] <= 16])
 def test_one_shot_every_element(dev, entry, M, N, K):
     say(f"one-shot skinny via {entry} M={M} N={N} K={K}")
     A = inputs.activations(M, K, 4100 + M)
@@ -89,7 +97,7 @@ def test_one_shot_matches_between_entries(dev):
     assert np.array_equal(run("gemv", A, W, S, dev), run("gemm", A, W, S, dev))
 
 
-@pytest.mark.parametrize("M,N,K", [(2, 4100, 4096), (6, 4096, 8192), (12, 4096, 8192)])
+@pytest.mark.parametrize("M,N,K", [(2, 4100, 4096), (6, 4096, 8192), (12, 4096, 8192), (48, 4096, 8192)])
 def test_one_shot_residual_epilogue_bits(dev, M, N, K):
     say(f"one-shot skinny + residual M={M} N={N} K={K}")
     A = inputs.activations(M, K, 4500 + M)
@@ -103,12 +111,12 @@ def test_one_shot_residual_epilogue_bits(dev, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["block_f32", "row_f32"])
-@pytest.mark.parametrize("M,N,K", [(3, 129, 4112), (6, 4096, 8192), (14, 300, 8192)])
+@pytest.mark.parametrize("M,N,K", [(3, 129, 4112), (6, 4096, 8192), (14, 300, 8192), (36, 300, 8192)])
 def test_one_shot_scale_formats(dev, fmt, M, N, K):
     say(f"one-shot skinny {fmt} M={M} N={N} K={K}")
     A = inputs.activations(M, K, 4800 + M)
     W, S = inputs.weights_fmt(N, K, 0.02, 4900 + K, fmt)
-    for entry in ("gemv", "gemm"):
+    for entry in ("gemv", "gemm") if M <= 16 else ("gemm",):
         got = run(entry, A, W, S, dev, fmt)
         ref, den = oracle.w8a16(A, W, S, fmt=fmt)
         assert_within_tol(got, ref, den, f"{entry} {fmt}")
