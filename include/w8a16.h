@@ -92,10 +92,11 @@ enum w8a16_scale_format {
  * weights read once for all of them). 1 <= M <= 16, N >= 0, K % 16 == 0,
  * 16 <= K <= 16384 for M <= 8 and 16 <= K <= 8192 for M >= 9.
  * M == 0 or N == 0 is a no-op returning W8A16_OK.
- * Each weight byte is read from HBM once per call for all M rows. From
- * M = 4 on with K <= 4096, and from M = 12 on with K <= 8192, the call runs
- * the skinny path of w8a16_gemm
- * (products on the matrix cores; same result contract).
+ * Each weight byte is read from HBM once per call for all M rows. M = 1
+ * runs a GEMV on the vector ALU (dot products over 16-byte weight chunks,
+ * reduced across the wavefront and the workgroup in a fixed order). From
+ * M = 2 on, where the skinny path of w8a16_gemm applies (below), the call
+ * runs it (products on the matrix cores; same result contract).
  */
 int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
                int64_t M, int64_t N, int64_t K, void* stream);
@@ -106,14 +107,20 @@ int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
  * the skinny case of a few tokens (speculative verify, batched decode).
  * M >= 0 (any), N >= 0, 16 <= K < 2^23, K % 16 == 0; M == 0 or N == 0 is a
  * no-op. Paths, chosen by M, N, K and the device's CU count only:
- *  - M <= 16 and K <= 4096, or 12 <= M <= 16 and K <= 8192 (two passes over
- *    K): the weights stream from HBM straight into the
- *    matrix-core operands (one kernel, no workspace);
+ *  - skinny (one kernel, no workspace; the weights stream from HBM straight
+ *    into the matrix-core operands, each 16-row weight block read once for
+ *    all M rows): M <= 64 with K <= 8192 where one workgroup per 16-row
+ *    block fits (the activations, in LDS, copied in up to 8 parts of K;
+ *    above 16 rows only when N <= 16 * CUs); else M <= 16 with K <= 4096, or
+ *    12 <= M <= 16 with K <= 8192, with workgroups walking several blocks;
  *  - M >= 65 where 256 x 256 output tiles fill every round of CU-many tiles
  *    to at least 85 % (e.g. the 8192-token prefill): one workgroup per CU
  *    walks those tiles; each weight is converted once per tile as
  *    bf16(e * s), the block scale folded in (e * s is exact in fp32, rounded
- *    once), and the matrix cores accumulate over the whole K range;
+ *    once), and the matrix cores accumulate over the whole K range; where
+ *    they cover at least one whole round but leave a sparse one (the
+ *    1024-token in_proj), whole rounds of them take the first columns and
+ *    the tiles below the rest;
  *  - otherwise output tiles of 32 (M <= 32), 64 (M <= 64) or 128 rows by 128
  *    columns: the E4M3 weight bytes of a tile are staged once per workgroup
  *    and decoded in registers, and the block scale multiplies each 128-wide
