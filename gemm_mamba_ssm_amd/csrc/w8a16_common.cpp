@@ -1,6 +1,9 @@
 // Status strings and the per-device compute-unit count used to size grids.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <vector>
+
 #include "w8a16_host.h"
 
 namespace w8a16 {
@@ -17,6 +20,30 @@ int device_cu_count() {
         cached[dev] = cus;
     }
     return cached[dev];
+}
+
+bool allow_large_lds(const void* kernel, size_t bytes) {
+    struct Raised {
+        int dev;
+        const void* kernel;
+        size_t bytes;
+    };
+    static std::mutex mu;
+    static std::vector<Raised> done;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    Raised* entry = nullptr;
+    for (auto& d : done)
+        if (d.dev == dev && d.kernel == kernel) entry = &d;
+    if (entry && entry->bytes >= bytes) return true;
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes)) != hipSuccess)
+        return false;
+    if (entry)
+        entry->bytes = bytes;
+    else
+        done.push_back(Raised{dev, kernel, bytes});
+    return true;
 }
 
 }  // namespace w8a16

@@ -121,14 +121,16 @@ inline int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s
     return e == hipSuccess ? W8A16_OK : W8A16_ERR_LAUNCH;
 }
 
-// The same with `lds_bytes` of dynamic LDS (the kernel's limit is raised
-// first when that exceeds 64 KB).
+// Raise `kernel`'s dynamic LDS limit to at least `bytes` on the current
+// device (a HIP call only when that raises it); false if that fails.
+bool allow_large_lds(const void* kernel, size_t bytes);
+
+// The same with `lds_bytes` of dynamic LDS (above 64 KB the kernel's limit
+// is raised first).
 template <typename... KArgs>
 inline int launch_with_lds(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream,
                            KArgs... args) {
-    if (lds_bytes > 64 * 1024 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds_bytes)) != hipSuccess)
+    if (lds_bytes > 64 * 1024 && !allow_large_lds(reinterpret_cast<const void*>(kernel), lds_bytes))
         return W8A16_ERR_LAUNCH;
     void* argv[] = {static_cast<void*>(&args)...};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds_bytes, stream);
