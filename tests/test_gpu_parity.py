@@ -219,6 +219,18 @@ def test_gemm_prefill_8k_every_tile(dev, proj):
     assert_within_tol(got[mi, ni], ref, den, f"{p.name}: {cols.size} whole columns")
 
 
+# Long K past what the 256 x 256 tiles and the skinny kernel take (K = 65552,
+# 513 k-blocks with a k-tail of 16): 128 x 128 tiles, every element.
+def test_gemm_long_k_every_element(dev):
+    M, N, K = 130, 300, 65552
+    say(f"gemm long K M={M} N={N} K={K}")
+    A = inputs.activations(M, K, 7700)
+    W, S = inputs.weights(N, K, 0.02, 7800)
+    got = run(binding.w8a16_gemm, A, W, S, dev)
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(got, ref, den, f"gemm M={M} N={N} K={K}")
+
+
 def test_gemv_matches_gemm_on_decode_shapes(dev):
     for p in inputs.WORKLOADS["multiseq_m8"]:
         A, W, S = inputs.make(p)

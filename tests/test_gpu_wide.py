@@ -214,3 +214,23 @@ def test_wide_split_columns_residual_and_workspace(dev):
     assert_within_tol(bits(yw), ref, den, "split columns, tail tiles split through the workspace")
     # the 256 x 256 part is the same kernel either way: its columns are bit-identical
     assert np.array_equal(bits(yw)[:, :16384], bits(y)[:, :16384])
+
+
+# Long K on the 256 x 256 tiles: K = 16400 holds 129 k-blocks, so the tile's
+# scale row spans three of the four per-lane scale registers, and the k-tail
+# is 16. M = 1000, N = 16384: one round of 4 x 64 tiles. Checked on a whole
+# row in every 128-row block and a whole column in every 128-column block.
+def test_wide_long_k_every_tile(dev):
+    M, N, K = 1000, 16384, 16400
+    say(f"wide gemm long K M={M} N={N} K={K}")
+    A = inputs.activations(M, K, 3600)
+    W, S = inputs.weights(N, K, 0.02, 3700)
+    got = gemm(A, W, S, dev)
+    rows = np.unique(np.r_[np.arange(0, M, 128) + 37, M - 1].clip(0, M - 1))
+    cols = np.unique(np.r_[np.arange(0, N, 128) + 91, N - 1].clip(0, N - 1))
+    ref, den = oracle.w8a16(A[rows], W, S)
+    assert_within_tol(got[rows], ref, den, f"long K: {rows.size} whole rows")
+    mi = np.repeat(np.arange(M), cols.size)
+    ni = np.tile(cols, M)
+    ref, den = oracle.w8a16_points(A, W, S, mi, ni)
+    assert_within_tol(got[mi, ni], ref, den, f"long K: {cols.size} whole columns")
