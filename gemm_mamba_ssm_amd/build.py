@@ -21,8 +21,8 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw8a16.so")
 ARCH = "gfx950"
 
-SOURCES = ["w8a16_common.cpp", "w8a16_gemv.hip", "w8a16_gemm.hip", "w8a16_gemm_wide.hip", "w8a16_skinny.hip", "w8a16_dequant.hip", "w8a16_norm.hip",
-           "w8a16_mamba2.hip", "w8a16_read.hip"]
+SOURCES = ["w8a16_common.cpp", "w8a16_gemv.hip", "w8a16_gemm.hip", "w8a16_gemm_wide.hip", "w8a16_skinny.hip",
+           "w8a16_mid.hip", "w8a16_dequant.hip", "w8a16_norm.hip", "w8a16_mamba2.hip", "w8a16_read.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -801,9 +801,10 @@ int run_gemm(const void* A, const void* Wq, const void* scale, const void* resid
 //  first columns, the rest of the columns (less than a round) with the
 //  128-row tiles; e.g. the 1024-token in_proj: 256 tiles over columns
 //  0..16383, then 8 x 17 tiles of 128 x 128.
-enum class Path { kSkinny, kTile32, kTile64, kWide, kWideSplitN, kBigSplit, kBigTile };
+enum class Path { kSkinny, kMid, kTile32, kTile64, kWide, kWideSplitN, kBigSplit, kBigTile };
 
 Path choose_path(int64_t M, int64_t N, int64_t K, int64_t* n_wide = nullptr) {
+    if (mid_plan(M, N, K, device_cu_count()) >= 0) return Path::kMid;
     if (skinny_fits(M, K) || skinny_lds_fits(M, N, K, device_cu_count())) return Path::kSkinny;
     if (M <= Skinny32::TM) return Path::kTile32;
     if (M <= Skinny64::TM) return Path::kTile64;
@@ -847,6 +848,7 @@ int gemm_by_shape(const void* A, const void* Wq, const void* scale, const void* 
     int64_t nw = 0;
     switch (choose_path(M, N, K, &nw)) {
         case Path::kSkinny: return skinny_gemm(A, Wq, scale, SF, residual, out, M, N, K, s);
+        case Path::kMid: return mid_gemm(A, Wq, scale, SF, residual, out, M, N, K, N, s);
         case Path::kTile32:
             return run_gemm<Skinny32, SF, RES>(A, Wq, scale, residual, out, M, N, K, N, partials, workspace_bytes, s);
         case Path::kTile64:

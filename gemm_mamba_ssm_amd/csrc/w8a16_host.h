@@ -74,7 +74,7 @@ constexpr int64_t kSkinnyMaxM = 16;
 constexpr int64_t kSkinnyOnePassK = 4096;
 constexpr int64_t kSkinnyMaxK = 8192;
 constexpr int64_t kSkinnyTwoPassMinM = 12;
-constexpr int64_t kSkinnyLdsMaxM = 64;          // the one-shot form: up to four 16-row blocks of A
+constexpr int64_t kSkinnyLdsMaxM = 16;          // the one-shot form: one 16-row block of A
 inline bool skinny_fits(int64_t M, int64_t K) {
     return M >= 1 && M <= kSkinnyMaxM &&
            (K <= kSkinnyOnePassK || (K <= kSkinnyMaxK && M >= kSkinnyTwoPassMinM));
@@ -93,6 +93,19 @@ int skinny_lds_gemm(const void* A, const void* Wq, const void* scale, int fmt, c
 // `residual` ([M][N] BF16, or nullptr) adds the residual epilogue.
 int skinny_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out,
                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Mid-size GEMM (w8a16_mid.hip): kMidMinM..kMidMaxM rows, K <= kMidMaxK; one
+// workgroup per small output tile, K split across its waves, A and W streamed
+// into registers. mid_plan returns the tile shape for (M, N, K) on `cus` CUs
+// (an index, or -1 when the kernel does not apply); mid_gemm launches it
+// (`residual` as for skinny_gemm, BF16 block scales only; `ldo` the row
+// stride of out and residual, in elements).
+constexpr int64_t kMidMinM = 17;
+constexpr int64_t kMidMaxM = 256;
+constexpr int64_t kMidMaxK = 32768;
+int mid_plan(int64_t M, int64_t N, int64_t K, int cus);
+int mid_gemm(const void* A, const void* Wq, const void* scale, int fmt, const void* residual, void* out, int64_t M,
+             int64_t N, int64_t K, int64_t ldo, hipStream_t stream);
 
 // Prefill GEMM with 256 x 256 tiles (w8a16_gemm_wide.hip): the weight
 // convert is done once per workgroup tile, with the block scale folded in.

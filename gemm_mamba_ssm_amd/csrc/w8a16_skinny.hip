@@ -298,14 +298,14 @@ __device__ __forceinline__ void lds_sync() {
 // touches at one k land in 16 different 16-byte slots of a 256-byte line.
 __device__ __forceinline__ int a_chunk_swz(int q, int m) { return (q & ~15) | ((q ^ m) & 15); }
 
-template <int KB, int PH, int MB, int SF>
+template <int KB, int PH, int SF>
 __global__ void __launch_bounds__(64 * kLdsWaves, 1)
 skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W, const void* __restrict__ S,
                   const uint16_t* __restrict__ res, uint16_t* __restrict__ out, int M, int N, int K) {
     constexpr bool kRowScale = SF == kScaleRowF32;
     constexpr int KBP = KB / PH;                        // k-blocks per wave and phase
     static_assert(PH >= 1 && PH <= 8 && KB % PH == 0, "phases of whole k-blocks");
-    static_assert(MB == 1 || MB == 2 || MB == 4, "16, 32 or 64 rows of A");
+    constexpr int MB = 1;                               // one 16-row block of A
     constexpr int kLoads = KB * 2;                      // weight loads per lane
     static_assert(kLoads < 64, "vmcnt field");
     extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];   // M * kph * 2 bytes, rounded to 1 KB
@@ -469,36 +469,28 @@ skinny_lds_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     }
 }
 
-template <int KB, int MB, int SF>
-int launch_lds_mb(int phases, dim3 grid, hipStream_t s, const uint16_t* a, const uint8_t* w, const void* scale,
-                  const uint16_t* r, uint16_t* o, int m, int n, int k) {
+template <int KB, int SF>
+int launch_lds(int phases, dim3 grid, hipStream_t s, const uint16_t* a, const uint8_t* w, const void* scale,
+               const uint16_t* r, uint16_t* o, int m, int n, int k) {
     const size_t lds = static_cast<size_t>((m * KB / phases * kLdsWaves * kScaleBlock * 2 + 1023) / 1024 * 1024);
     const dim3 block(64 * kLdsWaves);
     switch (phases) {
         case 8:
             if constexpr (KB % 8 == 0)
-                return launch_with_lds(&skinny_lds_kernel<KB, 8, MB, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
+                return launch_with_lds(&skinny_lds_kernel<KB, 8, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
             break;
         case 4:
             if constexpr (KB % 4 == 0)
-                return launch_with_lds(&skinny_lds_kernel<KB, 4, MB, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
+                return launch_with_lds(&skinny_lds_kernel<KB, 4, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
             break;
         case 2:
             if constexpr (KB % 2 == 0)
-                return launch_with_lds(&skinny_lds_kernel<KB, 2, MB, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
+                return launch_with_lds(&skinny_lds_kernel<KB, 2, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
             break;
         default:
-            return launch_with_lds(&skinny_lds_kernel<KB, 1, MB, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
+            return launch_with_lds(&skinny_lds_kernel<KB, 1, SF>, grid, block, lds, s, a, w, scale, r, o, m, n, k);
     }
     return W8A16_ERR_SHAPE;
-}
-
-template <int KB, int SF>
-int launch_lds(int phases, dim3 grid, hipStream_t s, const uint16_t* a, const uint8_t* w, const void* scale,
-               const uint16_t* r, uint16_t* o, int m, int n, int k) {
-    if (m > 32) return launch_lds_mb<KB, 4, SF>(phases, grid, s, a, w, scale, r, o, m, n, k);
-    if (m > 16) return launch_lds_mb<KB, 2, SF>(phases, grid, s, a, w, scale, r, o, m, n, k);
-    return launch_lds_mb<KB, 1, SF>(phases, grid, s, a, w, scale, r, o, m, n, k);
 }
 
 }  // namespace
@@ -572,10 +564,8 @@ bool skinny_lds_plan(int64_t M, int64_t N, int64_t K, int cus, int* kb, int* pha
     // that several workgroups share a CU and cover each other's copies) and
     // no more than two phases (measured on the Mamba-2 in_proj: 19.5 against
     // 20.0 us for the ring form at M = 8 in two phases; 23.1 against 21.4 at
-    // M = 16 in four). Above 16 rows (two or four MFMA row blocks sharing
-    // each decoded weight fragment), only where every weight block has a CU.
+    // M = 16 in four).
     const bool own_cu = nblk <= cus;
-    if (M > kSkinnyMaxM && !own_cu) return false;
     const int64_t budget = own_cu ? kLdsABytes : 32 * 1024;
     int ph = 1;
     while (a_bytes > ph * budget && ph < (own_cu ? 8 : 2)) ph *= 2;

@@ -314,16 +314,20 @@ def test_gemm_workspace_size_follows_the_split_schedule():
     assert ws(1024, 18560, 4096) == 0                   # whole 128 x 128 tiles
     assert ws(1024, 4096, 8192) == 0                    # k split inside the workgroup
     assert ws(8192, 35072, 8192) == 0                   # 256 x 256 tiles
-    need = ws(128, 4096, 8192)                          # 32 tiles of 128 x 128 on 512 slots
+    need = ws(512, 4096, 8192)                          # 128 tiles of 128 x 128 on 512 slots
     assert need > 0 and need % (128 * 128 * 4) == 0
-    assert ws(32, 4096, 8192) == 0                      # one-shot skinny kernel (every weight block on a CU)
-    assert ws(32, 18560, 4096) > 0                      # 145 tiles of 32 x 128 on 1024 slots
+    assert ws(16, 4096, 8192) == 0                      # one-shot skinny kernel (every weight block on a CU)
+    for m in (17, 32, 128, 256):                        # mid-size kernel: K split inside the workgroup
+        assert ws(m, 4096, 8192) == 0 and ws(m, 18560, 4096) == 0
+    assert ws(32, 18560, 40960) > 0                     # K past the mid-size kernel: 145 tiles of 32 x 128
+    assert ws(384, 18560, 4096) == 64 << 20             # 435 tiles of 128 x 128 cut over 512 workgroups
 
 
 def test_gemm_ws_rejections_before_any_hip_call():
     A, Wq, scale, out = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
-    M, N, K = 128, 4096, 8192
+    M, N, K = 512, 4096, 8192
     need = binding.gemm_workspace_size(M, N, K)
+    assert need > 0
     wsp = FAKE + (4 << 30)
     call = binding.gemm_ws_raw
     assert call(A, Wq, scale, out, M, N, K, wsp + 16, need, 0) == binding.ERR_ALIGN
@@ -338,7 +342,7 @@ def test_gemm_noalloc_scratch_and_rejections_before_any_hip_call():
     # 64 MiB: two 128 x 128 fp32 partial tiles for each of 512 workgroups,
     # the largest split schedule on a 256-CU device
     assert binding.gemm_noalloc_scratch_bytes() == 64 << 20
-    for M, N, K in ((32, 18560, 4096), (128, 4096, 8192), (256, 18560, 4096), (129, 1000, 1040)):
+    for M, N, K in ((32, 18560, 40960), (512, 4096, 8192), (384, 18560, 4096), (300, 1000, 1040)):
         assert 0 < binding.gemm_workspace_size(M, N, K) <= binding.gemm_noalloc_scratch_bytes()
     A, Wq, scale, out = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
     call = binding.gemm_noalloc_raw

@@ -191,13 +191,14 @@ def test_gemv_fused_without_prologue_matches_plain_bits(dev, M):
 
 GEMM_RES_SHAPES = [(1, 384, 256), (16, 1000, 4096), (20, 4096, 8192), (40, 98400, 528), (129, 1000, 1040),
                    (300, 257, 4096), (66, 65704, 1040), (513, 640, 1024), (200, 12200, 1280),
-                   (12, 300, 6160)]
+                   (12, 300, 6160), (20, 1000, 36880), (768, 4096, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_RES_SHAPES)
 def test_gemm_residual_epilogue_bits(dev, M, N, K):
     """out = bf16(residual + y) exactly, y = the same GEMM without the residual
-    (skinny kernel, 32/64/128-row tiles, whole and split tiles)."""
+    (skinny kernel, mid-size kernel, 32-, 64- and 128-row tiles, the k-split
+    workgroups)."""
     say(f"gemm_residual M={M} N={N} K={K}")
     A = inputs.activations(M, K, 4600 + M)
     Wq, S = inputs.weights(N, K, 0.02, 4700 + N + K)

@@ -100,12 +100,14 @@ def test_layer_decode_step_graph_replays_match_eager(dev, M):
                 f"replay {rep}: {name} differs from the eager run"
 
 
-# GEMM shapes of every tile schedule: whole 128 x 128 tiles (16 tiles), the
-# k-split inside the workgroup (192..256 tiles), the 256 x 256 tiles (one
-# round of 256), the skinny kernel's one-shot form (two and four activation
-# phases of 128 KB of dynamic LDS), and 32-row tiles.
-CAPTURE_SHAPES = [(129, 1000, 1040), (200, 12200, 1280), (256, 65536, 64), (16, 4096, 8192), (32, 4096, 8192),
-                  (20, 18560, 8192)]
+# GEMM shapes of every tile schedule: whole 128 x 128 tiles (24 of them; with
+# a workspace, split), the k-split inside the workgroup (256 tiles), the
+# 256 x 256 tiles (one round of 256), the skinny kernel's one-shot form (two
+# activation phases of 128 KB of dynamic LDS), 32-row tiles past the
+# mid-size kernel's K (split with a workspace), and the mid-size kernel.
+CAPTURE_SHAPES = [(300, 1000, 1040), (1024, 4096, 512), (512, 32768, 64), (16, 4096, 8192), (20, 4100, 40960),
+                  (20, 18560, 8192), (129, 1000, 1040), (256, 4096, 8192)]
+SPLIT_WITH_WORKSPACE = {(300, 1000, 1040), (20, 4100, 40960)}
 
 
 @pytest.mark.parametrize("M,N,K", CAPTURE_SHAPES)
@@ -119,8 +121,8 @@ def test_gemm_captured_as_first_call_on_a_fresh_stream(dev, M, N, K, with_worksp
     W, S = inputs.weights(N, K, 0.02, 9300 + N)
     dW, dS = u8(W, dev), bf(S, dev)
     ws = binding.gemm_workspace(M, N, K, dev) if with_workspace else None
-    if with_workspace and M == 20:
-        assert ws is not None, "32-row tiles at this shape split their k-blocks"
+    if with_workspace:
+        assert (ws is not None) == ((M, N, K) in SPLIT_WITH_WORKSPACE), "the schedule this shape is meant to take"
     ref = binding.w8a16_gemm_ws(A, dW, dS, ws) if with_workspace else binding.w8a16_gemm(A, dW, dS)
     torch.cuda.synchronize()
     out = torch.empty_like(ref)

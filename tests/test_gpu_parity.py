@@ -140,25 +140,23 @@ def test_gemv_k_edges(dev, M, N, K):
 # --- GEMM ------------------------------------------------------------------------
 
 # Paths of the GEMM entry (w8a16_gemm, which computes every tile whole in one
-# workgroup and uses no workspace). M <= 64 takes the skinny kernel's one-shot
-# form (one 16-row weight block per workgroup, activations in LDS, in phases
-# of part of K) where its plan fits: every weight block on a CU of its own
-# (N <= 16 * CUs: here N = 130..4100 with M up to 64), or more blocks than
-# CUs with at most 16 rows and 64 KB of activations (N = 140000 / 166400 with
-# M = 3 / 5, N = 4100 with M = 2). Otherwise M <= 16 with
-# K <= 4096 (M >= 12: K <= 8192) takes its ring form (16-row weight blocks,
-# K split over 16 waves, ring of 2 blocks per wave, several blocks per
-# workgroup; M = 16, N = 18560, K = 4096). Otherwise the tiles are 32 x 128
-# for M <= 32 (N = 18560 at M = 32; M = 7 with K = 8208, past the one-shot
-# form's 64 k-blocks), 64 x 128 for M <= 64 (N = 18560, 98400
-# at M = 48, 40) and 128 x 128 above; 128 x 128 tiles numbering 192..256 (on
-# 256 CUs) with K a multiple of 256 split their k-steps between two wave
-# groups of one workgroup (M = 200, N = 12200, K = 1280: ragged M and N, 10
-# k-steps per group; M = 256, N = 12288, K = 512: 4 per group). The shapes
-# span few tiles, more tiles than one round of the grid (N = 65704, 78339,
-# 89603 with 65 <= M <= 128) and ragged M, N and K tails. The one-shot form,
-# the 256 x 256 tiles and the split schedules of w8a16_gemm_ws have their own
-# tests (test_gpu_skinny.py, test_gpu_wide.py, below).
+# workgroup and uses no workspace). M <= 16 takes the skinny kernel: its
+# one-shot form (one 16-row weight block per workgroup, activations in LDS)
+# where its plan fits (every weight block on a CU of its own: N = 130..4100
+# here; more blocks than CUs with 64 KB of activations or less: N = 140000 /
+# 166400 with M = 3 / 5, N = 4100 with M = 2), else its ring form (M = 16,
+# N = 18560, K = 4096). 17 <= M <= 256 with K <= 32768 takes the mid-size
+# kernel (small tiles, one per workgroup; every tile shape of it in
+# test_gpu_mid.py): here ragged M, N and K, K below one stage, several rounds
+# of tiles over the CUs (N = 65704, 78339, 89603, 98400). Past those, the
+# tiles are 32 x 128 for M <= 32 and 64 x 128 for M <= 64 (M = 7 with K =
+# 8208 past the one-shot form's 64 k-blocks; M = 20 and 40 with K above
+# 32768), 128 x 128 above (several rounds of them at M = 300, N = 40000);
+# 128 x 128 tiles numbering 192..256 (on 256 CUs) with K a multiple of 256
+# split their k-steps between two wave groups of one workgroup (M = 1000,
+# N = 3000, K = 1280: ragged M and N, 10 k-steps per group). The 256 x 256
+# tiles and the split schedules of w8a16_gemm_ws have their own tests
+# (test_gpu_wide.py, below).
 @pytest.mark.parametrize("M,N,K", [(1, 384, 256), (17, 130, 144), (127, 300, 272), (129, 1000, 1040),
                                    (300, 257, 4096), (256, 256, 128), (1, 1, 16), (64, 4096, 512),
                                    (513, 640, 1024), (130, 18560, 128), (66, 65704, 1040),
@@ -166,7 +164,8 @@ def test_gemv_k_edges(dev, M, N, K):
                                    (3, 140000, 1040), (5, 166400, 528), (33, 1000, 1040), (48, 18560, 2048),
                                    (40, 98400, 528), (31, 300, 4112), (16, 18560, 4096), (9, 1000, 4096),
                                    (7, 1000, 8208), (2, 4100, 1936), (200, 12200, 1280), (256, 12288, 512),
-                                   (130, 38300, 512), (16, 4096, 8192), (13, 1000, 4224), (12, 300, 6160)])
+                                   (130, 38300, 512), (16, 4096, 8192), (13, 1000, 4224), (12, 300, 6160),
+                                   (20, 1000, 36880), (40, 300, 40960), (1000, 3000, 1280), (300, 40000, 272)])
 def test_gemm_every_element(dev, M, N, K):
     say(f"gemm M={M} N={N} K={K}")
     A = inputs.activations(M, K, 900 + M)
@@ -340,9 +339,12 @@ def test_empty_and_rejected_calls(dev, entry):
 
 # Shapes whose tiles split their k-blocks between workgroups when a workspace
 # is given (w8a16_gemm_ws): fewer tiles than slots (32-, 64- and 128-row
-# tiles), a whole round plus a split remainder, and one split tile.
-SPLIT_SHAPES = [(129, 1000, 1040), (300, 257, 4096), (20, 18560, 8192), (48, 18560, 2048), (130, 38300, 512),
-                (66, 65704, 1040), (17, 140000, 1040), (40, 98400, 528), (128, 4096, 8192), (256, 4096, 8192)]
+# tiles; the 32- and 64-row ones with K past the mid-size kernel's 32768),
+# a whole round plus a split remainder (M = 300, N = 33000) and one split
+# tile. (The schedule that fills the whole 64 MiB, M = 384 on the Mamba-2
+# in_proj, runs in test_zz_no_alloc.py.)
+SPLIT_SHAPES = [(300, 1000, 1040), (300, 257, 4096), (512, 2048, 4096), (20, 1000, 36880), (40, 4100, 40960),
+                (300, 33000, 272)]
 
 
 @pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
@@ -364,12 +366,13 @@ def test_gemm_ws_split_tiles_every_element(dev, M, N, K):
 def test_gemm_ws_on_two_streams_with_two_workspaces(dev):
     """Two split GEMMs run concurrently on two streams, each with its own
     workspace: neither result is disturbed, and repeats agree bit for bit."""
-    shapes = [(129, 1000, 1040, 21), (300, 257, 4096, 22)]
+    shapes = [(300, 1000, 1040, 21), (300, 257, 4096, 22)]
     ops = []
     for M, N, K, seed in shapes:
         A = inputs.activations(M, K, seed)
         W, S = inputs.weights(N, K, 0.02, seed + 100)
         ops.append((A, W, S, *upload(A, W, S, dev), binding.gemm_workspace(M, N, K, dev)))
+        assert ops[-1][-1] is not None, "this shape splits"
     streams = [torch.cuda.Stream(device=dev) for _ in shapes]
     outs = []
     torch.cuda.synchronize()

@@ -6,8 +6,9 @@ the finished fp32 row sum (Qwen3SsmLayer docs,
 `set_fp8_rowwise_prefill_weights`). Every path is covered for each format:
 the GEMV kernels (M <= 3, K > 8192, or K > 4096 below 12 rows), the skinny kernel
 (4 <= M <= 16 via the GEMV entry, M <= 16 via the GEMM entry; K <= 4096, or
-K <= 8192 from 12 rows on), and the GEMM's
-32-, 64- and 128-row tiles with whole and split tiles. Bar as for the BF16
+K <= 8192 from 12 rows on), the mid-size kernel (17 <= M <= 256; more of it in
+test_gpu_mid.py), and the GEMM's 32-, 64- and 128-row tiles (K past 32768, or
+M past 256) and its k-split workgroups. Bar as for the BF16
 grid: |gpu - ref| <= 4e-3 * sum_k |A * Wdeq| + 1e-6 on every element, and
 bit-exact where the answer is unique (an FP32 grid holding BF16 values gives
 the BF16 grid's bits; a power-of-two row scale scales its column's bits).
@@ -71,7 +72,8 @@ GEMV_SHAPES = [(1, 1000, 1040), (1, 18560, 4096), (1, 4096, 8192), (3, 300, 1638
                (4, 1000, 1040), (8, 259, 272), (16, 18560, 4096), (9, 300, 8192), (13, 130, 3072)]
 GEMM_SHAPES = [(1, 384, 256), (16, 1000, 4096), (3, 140000, 1040), (20, 4096, 8192), (31, 300, 4112),
                (33, 1000, 1040), (40, 98400, 528), (129, 1000, 1040), (300, 257, 4096), (66, 65704, 1040),
-               (65, 89603, 1040), (513, 640, 1024), (200, 12200, 1280)]
+               (65, 89603, 1040), (513, 640, 1024), (200, 12200, 1280), (20, 1000, 36880), (40, 300, 40960),
+               (768, 4096, 256)]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -115,7 +117,7 @@ def test_prefill_1k_in_proj_sampled(dev, fmt):
 ALL_PATHS = [("gemv", 1, 1000, 1040), ("gemv", 3, 300, 8192), ("gemv", 8, 1000, 1040), ("gemm", 16, 1000, 2048),
              ("gemm", 24, 4096, 8192), ("gemm", 50, 1000, 1040), ("gemm", 200, 1000, 1040),
              ("gemm", 72, 78339, 1040), ("gemm", 256, 12288, 512),
-             ("gemm", 12, 300, 6160)]
+             ("gemm", 12, 300, 6160), ("gemm", 20, 1000, 36880), ("gemm", 768, 4096, 256), ("gemm", 300, 1000, 1040)]
 ENTRY = {"gemv": binding.w8a16_gemv, "gemm": binding.w8a16_gemm}
 
 
