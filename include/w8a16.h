@@ -107,26 +107,34 @@ int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
  * the skinny case of a few tokens (speculative verify, batched decode).
  * M >= 0 (any), N >= 0, 16 <= K < 2^23, K % 16 == 0; M == 0 or N == 0 is a
  * no-op. Paths, chosen by M, N, K and the device's CU count only:
- *  - skinny (one kernel, no workspace; the weights stream from HBM straight
- *    into the matrix-core operands, each 16-row weight block read once for
- *    all M rows): M <= 64 with K <= 8192 where one workgroup per 16-row
- *    block fits (the activations, in LDS, copied in up to 8 parts of K;
- *    above 16 rows only when N <= 16 * CUs); else M <= 16 with K <= 4096, or
- *    12 <= M <= 16 with K <= 8192, with workgroups walking several blocks;
- *  - M >= 65 where 256 x 256 output tiles fill every round of CU-many tiles
- *    to at least 85 % (e.g. the 8192-token prefill): one workgroup per CU
- *    walks those tiles; each weight is converted once per tile as
- *    bf16(e * s), the block scale folded in (e * s is exact in fp32, rounded
- *    once), and the matrix cores accumulate over the whole K range; where
- *    they cover at least one whole round but leave a sparse one (the
+ *  - mid-size, 17 <= M <= 256 with K <= 32768 (one kernel, no workspace):
+ *    one workgroup per output tile of 16 to 128 rows by 32 to 160 columns,
+ *    the tile chosen so that the tiles about fill the CUs; its rows of A and
+ *    its weight bytes stream into LDS, the waves split each stage's k and
+ *    add their fp32 partial tiles in LDS in a fixed order, and the block
+ *    scale multiplies each wave's fp32 partial sum over its part of a
+ *    128-wide k-block;
+ *  - skinny, M <= 16 (one kernel, no workspace; the weights stream from HBM
+ *    straight into the matrix-core operands, each 16-row weight block read
+ *    once for all M rows): K <= 8192 where one workgroup per 16-row block
+ *    fits (the activations, in LDS, copied in up to 8 parts of K); else
+ *    K <= 4096, or 12 <= M <= 16 with K <= 8192, with workgroups walking
+ *    several blocks;
+ *  - otherwise, M >= 65 where 256 x 256 output tiles fill every round of
+ *    CU-many tiles to at least 85 % (e.g. the 8192-token prefill): one
+ *    workgroup per CU walks those tiles; each weight is converted once per
+ *    tile as bf16(e * s), the block scale folded in (e * s is exact in fp32,
+ *    rounded once), and the matrix cores accumulate over the whole K range;
+ *    where they cover at least one whole round but leave a sparse one (the
  *    1024-token in_proj), whole rounds of them take the first columns and
  *    the tiles below the rest;
- *  - otherwise output tiles of 32 (M <= 32), 64 (M <= 64) or 128 rows by 128
- *    columns: the E4M3 weight bytes of a tile are staged once per workgroup
- *    and decoded in registers, and the block scale multiplies each 128-wide
- *    k-block's fp32 partial sum. 128-row tiles numbering between three
- *    quarters of the CUs and the CUs split their k-range between two halves
- *    of one workgroup, added in LDS. Every tile is computed whole by one
+ *  - otherwise output tiles of 32 (M <= 32), 64 (M <= 64; these two only
+ *    for K past the mid-size kernel's) or 128 rows by 128 columns: the E4M3
+ *    weight bytes of a tile are staged once per workgroup and decoded in
+ *    registers, and the block scale multiplies each 128-wide k-block's fp32
+ *    partial sum. 128-row tiles numbering between three quarters of the
+ *    CUs and the CUs split their k-range between two halves of one
+ *    workgroup, added in LDS. Every tile is computed whole by one
  *    workgroup: w8a16_gemm needs no workspace and allocates nothing (it may
  *    be captured in a HIP graph on any stream).
  * Every choice depends only on M, N, K and the device's compute-unit count,
@@ -153,8 +161,8 @@ int w8a16_gemm_ex(const void* A, const void* Wq, const void* scale, int scale_fo
 /*
  * The GEMM with a caller-supplied workspace, for shapes whose 32-, 64- or
  * 128-row tiles do not fill the GPU (fewer tiles than it holds at once, or a
- * last wave less than a quarter full; typically a few dozen to a few hundred
- * tokens against weights with few rows, like the Mamba-2 out_proj): the
+ * last wave less than a quarter full; e.g. a few hundred tokens against
+ * weights with few rows, or a few dozen tokens with K past 32768): the
  * k-blocks of the remaining tiles are then split between workgroups, whose
  * fp32 partial tiles go to the workspace, and a second kernel enqueued on the
  * same stream adds them in k order (deterministic: the split depends only on
