@@ -31,7 +31,9 @@
 //    ways) and each stage's k (KQ ways): each weight is decoded by MQ waves
 //    (the exact packed convert), v_mfma_f32_16x16x32_bf16 does the products,
 //    and the block scale is applied exactly in fp32 (acc += s * blk over the
-//    wave's part of each scale block; the scales come by scalar loads);
+//    wave's part of each scale block; the tile's scale rows are copied
+//    into LDS once, by DMA ahead of the first stage, so that inside the
+//    loop every wait on LDS is an exact count);
 //  * a wave reads the next stage's operands from LDS into registers while
 //    its MFMAs work on the current stage's (the stage's work is small next
 //    to the latency of a barrier, an LDS read and an MFMA chain, which
@@ -97,7 +99,11 @@ struct MidCfg {
     static constexpr int kRing = STAGES * kStageBytes;
     static constexpr int kPartBytes = KQ * TM * TN * 4;
     static constexpr int kMain = kRing > kPartBytes ? kRing : kPartBytes;
-    static constexpr int kLds = kMain + 1024;
+    // Rows of the scale grid that TN consecutive columns can span, and the
+    // LDS that holds them for K up to kMidMaxK (fp32-sized entries).
+    static constexpr int kScaleRows = (TN - 1 + kScaleBlock - 1) / kScaleBlock + 1;
+    static constexpr int kScaleTable = kScaleRows * static_cast<int>(kMidMaxK / kScaleBlock) * 4;
+    static constexpr int kLds = kMain + 1024 + kScaleTable;
     static constexpr int MBW = MB / MQ, NBW = NB / NQ, KW = KS / KQ, kSteps = KW / 32;
     static constexpr int kStepsPerBlock = kSteps < 4 ? kSteps : 4;       // MFMA steps of a wave per scale block
     static_assert(KS == 128 || KS == 256, "one or two scale blocks per stage");
@@ -118,24 +124,6 @@ __device__ __forceinline__ int w_pos(int r, int c) {
     return r * KS + ((c ^ (KS == 128 ? (r >> 1) & 7 : r & 15)) << 4);
 }
 
-// Block scale `idx` of the grid in format SF, for an index that is the same
-// in every lane: a scalar load (through the constant address space), which
-// the vector-memory counter does not see, so it never waits on, or makes
-// anything wait on, the DMA in flight. A BF16 scale is read as the aligned
-// dword that holds it (which cannot cross a page).
-typedef __attribute__((address_space(4))) const uint32_t const_u32;
-template <int SF>
-__device__ __forceinline__ float scale_uniform(const void* S, int64_t idx) {
-    if constexpr (SF == kScaleBlockBf16) {
-        const uintptr_t a = reinterpret_cast<uintptr_t>(S) + static_cast<uintptr_t>(idx) * 2;
-        const uint32_t v = *reinterpret_cast<const_u32*>(a & ~static_cast<uintptr_t>(3));
-        return __uint_as_float((a & 2) ? (v & 0xFFFF0000u) : (v << 16));
-    } else {
-        const uintptr_t a = reinterpret_cast<uintptr_t>(S) + static_cast<uintptr_t>(idx) * 4;
-        return __uint_as_float(*reinterpret_cast<const_u32*>(a));
-    }
-}
-
 // 8 E4M3 codes (two dwords) -> 8 BF16, exact.
 __device__ __forceinline__ bf16x8_t e4m3x8(uint32_t lo, uint32_t hi) {
     const bf16x2_t p0 = e4m3x2_to_bf16(lo, false), p1 = e4m3x2_to_bf16(lo, true);
@@ -152,6 +140,38 @@ struct MidOps {
     float s[C::NBW][C::kSteps / C::kStepsPerBlock];
 };
 
+// The finished fp32 sums of columns n .. n + 3 of output row m (n < N):
+// the per-row scale (FP32 row format), BF16, the residual (out = bf16(res +
+// bf16(sum)), nemotron_mamba2.rs module docs, forward step 8), and the store
+// (8 bytes at once where `vec` says out and res allow it).
+template <int SF, bool RES>
+__device__ __forceinline__ void mid_store4(f32x4_t sum, const void* __restrict__ S, const uint16_t* __restrict__ res,
+                                           uint16_t* __restrict__ out, int m, int n, int N, int64_t ldo, bool vec) {
+    const int64_t o = static_cast<int64_t>(m) * ldo + n;
+    uint16_t y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float v = sum[e];
+        if constexpr (SF == kScaleRowF32) v *= n + e < N ? row_scale<SF>(S, n + e) : 0.0f;
+        y[e] = f32_to_bf16_bits(v);
+    }
+    if (vec && n + 4 <= N) {
+        if constexpr (RES) {
+            const uint2 rv = *reinterpret_cast<const uint2*>(res + o);
+            y[0] = residual_add_bits(y[0], rv.x & 0xFFFFu);
+            y[1] = residual_add_bits(y[1], rv.x >> 16);
+            y[2] = residual_add_bits(y[2], rv.y & 0xFFFFu);
+            y[3] = residual_add_bits(y[3], rv.y >> 16);
+        }
+        *reinterpret_cast<uint2*>(out + o) =
+            make_uint2(y[0] | (static_cast<uint32_t>(y[1]) << 16), y[2] | (static_cast<uint32_t>(y[3]) << 16));
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < N) out[o + e] = RES ? residual_add_bits(y[e], res[o + e]) : y[e];
+    }
+}
+
 // Scale format SF; residual epilogue when RES (out = bf16(res + bf16(sum)),
 // nemotron_mamba2.rs module docs, forward step 8); `ldo`: the row stride of
 // out and res, in elements.
@@ -163,10 +183,12 @@ __device__ __forceinline__ void mid_body(const uint16_t* __restrict__ A, const u
     constexpr int TM = C::TM, TN = C::TN, MBW = C::MBW, NBW = C::NBW, KW = C::KW, KS = C::KS;
     constexpr int STAGES = C::STAGES, kStage = C::kStageBytes, kLoads = C::kLoads;
     constexpr int kSteps = C::kSteps, kSpb = C::kStepsPerBlock, kBlocks = kSteps / kSpb;
-    // One LDS array: the ring (afterwards the partial tiles) and a 1 KB pad
-    // that takes the loads of waves with no chunk left in a stage.
+    // One LDS array: the ring (afterwards the partial tiles), a 1 KB pad
+    // that takes the loads of waves with no chunk left in a stage, and the
+    // tile's block scales.
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
     uint8_t* const pad = lds + C::kMain;
+    uint8_t* const stab = lds + C::kMain + 1024;
 
     const int t = mid_xcd_remap(blockIdx.x, gridDim.x);
     const int tm = t % tiles_m, tn = t / tiles_m;
@@ -255,18 +277,54 @@ __device__ __forceinline__ void mid_body(const uint16_t* __restrict__ A, const u
         for (int j = 0; j < NBW; ++j)
             w_addr[j][s] = C::kABytes + w_pos<KS>((nq * NBW + j) * 16 + r, k / 16) + (k % 16);
     }
-    // Scale rows of the wave's column blocks (a block past N reads row j0:
-    // its weights are zero), and the wave's first scale block in a stage.
+    // The tile's block scales, an fp32 table [row - j0][k-block] in LDS for
+    // rows j0 .. j1 of the grid. Those rows lie one after another in memory;
+    // they are copied once by DMA, as the dwords from the 4-byte boundary at
+    // or below the first scale (a dword that holds a scale cannot cross a
+    // page): FP32 straight into the table, BF16 into the ring's last slot
+    // (free until the prologue refills it), from where the prologue widens
+    // them into the table. Every wave issues kScaleLoads 256-byte loads
+    // (past the copy: the pad, reading nothing), so the DMA counts stay the
+    // same in every wave; they go before the ring's first stages, so the
+    // wait for stage 0 covers them.
+    constexpr bool kBf16Scale = SF == kScaleBlockBf16;
+    constexpr int kEsz = kBf16Scale ? 2 : 4;
+    constexpr int kScaleLoads =
+        kRowScale ? 0 : (C::kScaleTable / (kEsz == 4 ? 1 : 2) + 4 + 255) / 256 / kMidWaves + 1;
+    static_assert(kRowScale || C::kScaleTable / 2 + 256 + 4 <= kStage, "the BF16 copy fits a ring slot");
+    const int j1 = min((n0 + TN - 1) / kScaleBlock, (N - 1) / kScaleBlock);
+    const int n_scales = (j1 - j0 + 1) * k_blocks;
+    uint8_t* const s_raw = kBf16Scale ? lds + (STAGES - 1) * kStage : stab;
+    int s_lead = 0;
+    if constexpr (!kRowScale) {
+        const uintptr_t first = reinterpret_cast<uintptr_t>(S) + static_cast<uintptr_t>(j0) * k_blocks * kEsz;
+        s_lead = static_cast<int>(first & 3);
+        const int nrec = (s_lead + n_scales * kEsz + 3) & ~3;
+        const int n_instr = (nrec + 255) / 256;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void*>(first - s_lead), 0, nrec, kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < kScaleLoads; ++i) {
+            const int q = wave + kMidWaves * i;                                // uniform
+            const bool real = q < n_instr;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(real ? s_raw + q * 256 : pad), 4, lane * 4,
+                                                     real ? q * 256 : kPastEnd, 0, 0);
+        }
+    }
+    // The table byte of each of the wave's column blocks' scale row (a block
+    // past N reads row j0: its weights are zero), and the wave's first scale
+    // block in a stage.
     int srow[NBW];
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
         const int n = n0 + (nq * NBW + j) * 16;
-        srow[j] = n < N ? n / kScaleBlock : j0;
+        srow[j] = ((n < N ? n / kScaleBlock : j0) - j0) * k_blocks * 4;
     }
     const int kb_wave = (kq * KW) / kScaleBlock;
 
     // The wave's operands of stage st from ring slot `slot`, and its scales
-    // (a scale block past K reads the last one: its products are zero).
+    // from the table (a scale block past K reads the last one: its products
+    // are zero).
     auto read_ops = [&](int st, int slot, MidOps<C>& o) __attribute__((always_inline)) {
         const uint8_t* const base = lds + slot * kStage;
 #pragma unroll
@@ -284,8 +342,7 @@ __device__ __forceinline__ void mid_body(const uint16_t* __restrict__ A, const u
             for (int b = 0; b < kBlocks; ++b) {
                 const int kb = min(st * (KS / kScaleBlock) + kb_wave + b, k_blocks - 1);
 #pragma unroll
-                for (int j = 0; j < NBW; ++j)
-                    o.s[j][b] = scale_uniform<SF>(S, static_cast<int64_t>(srow[j]) * k_blocks + kb);
+                for (int j = 0; j < NBW; ++j) o.s[j][b] = *reinterpret_cast<const float*>(stab + srow[j] + kb * 4);
             }
         }
     };
@@ -339,8 +396,19 @@ __device__ __forceinline__ void mid_body(const uint16_t* __restrict__ A, const u
 #pragma unroll
     for (int sl = 0; sl + 1 < STAGES; ++sl) issue(sl, sl);
     MidOps<C> ops0, ops1;
+    constexpr int kOpsRegs = MBW * kSteps * 4 + NBW * kSteps * 2 + NBW * kBlocks;
+    constexpr bool kPinReads = 2 * kOpsRegs + 8 * MBW * NBW <= 200;
     wait_vmem<(STAGES - 2) * kLoads>();
     lds_barrier();
+    if constexpr (kBf16Scale) {
+        // BF16 -> fp32 is exact: the BF16 bits become the high half.
+        for (int e = threadIdx.x; e < n_scales; e += kMidThreads)
+            reinterpret_cast<float*>(stab)[e] =
+                __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(s_raw + s_lead + 2 * e))
+                                << 16);
+        __builtin_amdgcn_s_waitcnt(0xC07F);                                // lgkmcnt(0): the table is written
+        lds_barrier();
+    }
     read_ops(0, 0, ops0);
     issue(STAGES - 1, STAGES - 1);
     auto step = [&](int st, int slot, const MidOps<C>& cur, MidOps<C>& nxt) __attribute__((always_inline)) {
@@ -353,6 +421,10 @@ __device__ __forceinline__ void mid_body(const uint16_t* __restrict__ A, const u
         // used: a branch here makes the compiler wait for these reads
         // before the MFMAs below)
         read_ops(st + 1, nslot, nxt);
+        // Kept ahead of the products where the registers allow (the
+        // scheduler would otherwise sink the reads below them, and their
+        // latency would then show at the next barrier).
+        if constexpr (kPinReads) __builtin_amdgcn_sched_barrier(0);
         compute(cur);
         return nslot;
     };
@@ -386,29 +458,7 @@ __device__ __forceinline__ void mid_body(const uint16_t* __restrict__ A, const u
         f32x4_t sum = *reinterpret_cast<const f32x4_t*>(part + row * TN + col);
 #pragma unroll
         for (int k2 = 1; k2 < C::KQ; ++k2) sum += *reinterpret_cast<const f32x4_t*>(part + (k2 * TM + row) * TN + col);
-        const int64_t o = static_cast<int64_t>(m) * ldo + n;
-        uint16_t y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float v = sum[e];
-            if constexpr (kRowScale) v *= n + e < N ? row_scale<SF>(S, n + e) : 0.0f;
-            y[e] = f32_to_bf16_bits(v);
-        }
-        if (vec && n + 4 <= N) {
-            if constexpr (RES) {
-                const uint2 rv = *reinterpret_cast<const uint2*>(res + o);
-                y[0] = residual_add_bits(y[0], rv.x & 0xFFFFu);
-                y[1] = residual_add_bits(y[1], rv.x >> 16);
-                y[2] = residual_add_bits(y[2], rv.y & 0xFFFFu);
-                y[3] = residual_add_bits(y[3], rv.y >> 16);
-            }
-            *reinterpret_cast<uint2*>(out + o) = make_uint2(y[0] | (static_cast<uint32_t>(y[1]) << 16),
-                                                            y[2] | (static_cast<uint32_t>(y[3]) << 16));
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (n + e < N) out[o + e] = RES ? residual_add_bits(y[e], res[o + e]) : y[e];
-        }
+        mid_store4<SF, RES>(sum, S, res, out, m, n, N, ldo, vec);
     }
 }
 
