@@ -90,6 +90,42 @@ def test_mid_every_element(dev, M, N, K):
     assert_within_tol(got, ref, den, f"M={M} N={N} K={K}")
 
 
+# Edges: K = 16 (one stage, one k-chunk), N = 1, the largest K at the fewest
+# and the most rows, every dimension ragged.
+EDGE_SHAPES = [(20, 50, 16), (256, 1, 32768), (17, 16, 32768), (255, 129, 4112), (200, 3, 48)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
+def test_mid_edges_every_element(dev, M, N, K):
+    say(f"mid-size gemm edge M={M} N={N} K={K}")
+    A = inputs.activations(M, K, 7100 + M)
+    W, S = inputs.weights(N, K, 0.02, 7200 + N + K)
+    out = binding.w8a16_gemm(to_dev(A, torch.bfloat16, dev), to_dev(W, torch.uint8, dev),
+                             to_dev(S, torch.bfloat16, dev))
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(bits(out), ref, den, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(129, 1000, 1040), (64, 4096, 8192)])
+def test_mid_scale_grid_at_two_byte_offset(dev, M, N, K):
+    """A BF16 scale grid that starts 2 bytes past a 4-byte boundary (a view at
+    an odd element offset): the kernel copies the grid rows as aligned dwords,
+    so the bits must equal those from an aligned copy of the same grid."""
+    say(f"mid-size gemm, scale grid at offset 2, M={M} N={N} K={K}")
+    A = inputs.activations(M, K, 7300 + M)
+    W, S = inputs.weights(N, K, 0.02, 7400 + K)
+    dA, dW, dS = to_dev(A, torch.bfloat16, dev), to_dev(W, torch.uint8, dev), to_dev(S, torch.bfloat16, dev)
+    store = torch.zeros(dS.numel() + 1, dtype=torch.bfloat16, device=dev)
+    shifted = store[1:].view(dS.shape)
+    shifted.copy_(dS)
+    assert shifted.data_ptr() % 4 == 2
+    aligned = bits(binding.w8a16_gemm(dA, dW, dS))
+    odd = bits(binding.w8a16_gemm(dA, dW, shifted))
+    assert np.array_equal(aligned, odd)
+    ref, den = oracle.w8a16(A, W, S)
+    assert_within_tol(odd, ref, den, f"offset grid M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(17, 130, 144), (128, 4096, 8192), (64, 18560, 4096), (66, 65704, 1040)])
 def test_mid_residual_epilogue_bits(dev, M, N, K):
     """out = bf16(residual + y) exactly, y = the same GEMM without the residual."""
