@@ -58,7 +58,7 @@ __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// MB = 16-row blocks of A (1 for M <= 16, 2 for M <= 32); KB = k-blocks per
+// MB = 16-row blocks of A (the entry points use 1: M <= 16); KB = k-blocks per
 // wave at most (the activations of KB k-blocks take 16 * MB * KB VGPRs); D =
 // weight blocks in flight per wave; MAXW = waves per workgroup at most; SF =
 // scale format; NPASS = passes over K (1 or 2): in pass p, wave w owns the
