@@ -82,7 +82,7 @@ def _load():
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_rmsnorm.restype = None
-    lib.oracle_rmsnorm.argtypes = [P, P, P, ctypes.c_double, I64, I64, P, P]
+    lib.oracle_rmsnorm.argtypes = [P, P, P, ctypes.c_double, I64, I64, I64, P, P]
     lib.oracle_residual_add.restype = None
     lib.oracle_residual_add.argtypes = [P, P, I64, P]
     D = ctypes.c_double
@@ -217,16 +217,19 @@ def silu(z: float) -> float:
     return float(_load().oracle_silu(float(z)))
 
 
-def rmsnorm(x, weight, eps: float, gate=None) -> tuple[np.ndarray, np.ndarray]:
-    """Row-wise RMSNorm of BF16 x [M, K] times BF16 weight [K] (times silu(gate)).
+def rmsnorm(x, weight, eps: float, gate=None, group=None) -> tuple[np.ndarray, np.ndarray]:
+    """RMSNorm of BF16 x [M, K] times BF16 weight [K] (times silu(gate)), over
+    consecutive groups of `group` channels of each row (None: the whole row).
 
-    Returns (exact fp64 values [M, K], their BF16 bits [M, K]); the norm is
-    one over each whole row (nemotron_mamba2.rs module docs, forward steps 1
-    and 6)."""
+    Returns (exact fp64 values [M, K], their BF16 bits [M, K])
+    (nemotron_mamba2.rs module docs, forward steps 1 and 6)."""
     x = _c(x, np.uint16)
     w = _c(weight, np.uint16)
     if x.ndim != 2 or w.shape != (x.shape[1],):
         raise ValueError(f"x must be [M, K] and weight [K], got {x.shape} and {w.shape}")
+    G = x.shape[1] if group is None else int(group)
+    if G < 1 or x.shape[1] % G != 0:
+        raise ValueError(f"group must divide K = {x.shape[1]}, got {group}")
     g = None
     if gate is not None:
         g = _c(gate, np.uint16)
@@ -235,7 +238,7 @@ def rmsnorm(x, weight, eps: float, gate=None) -> tuple[np.ndarray, np.ndarray]:
     M, K = x.shape
     exact = np.empty((M, K), np.float64)
     bits = np.empty((M, K), np.uint16)
-    _load().oracle_rmsnorm(_ptr(x), _ptr(g) if g is not None else None, _ptr(w), float(eps), M, K,
+    _load().oracle_rmsnorm(_ptr(x), _ptr(g) if g is not None else None, _ptr(w), float(eps), G, M, K,
                            _ptr(exact), _ptr(bits))
     return exact, bits
 

@@ -201,17 +201,20 @@ void oracle_w8a16_points(const uint16_t* A, const uint8_t* W, const uint16_t* S,
  * Mamba-2 layer's forward steps in the nemotron_mamba2.rs module docs: step 1,
  * RMS norm scaled by its weight, before in_proj; step 6, the gated norm
  * rms_norm(y, ssm_norm) * silu(z), before out_proj; step 8, the residual add
- * after out_proj). The pages give neither epsilon nor the norm's grouping; the
- * reading taken here is one norm over the whole row of K values, with epsilon
- * an argument.
+ * after out_proj). The pages give neither epsilon nor the norm's grouping, so
+ * both are arguments: the norm runs over consecutive groups of `group`
+ * channels of each row (group = K: one norm over the whole row, the plain
+ * reading of rms_norm(y, ssm_norm); group = K / n_groups: the published
+ * Mamba-2 gated norm, one norm per group of channels). For channel k in
+ * group g = k / group:
  *
- *   r        = 1 / sqrt( (sum_k x[k]^2) / K + eps )
- *   v[k]     = x[k] * r * weight[k]                  (RMSNorm)
- *   v[k]     = x[k] * r * weight[k] * silu(z[k])     (gated RMSNorm)
+ *   r_g      = 1 / sqrt( (sum_{k' in g} x[k']^2) / group + eps )
+ *   v[k]     = x[k] * r_g * weight[k]                  (RMSNorm)
+ *   v[k]     = x[k] * r_g * weight[k] * silu(z[k])     (gated RMSNorm)
  *   silu(z)  = z / (1 + exp(-z))
  *
  * computed in fp64; `exact` receives v and `bits` its BF16 rounding (the
- * activation the projection then reads).
+ * activation the projection then reads). group must divide K.
  */
 double oracle_silu(double z)
 {
@@ -219,22 +222,24 @@ double oracle_silu(double z)
 }
 
 void oracle_rmsnorm(const uint16_t* x, const uint16_t* gate, const uint16_t* weight, double eps,
-                    int64_t M, int64_t K, double* exact, uint16_t* bits)
+                    int64_t group, int64_t M, int64_t K, double* exact, uint16_t* bits)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
-        double ss = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            double v = oracle_bf16_value(x[m * K + k]);
-            ss += v * v;
-        }
-        double r = 1.0 / sqrt(ss / (double)K + eps);
-        for (int64_t k = 0; k < K; ++k) {
-            double v = oracle_bf16_value(x[m * K + k]) * r * oracle_bf16_value(weight[k]);
-            if (gate)
-                v *= oracle_silu(oracle_bf16_value(gate[m * K + k]));
-            exact[m * K + k] = v;
-            bits[m * K + k] = oracle_bf16_rne(v);
+        for (int64_t g0 = 0; g0 < K; g0 += group) {
+            double ss = 0.0;
+            for (int64_t k = g0; k < g0 + group; ++k) {
+                double v = oracle_bf16_value(x[m * K + k]);
+                ss += v * v;
+            }
+            double r = 1.0 / sqrt(ss / (double)group + eps);
+            for (int64_t k = g0; k < g0 + group; ++k) {
+                double v = oracle_bf16_value(x[m * K + k]) * r * oracle_bf16_value(weight[k]);
+                if (gate)
+                    v *= oracle_silu(oracle_bf16_value(gate[m * K + k]));
+                exact[m * K + k] = v;
+                bits[m * K + k] = oracle_bf16_rne(v);
+            }
         }
     }
 }

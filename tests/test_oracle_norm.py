@@ -37,6 +37,52 @@ def test_matches_torch_float64(M, K, gated):
     assert np.array_equal(bits, oracle.bf16_rne(exact))
 
 
+@pytest.mark.parametrize("M,K,G", [(2, 8192, 1024), (3, 4096, 2048), (1, 16384, 1024), (4, 2048, 2048),
+                                   (2, 272, 16)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_grouped_matches_torch_float64(M, K, G, gated):
+    """The grouped norm is torch's RMSNorm over each group of G channels (the
+    row reshaped to [K / G, G]), then the per-channel weight (and gate)."""
+    x = inputs.activations(M, K, 21 + K + G)
+    w = inputs.norm_weight(K, 22 + K)
+    z = inputs.activations(M, K, 23 + K) if gated else None
+    eps = inputs.NORM_EPS
+    exact, bits = oracle.rmsnorm(x, w, eps, gate=z, group=G)
+    xt = bf16_to_f64(x).reshape(M, K // G, G)
+    want = torch.nn.functional.rms_norm(xt, (G,), eps=eps).reshape(M, K) * bf16_to_f64(w)
+    if gated:
+        want = want * torch.nn.functional.silu(bf16_to_f64(z))
+    want = want.numpy()
+    assert np.all(np.abs(exact - want) <= 1e-13 * np.abs(want) + 1e-300)
+    assert np.array_equal(bits, oracle.bf16_rne(exact))
+
+
+def test_grouped_norm_whole_row_and_group_independence():
+    """group = K is the whole-row norm, bit for bit; each group is normalized
+    on its own: at eps = 0 scaling one group of x by a power of two changes
+    no output, and changing another group's values leaves a group's outputs
+    as they were."""
+    M, K, G = 3, 4096, 1024
+    x = inputs.activations(M, K, 31)
+    w = inputs.norm_weight(K, 32)
+    z = inputs.activations(M, K, 33)
+    e_row, b_row = oracle.rmsnorm(x, w, 1e-5, gate=z)
+    e_k, b_k = oracle.rmsnorm(x, w, 1e-5, gate=z, group=K)
+    assert np.array_equal(b_row, b_k) and np.array_equal(e_row, e_k)
+    e0, _ = oracle.rmsnorm(x, w, 0.0, gate=z, group=G)
+    xs = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16)
+    xs[:, G:2 * G] *= 4.0                                  # exact in BF16
+    x2 = xs.view(torch.int16).numpy().view(np.uint16)
+    e1, _ = oracle.rmsnorm(x2, w, 0.0, gate=z, group=G)
+    assert np.array_equal(e0, e1)
+    x3 = x.copy()
+    x3[:, 3 * G:] = inputs.activations(M, G, 34)
+    e3, _ = oracle.rmsnorm(x3, w, 1e-5, gate=z, group=G)
+    e4, _ = oracle.rmsnorm(x, w, 1e-5, gate=z, group=G)
+    assert np.array_equal(e3[:, :3 * G], e4[:, :3 * G])
+    assert not np.array_equal(e_row, e4)                   # the grouping matters
+
+
 def test_silu_matches_torch_and_identities():
     z = np.concatenate([np.linspace(-30, 30, 2001), [0.0, 1e-8, -1e-8, 80.0, -80.0]])
     got = np.array([oracle.silu(v) for v in z])
@@ -123,3 +169,5 @@ def test_norm_contract():
         oracle.rmsnorm(x, w, 1e-5, gate=x[:1])
     with pytest.raises(TypeError):
         oracle.rmsnorm(x.astype(np.float32), w, 1e-5)
+    with pytest.raises(ValueError):
+        oracle.rmsnorm(x, w, 1e-5, group=100)
