@@ -86,6 +86,7 @@ CALIBRATION_BYTES = 256 << 20   # the plain copy run with --copy-calibration rea
 # GEMVs, the last is the out_proj's and the others the in_proj's.
 LAUNCHES = ["gemv_in_proj", "gemv_out_proj", "gemm_in_proj", "gemm_out_proj"]
 DEFAULT_LAYERS = 8
+NORM_GROUP = 1024               # the gated norm in groups: Mamba-2 with d_inner 8192 and 8 groups
 
 
 def _kernel_kind(name):
@@ -590,6 +591,11 @@ def layer_ends_report(projs, device, stream, L, check, reps=10):
         check(binding.gemv_fused_raw(y1.data_ptr(), z1.data_ptr(), w_out.data_ptr(), eps, w, s_, r1.data_ptr(),
                                      o_out.data_ptr(), 1, pout.p_dec.N, K_out, sh), "gemv_fused")
 
+    def out_fused_grouped(i):
+        w, s_ = W(pout, i)
+        check(binding.gemv_fused_raw(y1.data_ptr(), z1.data_ptr(), w_out.data_ptr(), eps, w, s_, r1.data_ptr(),
+                                     o_out.data_ptr(), 1, pout.p_dec.N, K_out, sh, group=NORM_GROUP), "gemv_fused")
+
     def out_chain(i):
         w, s_ = W(pout, i)
         check(binding.rmsnorm_raw(y1.data_ptr(), z1.data_ptr(), w_out.data_ptr(), eps, a_out.data_ptr(), 1, K_out,
@@ -613,6 +619,8 @@ def layer_ends_report(projs, device, stream, L, check, reps=10):
            "decode_in_proj": {"fused_norm_gemv": round(timed(in_fused), 2),
                               "rmsnorm_then_gemv": round(timed(in_chain), 2)},
            "decode_out_proj": {"fused_gated_norm_gemv_residual": round(timed(out_fused), 2),
+                               f"fused_gated_norm_{K_out // NORM_GROUP}_groups_gemv_residual":
+                                   round(timed(out_fused_grouped), 2),
                                "rmsnorm_then_gemv_then_add": round(timed(out_chain), 2)}}
 
     # prefill: standalone norms and the residual epilogue at M = 1024
@@ -632,6 +640,10 @@ def layer_ends_report(projs, device, stream, L, check, reps=10):
         check(binding.rmsnorm_raw(yp.data_ptr(), zp.data_ptr(), w_out.data_ptr(), eps, ap_out.data_ptr(), Mp, K_out,
                                   sh), "rmsnorm")
 
+    def norm_out_grouped(i):
+        check(binding.rmsnorm_raw(yp.data_ptr(), zp.data_ptr(), w_out.data_ptr(), eps, ap_out.data_ptr(), Mp, K_out,
+                                  sh, group=NORM_GROUP), "rmsnorm")
+
     def gemm_plain(i):
         w, s_ = W(pout, i)
         check(binding.gemm_raw(ap_out.data_ptr(), w, s_, op.data_ptr(), Mp, pout.p_pre.N, K_out, sh), "gemm")
@@ -648,6 +660,9 @@ def layer_ends_report(projs, device, stream, L, check, reps=10):
                                  "frac": round(b_ni / t_ni / 1e3 / HBM_PEAK_GBS, 4)}
     out["prefill_gated_rmsnorm_out"] = {"us": round(t_no, 2), "GB/s": round(b_no / t_no / 1e3, 1),
                                         "frac": round(b_no / t_no / 1e3 / HBM_PEAK_GBS, 4)}
+    t_ng = timed(norm_out_grouped)
+    out[f"prefill_gated_rmsnorm_out_{K_out // NORM_GROUP}_groups"] = {
+        "us": round(t_ng, 2), "GB/s": round(b_no / t_ng / 1e3, 1), "frac": round(b_no / t_ng / 1e3 / HBM_PEAK_GBS, 4)}
     out["prefill_out_proj_gemm"] = {"plain": round(timed(gemm_plain), 2), "with_residual": round(timed(gemm_res), 2)}
     return out
 

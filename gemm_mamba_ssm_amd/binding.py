@@ -88,9 +88,9 @@ def load() -> ctypes.CDLL:
     lib.w8a16_hbm_read.argtypes = [P, I64, ctypes.c_int, ctypes.c_int, P, P]
     F = ctypes.c_float
     lib.w8a16_rmsnorm.restype = ctypes.c_int
-    lib.w8a16_rmsnorm.argtypes = [P, P, P, F, P, I64, I64, P]
+    lib.w8a16_rmsnorm.argtypes = [P, P, P, F, I64, P, I64, I64, P]
     lib.w8a16_gemv_fused.restype = ctypes.c_int
-    lib.w8a16_gemv_fused.argtypes = [P, P, I64, P, F, P, P, P, P, I64, I64, I64, P]
+    lib.w8a16_gemv_fused.argtypes = [P, P, I64, P, F, I64, P, P, P, P, I64, I64, I64, P]
     lib.w8a16_gemm_residual.restype = ctypes.c_int
     lib.w8a16_gemm_residual.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.w8a16_conv1d_update.restype = ctypes.c_int
@@ -155,14 +155,16 @@ def gemm_ex_raw(A: int, Wq: int, scale: int, scale_format: int, out: int, M: int
     return load().w8a16_gemm_ex(A, Wq, scale, scale_format, out, M, N, K, stream)
 
 
-def rmsnorm_raw(x: int, gate: int, weight: int, eps: float, out: int, M: int, K: int, stream: int = 0) -> int:
-    return load().w8a16_rmsnorm(x, gate or None, weight, eps, out, M, K, stream)
+def rmsnorm_raw(x: int, gate: int, weight: int, eps: float, out: int, M: int, K: int, stream: int = 0,
+                group: int = 0) -> int:
+    return load().w8a16_rmsnorm(x, gate or None, weight, eps, group, out, M, K, stream)
 
 
 def gemv_fused_raw(A: int, gate: int, norm_weight: int, eps: float, Wq: int, scale: int, residual: int,
-                   out: int, M: int, N: int, K: int, stream: int = 0, ld_gate: int | None = None) -> int:
+                   out: int, M: int, N: int, K: int, stream: int = 0, ld_gate: int | None = None,
+                   group: int = 0) -> int:
     return load().w8a16_gemv_fused(A, gate or None, K if ld_gate is None else ld_gate, norm_weight or None, eps,
-                                   Wq, scale, residual or None, out, M, N, K, stream)
+                                   group, Wq, scale, residual or None, out, M, N, K, stream)
 
 
 def gemm_residual_raw(A: int, Wq: int, scale: int, residual: int, out: int, M: int, N: int, K: int,
@@ -388,11 +390,20 @@ def _eps(eps) -> float:
     return e
 
 
+def _group(group, K: int) -> int:
+    g = 0 if group is None else int(group)
+    _need(g in (0, K) or (g > 0 and g % 1024 == 0 and K % g == 0 and K <= 16384),
+          f"group must be K, or a multiple of 1024 dividing K <= 16384, got {group} for K = {K}")
+    return g
+
+
 def w8a16_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, gate: torch.Tensor | None = None,
-                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """bf16(x * rsqrt(mean(x^2) + eps) * weight [* silu(gate)]) per row of x [M, K] (BF16)."""
+                  out: torch.Tensor | None = None, stream=None, group: int | None = None) -> torch.Tensor:
+    """bf16(x * rsqrt(mean(x^2) + eps) * weight [* silu(gate)]) per row of x [M, K] (BF16), the mean
+    over each group of `group` channels (None: the whole row)."""
     _need(x.dim() == 2, f"x must be [M, K], got shape {tuple(x.shape)}")
     M, K = x.shape
+    grp = _group(group, K)
     _check_bf16(x, "x", (M, K))
     _check_bf16(weight, "weight", (K,))
     if gate is not None:
@@ -406,7 +417,7 @@ def w8a16_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, gate: torch
         _check_device(*[t for t in (x, weight, gate, out) if t is not None])
     with torch.cuda.device(x.device):
         st = load().w8a16_rmsnorm(x.data_ptr(), gate.data_ptr() if gate is not None else None, weight.data_ptr(),
-                                  e, out.data_ptr(), M, K, _stream_handle(x.device, stream))
+                                  e, grp, out.data_ptr(), M, K, _stream_handle(x.device, stream))
     if st != OK:
         raise W8A16Error("w8a16_rmsnorm", st)
     return out
@@ -415,9 +426,10 @@ def w8a16_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, gate: torch
 def w8a16_gemv_fused(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
                      norm_weight: torch.Tensor | None = None, eps: float = 1e-5,
                      gate: torch.Tensor | None = None, residual: torch.Tensor | None = None,
-                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Decode GEMV with the norm prologue (norm_weight, optional gate) and the
-    residual epilogue fused: out = [residual +] (norm(A) x dequant(Wq)^T), BF16.
+                     out: torch.Tensor | None = None, stream=None, group: int | None = None) -> torch.Tensor:
+    """Decode GEMV with the norm prologue (norm_weight, optional gate; the norm
+    over groups of `group` channels, None: the whole row) and the residual
+    epilogue fused: out = [residual +] (norm(A) x dequant(Wq)^T), BF16.
     The gate may be a column slice of a wider row-major tensor (z of the
     in_proj output), as long as its rows are contiguous and 16-byte aligned."""
     _need(A.dim() == 2, f"A must be [M, K], got shape {tuple(A.shape)}")
@@ -434,6 +446,7 @@ def w8a16_gemv_fused(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
     if residual is not None:
         _check_bf16(residual, "residual", (M, N))
     e = _eps(eps)
+    grp = _group(group, K) if norm_weight is not None else 0
     _need(M <= FUSED_MAX_M and (K <= GEMV_MAX_K if M > FUSED_MAX_M_LONG_K else K <= GEMV_MAX_K_SMALL_M),
           f"w8a16_gemv_fused takes M <= 4 with K <= {GEMV_MAX_K_SMALL_M} or M <= 8 with K <= {GEMV_MAX_K}, "
           f"got M={M}, K={K} (use w8a16_rmsnorm + w8a16_gemm_residual)")
@@ -446,7 +459,7 @@ def w8a16_gemv_fused(A: torch.Tensor, Wq: torch.Tensor, scale: torch.Tensor,
         _check_device(*ins, out)
     ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     with torch.cuda.device(A.device):
-        st = load().w8a16_gemv_fused(A.data_ptr(), ptr(gate), ld_gate, ptr(norm_weight), e, Wq.data_ptr(),
+        st = load().w8a16_gemv_fused(A.data_ptr(), ptr(gate), ld_gate, ptr(norm_weight), e, grp, Wq.data_ptr(),
                                      scale.data_ptr(), ptr(residual), out.data_ptr(), M, N, K,
                                      _stream_handle(A.device, stream))
     if st != OK:

@@ -139,6 +139,7 @@ struct Fusion {
     const uint16_t* residual;   // [M][N] BF16, or nullptr
     int64_t ld_gate;
     float eps;
+    int group;                  // channels per norm group: K (the whole row) or a multiple of 1024 dividing K
     // conv1d update on output columns [conv_begin, conv_begin + conv_dim)
     // (the in_proj form): FP32 state [M][conv_dim][d_conv], BF16 taps
     // [conv_dim][d_conv] and bias [conv_dim].
@@ -187,7 +188,7 @@ __device__ __forceinline__ u32x4_t norm8(u32x4_t x, u32x4_t w, u32x4_t g, float 
     return o;
 }
 
-// 1 / sqrt(mean of squares + eps) of a row of K values.
+// 1 / sqrt(mean of squares + eps) of K values (a row, or one group of it).
 __device__ __forceinline__ float rms_factor(float sumsq, int K, float eps) {
     return 1.0f / sqrtf(sumsq / static_cast<float>(K) + eps);
 }

@@ -241,27 +241,64 @@ struct NormOps {
 
     __device__ __forceinline__ void apply(uint32_t (&a)[MR][J][8], const Fusion& fu, int K, const int (&kch)[J],
                                           const bool (&kvalid)[J], int lane, int wave, int nwaves) {
+        static_assert(MR * J <= 16, "one LDS slot per row and chunk");
         __shared__ float ssq[kMaxWaves][16];
-        float r[MR];
+        float r[MR][J];
+        const int group = fu.group > 0 ? fu.group : K;
+        if (group == K) {
+            // One norm over the whole row: every chunk of row m shares r.
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            float ss = 0.0f;
+            for (int m = 0; m < MR; ++m) {
+                float ss = 0.0f;
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    ss += sumsq8(u32x4_t{a[m][j][0], a[m][j][1], a[m][j][2], a[m][j][3]});
+                    ss += sumsq8(u32x4_t{a[m][j][4], a[m][j][5], a[m][j][6], a[m][j][7]});
+                }
+                r[m][0] = wave_sum(ss);
+            }
+            if (lane == 0)
+#pragma unroll
+                for (int m = 0; m < MR; ++m) ssq[wave][m] = r[m][0];
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                float t = 0.0f;
+                for (int w = 0; w < nwaves; ++w) t += ssq[w][m];
+#pragma unroll
+                for (int j = 0; j < J; ++j) r[m][j] = rms_factor(t, K, fu.eps);
+            }
+        } else {
+            // In groups (a multiple of kWaveK channels): a wave's chunk j
+            // (kWaveK channels from wave * kWaveK * J + j * kWaveK) lies in one
+            // group; its sum goes to LDS, and each row's group adds the parts
+            // of its chunks in order.
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+                    r[m][j] = wave_sum(sumsq8(u32x4_t{a[m][j][0], a[m][j][1], a[m][j][2], a[m][j][3]}) +
+                                       sumsq8(u32x4_t{a[m][j][4], a[m][j][5], a[m][j][6], a[m][j][7]}));
+            if (lane == 0)
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+#pragma unroll
+                    for (int j = 0; j < J; ++j) ssq[wave][m * J + j] = r[m][j];
+            __syncthreads();
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                ss += sumsq8(u32x4_t{a[m][j][0], a[m][j][1], a[m][j][2], a[m][j][3]});
-                ss += sumsq8(u32x4_t{a[m][j][4], a[m][j][5], a[m][j][6], a[m][j][7]});
+                const int g = (wave * kWaveK * J + j * kWaveK) / group;
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    float t = 0.0f;
+                    for (int w = 0; w < nwaves; ++w)
+                        for (int j2 = 0; j2 < J; ++j2) {
+                            const int ch = w * kWaveK * J + j2 * kWaveK;
+                            if (ch < K && ch / group == g) t += ssq[w][m * J + j2];
+                        }
+                    r[m][j] = rms_factor(t, group, fu.eps);
+                }
             }
-            r[m] = wave_sum(ss);
-        }
-        if (lane == 0)
-#pragma unroll
-            for (int m = 0; m < MR; ++m) ssq[wave][m] = r[m];
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            float t = 0.0f;
-            for (int w = 0; w < nwaves; ++w) t += ssq[w][m];
-            r[m] = rms_factor(t, K, fu.eps);
         }
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -282,12 +319,12 @@ struct NormOps {
                         gl = load16(g);
                         gh = load16(g + 8);
                     }
-                    nl = norm8<true>(xl, wv[j][0], gl, r[m]);
-                    nh = norm8<true>(xh, wv[j][1], gh, r[m]);
+                    nl = norm8<true>(xl, wv[j][0], gl, r[m][j]);
+                    nh = norm8<true>(xh, wv[j][1], gh, r[m][j]);
                 } else {
                     const u32x4_t zero = {0u, 0u, 0u, 0u};
-                    nl = norm8<false>(xl, wv[j][0], zero, r[m]);
-                    nh = norm8<false>(xh, wv[j][1], zero, r[m]);
+                    nl = norm8<false>(xl, wv[j][0], zero, r[m][j]);
+                    nh = norm8<false>(xh, wv[j][1], zero, r[m][j]);
                 }
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
@@ -546,7 +583,7 @@ extern "C" int w8a16_gemv(const void* A, const void* Wq, const void* scale, void
 }
 
 extern "C" int w8a16_gemv_fused(const void* A, const void* gate, int64_t ld_gate, const void* norm_weight, float eps,
-                                const void* Wq, const void* scale, const void* residual, void* out,
+                                int64_t group, const void* Wq, const void* scale, const void* residual, void* out,
                                 int64_t M, int64_t N, int64_t K, void* stream) {
     using namespace w8a16;
     bool noop = false;
@@ -555,6 +592,7 @@ extern "C" int w8a16_gemv_fused(const void* A, const void* gate, int64_t ld_gate
     if (gate && !norm_weight) return W8A16_ERR_ARG;            // a gate belongs to the norm
     if (gate && (ld_gate < K || ld_gate % 8 != 0 || ld_gate > INT32_MAX)) return W8A16_ERR_SHAPE;
     if (norm_weight && (!(eps >= 0.0f) || eps > 3.0e38f)) return W8A16_ERR_ARG;   // also NaN
+    if (norm_weight && !norm_group_valid(group, K)) return W8A16_ERR_SHAPE;
     if (noop) return W8A16_OK;
     if (!fused_fits(M, K)) return W8A16_ERR_SHAPE;
     if (norm_weight && (!aligned(norm_weight, 16) || (gate && !aligned(gate, 16)))) return W8A16_ERR_ALIGN;
@@ -572,6 +610,7 @@ extern "C" int w8a16_gemv_fused(const void* A, const void* gate, int64_t ld_gate
     fu.residual = static_cast<const uint16_t*>(residual);
     fu.ld_gate = gate ? ld_gate : K;
     fu.eps = eps;
+    fu.group = static_cast<int>(group == 0 ? K : group);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (gate) return run_gemv<kScaleBlockBf16, kFuseGated>(A, Wq, scale, out, M, N, K, s, fu);
     if (norm_weight) return run_gemv<kScaleBlockBf16, kFuseNorm>(A, Wq, scale, out, M, N, K, s, fu);

@@ -59,10 +59,19 @@ inline int check_product_args(const void* A, const void* Wq, const void* scale, 
     return W8A16_OK;
 }
 
-// Checks of the norm arguments (w8a16_norm.hip): shapes, eps, NULL,
+// Channels per norm group: 0 or K (the whole row), or a multiple of 1024
+// that divides K with K <= 16384 (each wave's channels then lie in one group,
+// and the groups' sums fit the kernels' LDS).
+constexpr int64_t kNormGroupUnit = 1024, kMaxNormGroups = 16;
+inline bool norm_group_valid(int64_t group, int64_t K) {
+    if (group == 0 || group == K) return true;
+    return group > 0 && group % kNormGroupUnit == 0 && K % group == 0 && K <= kNormGroupUnit * kMaxNormGroups;
+}
+
+// Checks of the norm arguments (w8a16_norm.hip): shapes, eps, group, NULL,
 // 16-byte alignment, and `out` [M][K] overlapping an input.
-int check_norm_args(const void* x, const void* gate, const void* weight, float eps, const void* out,
-                    int64_t M, int64_t K, bool* noop);
+int check_norm_args(const void* x, const void* gate, const void* weight, float eps, int64_t group,
+                    const void* out, int64_t M, int64_t K, bool* noop);
 
 // Skinny GEMM (w8a16_skinny.hip): 1 <= M <= kSkinnyMaxM rows, K <= kSkinnyMaxK, weights
 // streamed from HBM straight into the matrix-core operands. Arguments as for

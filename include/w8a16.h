@@ -224,11 +224,15 @@ int w8a16_hbm_read(const void* buf, int64_t bytes, int threads, int loads_per_la
  * norm scaled by its weight, before in_proj; step 6, the gated norm
  * rms_norm(y, ssm_norm) * silu(z), before out_proj; step 8, the residual add
  * after out_proj). The pages give neither epsilon nor a grouping of the
- * norm: here the norm runs over each whole row of K values and epsilon is an
- * argument (finite, >= 0; anything else returns W8A16_ERR_ARG):
+ * norm, so both are arguments: eps (finite, >= 0; anything else returns
+ * W8A16_ERR_ARG) and group, the channels normalized together: 0 or K for
+ * one norm over each whole row (the plain reading of rms_norm(y, ssm_norm)),
+ * or a multiple of 1024 that divides K, with K <= 16384 (the published
+ * Mamba-2 gated norm: group = K / n_groups); anything else returns
+ * W8A16_ERR_SHAPE. For channel k in group g = k / group:
  *
- *   r[m]    = 1 / sqrt( (sum_k x[m][k]^2) / K + eps )
- *   a[m][k] = bf16( x[m][k] * r[m] * weight[k] [* silu(gate[m][k])] )
+ *   r[m][g] = 1 / sqrt( (sum_{k' in g} x[m][k']^2) / group + eps )
+ *   a[m][k] = bf16( x[m][k] * r[m][g] * weight[k] [* silu(gate[m][k])] )
  *   silu(z) = z / (1 + e^-z)
  *
  * computed in fp32 with one rounding to BF16 at the end. The residual add
@@ -239,14 +243,15 @@ int w8a16_hbm_read(const void* buf, int64_t bytes, int threads, int loads_per_la
  * >= 0, K % 16 == 0, K >= 16. The prefill path: the GEMM then reads `out`.
  * out must not overlap an input (W8A16_ERR_ALIAS).
  */
-int w8a16_rmsnorm(const void* x, const void* gate, const void* weight, float eps, void* out,
+int w8a16_rmsnorm(const void* x, const void* gate, const void* weight, float eps, int64_t group, void* out,
                   int64_t M, int64_t K, void* stream);
 
 /*
  * Decode GEMV with the prologue and epilogue fused (one launch per
  * projection): A is the layer input x (in_proj, norm_weight set, gate NULL)
  * or the SSM output y (out_proj, gate = z); norm_weight NULL means no norm
- * (then gate must be NULL too, else W8A16_ERR_ARG). The gate's rows (K BF16
+ * (then gate must be NULL too, else W8A16_ERR_ARG); eps and group as for
+ * w8a16_rmsnorm (group ignored without a norm). The gate's rows (K BF16
  * each) lie ld_gate elements apart, so z can be read in place from the
  * in_proj output row [z | xBC | dt] (ld_gate >= K, ld_gate % 8 == 0, gate
  * 16-byte aligned; ignored without a gate). residual ([M][N] BF16,
@@ -258,7 +263,7 @@ int w8a16_rmsnorm(const void* x, const void* gate, const void* weight, float eps
  * M runs the GEMV kernel (the skinny path of w8a16_gemv is not fused).
  */
 int w8a16_gemv_fused(const void* A, const void* gate, int64_t ld_gate, const void* norm_weight, float eps,
-                     const void* Wq, const void* scale, const void* residual, void* out,
+                     int64_t group, const void* Wq, const void* scale, const void* residual, void* out,
                      int64_t M, int64_t N, int64_t K, void* stream);
 
 /*

@@ -184,6 +184,14 @@ def test_norm_and_fused_rejections():
     assert binding.rmsnorm_raw(X, G, Wn, 1e-5, X + 16, 4, 256, 0) == binding.ERR_ALIAS   # out over x
     assert binding.rmsnorm_raw(X, G, Wn, 1e-5, G, 4, 256, 0) == binding.ERR_ALIAS        # out over gate
     assert binding.rmsnorm_raw(X, G, Wn, 1e-5, Wn - 16, 4, 256, 0) == binding.ERR_ALIAS  # out reaches weight
+    # group: 0 or K, else a multiple of 1024 dividing K <= 16384
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 0, 8192, 0, group=512) == binding.ERR_SHAPE
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 0, 8192, 0, group=3072) == binding.ERR_SHAPE   # 8192 % 3072
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 0, 32768, 0, group=1024) == binding.ERR_SHAPE  # K > 16384
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 0, 8192, 0, group=-1024) == binding.ERR_SHAPE
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 0, 8192, 0, group=16384) == binding.ERR_SHAPE  # > K
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 0, 8192, 0, group=2048) == binding.OK          # no-op, valid
+    assert binding.rmsnorm_raw(X, G, Wn, 1e-5, O, 0, 32768, 0, group=32768) == binding.OK        # group = K
     # w8a16_gemv_fused(A, gate, norm_weight, eps, Wq, scale, residual, out, M, N, K)
     A, Wq, S = F + (4 << 30), F + (5 << 30), F + (6 << 30)
     R = F + (7 << 30)
@@ -203,6 +211,8 @@ def test_norm_and_fused_rejections():
     assert fused(A, 0, O + 64, 1e-5, Wq, S, R, O, 1, 256, 256, 0) == binding.ERR_ALIAS   # out over norm weight
     assert fused(A, G, Wn, 1e-5, Wq, S, R, G + 2, 1, 256, 256, 0) == binding.ERR_ALIAS    # out over gate
     assert fused(A, 0, 0, 1e-5, Wq, S, 0, A, 1, 256, 256, 0) == binding.ERR_ALIAS        # out over A
+    assert fused(A, G, Wn, 1e-5, Wq, S, R, O, 1, 4096, 8192, 0, group=1000) == binding.ERR_SHAPE
+    assert fused(A, G, Wn, 1e-5, Wq, S, R, O, 0, 4096, 8192, 0, group=1024) == binding.OK     # no-op, valid
     # w8a16_gemm_residual(A, Wq, scale, residual, out, M, N, K)
     assert binding.gemm_residual_raw(A, Wq, S, 0, O, 4, 256, 256, 0) == binding.ERR_NULL
     assert binding.gemm_residual_raw(A, Wq, S, R + 1, O, 4, 256, 256, 0) == binding.ERR_ALIGN
@@ -221,6 +231,10 @@ def test_binding_refuses_bad_norm_arguments():
         binding.w8a16_rmsnorm(A, w, float("nan"))
     with pytest.raises(ValueError, match="eps"):
         binding.w8a16_gemv_fused(A, W, S, norm_weight=w, eps=-1.0)
+    with pytest.raises(ValueError, match="group"):
+        binding.w8a16_rmsnorm(A, w, 1e-5, group=100)
+    with pytest.raises(ValueError, match="group"):
+        binding.w8a16_gemv_fused(A, W, S, norm_weight=w, group=128)
     with pytest.raises(ValueError, match="gate needs"):
         binding.w8a16_gemv_fused(A, W, S, gate=A)
     with pytest.raises(ValueError, match="residual"):

@@ -99,6 +99,24 @@ def test_rmsnorm(dev, gated, M, K):
     check_norm_bits(bits(got), want, f"rmsnorm gated={gated} M={M} K={K}")
 
 
+# Grouped norm (the published Mamba-2 gated norm: groups of K / n_groups
+# channels): whole-row bits with group = K, the oracle's grouped norm otherwise.
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("M,K,G", [(3, 8192, 1024), (1024, 8192, 1024), (2, 16384, 2048), (5, 4096, 4096),
+                                   (4, 2048, 1024), (2, 12288, 3072), (3, 1024, 1024)])
+def test_rmsnorm_grouped(dev, gated, M, K, G):
+    say(f"rmsnorm grouped gated={gated} M={M} K={K} group={G}")
+    x = inputs.activations(M, K, 3150 + K + G)
+    w = inputs.norm_weight(K, 3250 + K)
+    z = inputs.activations(M, K, 3350 + K) if gated else None
+    dx, dw, dz = bf(x, dev), bf(w, dev), bf(z, dev) if gated else None
+    got = bits(binding.w8a16_rmsnorm(dx, dw, EPS, gate=dz, group=G))
+    _, want = oracle.rmsnorm(x, w, EPS, gate=z, group=G)
+    check_norm_bits(got, want, f"rmsnorm grouped gated={gated} M={M} K={K} group={G}")
+    if G == K:
+        assert np.array_equal(got, bits(binding.w8a16_rmsnorm(dx, dw, EPS, gate=dz)))
+
+
 def test_rmsnorm_zero_row_and_big_eps(dev):
     M, K = 3, 512
     x = inputs.activations(M, K, 3401)
@@ -147,6 +165,31 @@ def test_gemv_fused_gated_norm_and_residual(dev, M, N, K):
     ref, den = oracle.w8a16(a, Wq, S)
     want = oracle.bf16_value(res) + ref
     check_close(bits(got), want, den, f"fused gated+res M={M} N={N} K={K}", extra_rel=2.0 ** -8)
+
+
+@pytest.mark.parametrize("M,N,K,G", [(1, 4096, 8192, 1024), (2, 4096, 8192, 2048), (4, 1000, 16384, 1024),
+                                     (8, 4096, 8192, 1024), (1, 18560, 4096, 1024), (3, 300, 16384, 8192),
+                                     (1, 4096, 8192, 8192)])
+def test_gemv_fused_grouped_gated_norm(dev, M, N, K, G):
+    """out_proj form with the gated norm over groups of G channels (the
+    published Mamba-2 norm with K / G groups), the projection and the
+    residual; group = K gives the whole-row bits."""
+    say(f"gemv_fused grouped gated+residual M={M} N={N} K={K} group={G}")
+    y = inputs.activations(M, K, 3810 + M)
+    z = inputs.activations(M, K, 3910 + M)
+    w = inputs.norm_weight(K, 4010 + K)
+    res = inputs.activations(M, N, 4110 + N)
+    Wq, S = inputs.weights(N, K, 0.02, 4210 + N)
+    dy, dz, dw, dr = bf(y, dev), bf(z, dev), bf(w, dev), bf(res, dev)
+    dW, dS = u8(Wq, dev), bf(S, dev)
+    got = bits(binding.w8a16_gemv_fused(dy, dW, dS, norm_weight=dw, eps=EPS, gate=dz, residual=dr, group=G))
+    _, a = oracle.rmsnorm(y, w, EPS, gate=z, group=G)
+    ref, den = oracle.w8a16(a, Wq, S)
+    want = oracle.bf16_value(res) + ref
+    check_close(got, want, den, f"fused grouped M={M} N={N} K={K} group={G}", extra_rel=2.0 ** -8)
+    if G == K:
+        whole = bits(binding.w8a16_gemv_fused(dy, dW, dS, norm_weight=dw, eps=EPS, gate=dz, residual=dr))
+        assert np.array_equal(got, whole)
 
 
 @pytest.mark.parametrize("M", [1, 3, 8])
