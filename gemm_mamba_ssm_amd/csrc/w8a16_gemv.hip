@@ -118,12 +118,17 @@ struct Gemv {
         uint32_t voff[J];
 #pragma unroll
         for (int j = 0; j < J; ++j) voff[j] = kvalid[j] ? static_cast<uint32_t>(kch[j]) : kOutOfRange;
+        // In row order (the scheduler would otherwise issue them in any
+        // order, e.g. the last row first), so that row i's products wait for
+        // rows 0..i only.
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
+        for (int i = 0; i < RB; ++i) {
 #pragma unroll
             for (int j = 0; j < J; ++j)
                 r.w[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                 rw, voff[j], min(i, rows - 1) * K, kNonTemporal));
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // Output (m, n): BF16 of the sum, the residual epilogue, or on the conv
@@ -173,6 +178,10 @@ struct Gemv {
                             wv[t], __builtin_bit_cast(bf16x2_t, a[m][j][t]), p, false);
                     v[i * MR + m] = fmaf(p, sj, v[i * MR + m]);
                 }
+                // Row by row: the scheduler would otherwise interleave the
+                // rows' converts, and the first product would wait for the
+                // group's last row (and for any loads issued after it).
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         butterfly<P, P, 32>(v, lane);
@@ -520,11 +529,15 @@ int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_
     int64_t per_block;
     if (mr == 1 && j == 1) {
         // Single-token decode, launch shape measured on the Mamba-2 projection
-        // shapes: 4-row groups while they number at least 8 per CU, else
-        // 8-row groups; one group per workgroup up to about 18 workgroups per
-        // CU, then several.
-        const int rb = ceil_div(N, 4) >= 8 * cus ? 4 : 8;
-        c = {rb == 4 ? &gemv_kernel<1, 1, 4, SF, FU> : &gemv_kernel<1, 1, 8, SF, FU>, rb};
+        // shapes: 4-row groups while they number at least 8 per CU (in_proj),
+        // else 16-row groups while there is one for every CU (out_proj: 8.0
+        // against 8.1 us with 8-row groups), else 8-row groups; one group per
+        // workgroup up to about 18 workgroups per CU, then several.
+        const int rb = ceil_div(N, 4) >= 8 * cus ? 4 : ceil_div(N, 16) >= cus ? 16 : 8;
+        c = {rb == 4    ? &gemv_kernel<1, 1, 4, SF, FU>
+             : rb == 16 ? &gemv_kernel<1, 1, 16, SF, FU>
+                        : &gemv_kernel<1, 1, 8, SF, FU>,
+             rb};
         per_block = std::max<int64_t>(1, ceil_div(N, rb) / (18 * cus));
         if constexpr (FU == kFuseNorm || FU == kFuseGated || FU == kFuseNormConv) {
             // Every workgroup normalizes the whole activation row before its
