@@ -69,7 +69,8 @@ def assert_within_tol(got_bits, ref, den, what):
 
 
 GEMV_SHAPES = [(1, 1000, 1040), (1, 18560, 4096), (1, 4096, 8192), (3, 300, 16384), (2, 7, 16),
-               (4, 1000, 1040), (8, 259, 272), (16, 18560, 4096), (9, 300, 8192), (13, 130, 3072)]
+               (4, 1000, 1040), (8, 259, 272), (16, 18560, 4096), (9, 300, 8192), (13, 130, 3072),
+               (3, 9000, 1040)]
 GEMM_SHAPES = [(1, 384, 256), (16, 1000, 4096), (3, 140000, 1040), (20, 4096, 8192), (31, 300, 4112),
                (33, 1000, 1040), (40, 98400, 528), (129, 1000, 1040), (300, 257, 4096), (66, 65704, 1040),
                (65, 89603, 1040), (513, 640, 1024), (200, 12200, 1280), (20, 1000, 36880), (40, 300, 40960),
