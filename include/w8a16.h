@@ -94,9 +94,11 @@ enum w8a16_scale_format {
  * M == 0 or N == 0 is a no-op returning W8A16_OK.
  * Each weight byte is read from HBM once per call for all M rows. M = 1
  * runs a GEMV on the vector ALU (dot products over 16-byte weight chunks,
- * reduced across the wavefront and the workgroup in a fixed order). From
- * M = 2 on, where the skinny path of w8a16_gemm applies (below), the call
- * runs it (products on the matrix cores; same result contract).
+ * reduced across the wavefront and the workgroup in a fixed order), and so
+ * do M = 2..4 when K <= 8192 and the weights make at least 8 four-row groups
+ * per compute unit (N >= 8192 on 256 CUs). Otherwise, from M = 2 on, where
+ * the skinny path of w8a16_gemm applies (below), the call runs it (products
+ * on the matrix cores; same result contract).
  */
 int w8a16_gemv(const void* A, const void* Wq, const void* scale, void* out,
                int64_t M, int64_t N, int64_t K, void* stream);
