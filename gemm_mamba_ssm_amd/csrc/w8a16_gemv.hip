@@ -94,10 +94,14 @@ struct Gemv {
         uint32_t s_bits[J];        // the block scales' bits, decoded where they are used
     };
 
+    // Group g's scales and weight rows into r. A group past the workgroup's
+    // range (valid false) issues the same loads, which read zeros (an empty
+    // buffer range; the scale of row-block 0), so that the loop below has no
+    // branch around a load and the compiler's waits stay exact.
     __device__ static __forceinline__ void load(Regs& r, const uint8_t* __restrict__ W,
-                                                const void* __restrict__ S, int g, int N, int K,
+                                                const void* __restrict__ S, int g, bool valid, int N, int K,
                                                 int k_blocks, const int (&kch)[J], const bool (&kvalid)[J]) {
-        const int n0 = g * RB;
+        const int n0 = valid ? g * RB : 0;
         // The scales first: all RB rows sit in scale row-block n0/128, and
         // every row's sum needs them, so waiting for them must not wait for
         // the weight rows issued after them. The load is unconditional (a
@@ -112,7 +116,7 @@ struct Gemv {
         // gets an offset past num_records and reads as zero; a row past N
         // re-reads the group's last row (the scalar offset), and its sum is
         // never stored. The lane offset is the same for every row.
-        const int rows = min(RB, N - n0);
+        const int rows = valid ? min(RB, N - n0) : 0;
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(W + static_cast<int64_t>(n0) * K), 0, rows * K, kBufferFlags);
         uint32_t voff[J];
@@ -126,7 +130,7 @@ struct Gemv {
 #pragma unroll
             for (int j = 0; j < J; ++j)
                 r.w[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                rw, voff[j], min(i, rows - 1) * K, kNonTemporal));
+                                rw, voff[j], max(min(i, rows - 1), 0) * K, kNonTemporal));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -345,7 +349,18 @@ struct NormOps {
     }
 };
 
-template <int MR, int J, int RB, int SF, int FU>
+// How a workgroup walks its groups. kLoopAll: a double-buffered loop whose
+// next-group loads are always issued (past the range they read zeros), so
+// the compiler's waits stay per row; for several groups per workgroup.
+// kOneGroup: exactly one group each (groups_per_block == 1), no loop.
+// kLoopGuarded: the loop with the next-group loads behind a branch; with one
+// group per workgroup, the plain (unfused) decode's form, measured faster
+// there than kOneGroup (in_proj 13.57 against 13.71-13.74 us, out_proj 8.02-
+// 8.04 against 8.19-8.23 us; the one-group form takes fewer registers and
+// packs more workgroups per CU).
+constexpr int kLoopAll = 0, kOneGroup = 1, kLoopGuarded = 2;
+
+template <int MR, int J, int RB, int SF, int FU, int WALK>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
             const void* __restrict__ S, uint16_t* __restrict__ out,
@@ -401,20 +416,26 @@ gemv_kernel(const uint16_t* __restrict__ A, const uint8_t* __restrict__ W,
     if constexpr (kNorm) {
         NormOps<MR, J, FU == kFuseGated> no;
         no.issue(fu, K, kch, kvalid);
-        G::load(ra, W, S, g_begin, N, K, k_blocks, kch, kvalid);
+        G::load(ra, W, S, g_begin, true, N, K, k_blocks, kch, kvalid);
         no.apply(a, fu, K, kch, kvalid, lane, wave, nwaves);
     } else {
-        G::load(ra, W, S, g_begin, N, K, k_blocks, kch, kvalid);
+        G::load(ra, W, S, g_begin, true, N, K, k_blocks, kch, kvalid);
     }
     const uint16_t* res = FU != kFuseNone ? fu.residual : nullptr;
 
+    if constexpr (WALK == kOneGroup) {
+        G::process(ra, a, kvalid, red, 0, out, res, fu, S, g_begin, N, lane, wave, nwaves);
+        return;
+    }
+    // Double buffer: the next group's loads go out before this group's
+    // products.
     int parity = 0;
     for (int g = g_begin; g < g_end; g += 2) {
-        if (g + 1 < g_end) G::load(rb, W, S, g + 1, N, K, k_blocks, kch, kvalid);
+        if (WALK == kLoopAll || g + 1 < g_end) G::load(rb, W, S, g + 1, g + 1 < g_end, N, K, k_blocks, kch, kvalid);
         G::process(ra, a, kvalid, red, parity, out, res, fu, S, g, N, lane, wave, nwaves);
         parity ^= 1;
         if (g + 1 >= g_end) break;
-        if (g + 2 < g_end) G::load(ra, W, S, g + 2, N, K, k_blocks, kch, kvalid);
+        if (WALK == kLoopAll || g + 2 < g_end) G::load(ra, W, S, g + 2, g + 2 < g_end, N, K, k_blocks, kch, kvalid);
         G::process(rb, a, kvalid, red, parity, out, res, fu, S, g + 1, N, lane, wave, nwaves);
         parity ^= 1;
     }
@@ -441,9 +462,24 @@ constexpr int rows_for(int mr, int j, int fu) {
     return fu == kFuseNormConv && mr * rb >= 64 ? rb / 2 : rb;
 }
 
+// The kernels of one configuration: for several groups per workgroup, and
+// for one (the fused forms without a loop, the plain form with its guarded
+// loop).
+struct Choice {
+    gemv_fn fn;
+    gemv_fn fn_one;
+    int rows_per_group;
+};
+
+template <int MR, int J, int RB, int SF, int FU>
+Choice kernels() {
+    return {&gemv_kernel<MR, J, RB, SF, FU, kLoopAll>,
+            &gemv_kernel<MR, J, RB, SF, FU, FU == kFuseNone ? kLoopGuarded : kOneGroup>, RB};
+}
+
 template <int MR, int J, int SF, int FU>
-gemv_fn pick_j() {
-    return &gemv_kernel<MR, J, rows_for(MR, J, FU), SF, FU>;
+Choice pick_j() {
+    return kernels<MR, J, rows_for(MR, J, FU), SF, FU>();
 }
 
 // The fused kernels hold the norm's operands beside the activations; they
@@ -456,20 +492,15 @@ inline bool fused_fits(int64_t M, int64_t K) {
 }
 
 template <int MR, int SF, int FU>
-gemv_fn pick(int j) {
+Choice pick(int j) {
     if constexpr (max_chunks(MR) >= 2 && (FU == kFuseNone || MR <= kFusedMaxMTwoChunks))
         if (j == 2) return pick_j<MR, 2, SF, FU>();
     return pick_j<MR, 1, SF, FU>();
 }
 
-struct Choice {
-    gemv_fn fn;
-    int rows_per_group;
-};
-
 template <int MR, int SF, int FU>
 Choice choose(int j) {
-    return {pick<MR, SF, FU>(j), j == 2 ? rows_for(MR, 2, FU) : rows_for(MR, 1, FU)};
+    return pick<MR, SF, FU>(j);
 }
 
 template <int SF>
@@ -546,10 +577,7 @@ int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_
         // against 8.1 us with 8-row groups), else 8-row groups; one group per
         // workgroup up to about 18 workgroups per CU, then several.
         const int rb = ceil_div(N, 4) >= 8 * cus ? 4 : ceil_div(N, 16) >= cus ? 16 : 8;
-        c = {rb == 4    ? &gemv_kernel<1, 1, 4, SF, FU>
-             : rb == 16 ? &gemv_kernel<1, 1, 16, SF, FU>
-                        : &gemv_kernel<1, 1, 8, SF, FU>,
-             rb};
+        c = rb == 4 ? kernels<1, 1, 4, SF, FU>() : rb == 16 ? kernels<1, 1, 16, SF, FU>() : kernels<1, 1, 8, SF, FU>();
         per_block = std::max<int64_t>(1, ceil_div(N, rb) / (18 * cus));
         if constexpr (FU == kFuseNorm || FU == kFuseGated || FU == kFuseNormConv) {
             // Every workgroup normalizes the whole activation row before its
@@ -558,13 +586,11 @@ int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_
             // norm (whose prologue also computes silu of the gate). Measured
             // on the Mamba-2 projections: in_proj 15.2 -> 14.3 us, out_proj
             // 10.0 -> 9.1 us.
-            c = {&gemv_kernel<1, 1, 8, SF, FU>, 8};
+            c = kernels<1, 1, 8, SF, FU>();
             per_block = FU == kFuseGated ? 2 : 1;
         }
     } else if (FU == kFuseNone && valu_few_tokens(M, N, K, cus)) {
-        c = {mr == 2 ? &gemv_kernel<2, 1, 4, SF, FU> : mr == 3 ? &gemv_kernel<3, 1, 4, SF, FU>
-                                                               : &gemv_kernel<4, 1, 4, SF, FU>,
-             4};
+        c = mr == 2 ? kernels<2, 1, 4, SF, FU>() : mr == 3 ? kernels<3, 1, 4, SF, FU>() : kernels<4, 1, 4, SF, FU>();
         per_block = std::max<int64_t>(1, ceil_div(N, 4) / (18 * cus));
     } else {
         const int64_t resident = cus * (kWavesPerCu / nwaves > 0 ? kWavesPerCu / nwaves : 1);
@@ -573,7 +599,7 @@ int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_
     const int64_t groups = ceil_div(N, c.rows_per_group);
     const int64_t blocks = ceil_div(groups, per_block);
 
-    return launch(c.fn, dim3(static_cast<unsigned>(blocks)), dim3(64 * nwaves), stream,
+    return launch(per_block == 1 ? c.fn_one : c.fn, dim3(static_cast<unsigned>(blocks)), dim3(64 * nwaves), stream,
                   static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Wq), scale,
                   static_cast<uint16_t*>(out), static_cast<int>(N), static_cast<int>(K),
                   static_cast<int>(per_block), fu);
