@@ -546,21 +546,16 @@ Choice select_plain(int mr, int j) {
     }
 }
 
-// A few tokens with K of one chunk per lane, on the single-token launch
-// shapes (one group per workgroup, every load issued at the start): 2..4
-// rows where the weights make at least 8 four-row groups per CU (the Mamba-2
-// in_proj, 4-row groups), 2 rows where they make a 16-row group per CU (the
-// out_proj, 16-row groups). Measured on the in_proj (K = 4096, N = 18560):
-// 14.8 / 17.0 / 18.7 us at M = 2 / 3 / 4 against 18.6 / 19.1 / 20.1 us for
-// the skinny MFMA kernel, which stays faster from M = 5 (17.8 against
-// 21.2 us); on the out_proj (K = 8192, N = 4096): 8.1 against 8.6 us at
-// M = 2, 9.0 against 8.7 us at M = 3.
+// A few tokens (2..4) on a shape with at least 8 four-row groups per CU and
+// K of one chunk per lane (the Mamba-2 in_proj): the single-token launch
+// shape, 4-row groups with one group per workgroup, every load issued at the
+// start. Measured on the in_proj (K = 4096, N = 18560): 14.8 / 17.0 / 18.7 us
+// at M = 2 / 3 / 4 against 18.6 / 19.1 / 20.1 us for the skinny MFMA kernel,
+// which stays faster from M = 5 (17.8 against 21.2 us) and on the out_proj
+// (8.6 against 9.1 us at M = 2).
 constexpr int64_t kValuFewMaxM = 4;
-inline bool valu_few_in_proj(int64_t N, int64_t cus) { return ceil_div(N, 4) >= 8 * cus; }
 inline bool valu_few_tokens(int64_t M, int64_t N, int64_t K, int64_t cus) {
-    if (M < 2 || K > static_cast<int64_t>(kWaveK) * kMaxWaves) return false;
-    if (valu_few_in_proj(N, cus)) return M <= kValuFewMaxM;
-    return M == 2 && ceil_div(N, 16) >= cus;
+    return M >= 2 && M <= kValuFewMaxM && K <= static_cast<int64_t>(kWaveK) * kMaxWaves && ceil_div(N, 4) >= 8 * cus;
 }
 
 // The launch of the GEMV for scale format SF, fused or not (arguments
@@ -595,11 +590,8 @@ int run_gemv(const void* A, const void* Wq, const void* scale, void* out, int64_
             per_block = FU == kFuseGated ? 2 : 1;
         }
     } else if (FU == kFuseNone && valu_few_tokens(M, N, K, cus)) {
-        if (valu_few_in_proj(N, cus))
-            c = mr == 2 ? kernels<2, 1, 4, SF, FU>() : mr == 3 ? kernels<3, 1, 4, SF, FU>() : kernels<4, 1, 4, SF, FU>();
-        else
-            c = kernels<2, 1, 16, SF, FU>();
-        per_block = std::max<int64_t>(1, ceil_div(N, c.rows_per_group) / (18 * cus));
+        c = mr == 2 ? kernels<2, 1, 4, SF, FU>() : mr == 3 ? kernels<3, 1, 4, SF, FU>() : kernels<4, 1, 4, SF, FU>();
+        per_block = std::max<int64_t>(1, ceil_div(N, 4) / (18 * cus));
     } else {
         const int64_t resident = cus * (kWavesPerCu / nwaves > 0 ? kWavesPerCu / nwaves : 1);
         per_block = ceil_div(ceil_div(N, c.rows_per_group), resident);
@@ -632,8 +624,8 @@ extern "C" int w8a16_gemv_ex(const void* A, const void* Wq, const void* scale, i
     // 4 rows on its ring form is too, where it applies (in_proj: 21 against
     // 23 us at M = 4, 22 against 49 us at M = 16): the products cost the VALU
     // GEMV more than the weight stream takes. Except for 2..4 rows on the
-    // in_proj-sized shapes and 2 rows on the out_proj-sized ones, which run
-    // the GEMV with the single-token launch shapes (valu_few_tokens).
+    // in_proj-sized shapes, which run the GEMV with the single-token launch
+    // shape (valu_few_tokens).
     const int cus = device_cu_count();
     if (!valu_few_tokens(M, N, K, cus) &&
         ((M >= 2 && skinny_lds_fits(M, N, K, cus)) || (M >= 4 && skinny_fits(M, K))))

@@ -96,8 +96,7 @@ enum w8a16_scale_format {
  * runs a GEMV on the vector ALU (dot products over 16-byte weight chunks,
  * reduced across the wavefront and the workgroup in a fixed order), and so
  * do M = 2..4 when K <= 8192 and the weights make at least 8 four-row groups
- * per compute unit (N >= 8192 on 256 CUs), and M = 2 when K <= 8192 and they
- * make a 16-row group per compute unit (N >= 4081). Otherwise, from M = 2 on, where
+ * per compute unit (N >= 8192 on 256 CUs). Otherwise, from M = 2 on, where
  * the skinny path of w8a16_gemm applies (below), the call runs it (products
  * on the matrix cores; same result contract).
  */

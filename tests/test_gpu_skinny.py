@@ -4,11 +4,8 @@ calls through the C ABI.
 
 The host takes this form for 1 <= M <= 16 when the activations, padded to the
 waves' k-blocks, fit 128 KB of LDS and, with more 16-row weight blocks than
-CUs, 32 KB; the GEMV entry from M = 2 on (but for 2..4 rows with at least 8
-four-row weight groups per CU and 2 rows with a 16-row group per CU, which it
-keeps on the GEMV kernel: here M = 2 with N = 4100 and M = 4 with N = 18560
-take the one-shot form through the GEMM entry only), the GEMM entry for every
-M. The shapes below are chosen for that (on a 256-CU MI355X):
+CUs, 32 KB; the GEMV entry from M = 2 on, the GEMM entry for every M. The
+shapes below are chosen for that (on a 256-CU MI355X):
   * M = 2, N = 4100, K = 4096: 257 blocks (more than the CUs), 16 KB of
     activations, a ragged last block (N % 16 = 4);
   * M = 3, N = 129, K = 4112: 8 k-blocks per wave, a k-tail of 16, 9 blocks;
@@ -90,7 +87,7 @@ def test_one_shot_every_element(dev, entry, M, N, K):
 
 
 def test_one_shot_matches_between_entries(dev):
-    M, N, K = SHAPES[1]                      # a shape both entries run on the one-shot form
+    M, N, K = SHAPES[0]
     A = inputs.activations(M, K, 4300)
     W, S = inputs.weights(N, K, 0.02, 4400)
     assert np.array_equal(run("gemv", A, W, S, dev), run("gemm", A, W, S, dev))
